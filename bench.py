@@ -1,0 +1,185 @@
+"""Benchmark of the affinity pass on one MI355X.
+
+A step is one pass of the whole path over one batch of calibration tokens:
+weight fold, ||w^d||^2, the hot kernel (eq. (5), FO and ADD sums and the
+down-edge moment), the fixed-order reduction, the down-edge weight norms and
+S_down.  Inputs (seeded synthetic layer of the requested workload) are resident
+in HBM before the timed region starts.
+
+Prints one JSON line.  `value` is calibration tokens/s of the whole step;
+`roofline` describes the hot kernel (algorithmic MFMA FLOPs per launch over
+its average duration measured with HIP events on the launch stream);
+`cpu_baseline` is the float64 oracle timed on this host on a bounded token
+sample of the same layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (matrix)
+PEAK_HBM_GBS = 8000.0
+METRIC = "calibration tokens/s for S↑-fo affinity (Qwen3-0.6B layer); % MFMA peak"
+HOT_SRC = os.path.join(ROOT, "head_neuron_affinity_amd", "csrc", "k_affinity.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hot_kernel_traffic.json")
+
+
+def hot_source_hash() -> str:
+    with open(HOT_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per hot-kernel launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source for this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("source_sha256_16") != hot_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(layer_gpu, budget_s: float = 12.0):
+    """Time the float64 oracle on the first tokens of the same layer."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+
+    def sample(T):
+        out = {}
+        for k, v in layer_gpu.items():
+            if k in ("a", "g", "u", "r", "r_next"):
+                out[k] = v[:T].cpu()
+            elif isinstance(v, torch.Tensor):
+                out[k] = v.cpu()
+            else:
+                out[k] = v
+        return out
+
+    T0 = 64
+    s = sample(T0)
+    t = time.perf_counter()
+    oracle.affinity_layer(s)
+    dt0 = time.perf_counter() - t
+    # down-edge weight norms are a per-layer fixed cost; the rest scales with T
+    T1 = int(min(max(T0 * budget_s / max(dt0, 1e-3), 128), 8192, layer_gpu["a"].shape[0]))
+    s = sample(T1)
+    t = time.perf_counter()
+    oracle.affinity_layer(s)
+    dt = time.perf_counter() - t
+    return {"value": T1 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {T1} tokens of the same synthetic layer, whole pass "
+                      f"(S_fo, S_add, S_down) in float64 numpy, {dt:.1f} s"}
+
+
+def build_inputs(config: int, T=None):
+    import synth
+    return synth.make_config_layer(config, T=T, device="cuda")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1, help="workload: 1, 2, 3 (28-layer stack) or 4")
+    ap.add_argument("--tokens", type=int, default=None, help="override T (not for reported numbers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the pass would shard over tokens with one all-reduce of the partial sums, "
+              "which is not built here).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import head_neuron_affinity_amd as hna
+
+    torch.cuda.set_device(0)
+    shape = synth.layer_shape(args.config)
+    if args.tokens:
+        shape = shape.with_tokens(args.tokens)
+    n_layers = shape.layers
+    layers = [synth.make_config_layer(args.config, layer=i, T=args.tokens, device="cuda")
+              for i in range(n_layers)]
+    torch.cuda.synchronize()
+    L0 = layers[0]
+    passes = [hna.pass_for_layer(L) for L in layers]
+    grps = [[int(x) for x in L["group_of_head"].tolist()] for L in layers]
+    grps_n = [[int(x) for x in L["group_of_head_next"].tolist()] for L in layers]
+    T = shape.T
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for i, (L, P) in enumerate(zip(layers, passes)):
+            P.fold(L)
+            if ev is not None and i == 0:
+                ev[0].record(stream)
+            P.hot(L, grps[i])
+            if ev is not None and i == 0:
+                ev[1].record(stream)
+            P.finalize(1.0 / T)
+            if n_layers == 1 or i + 1 < n_layers:
+                P.down(L, grps_n[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    hot_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    H, d, I = shape.H, shape.d, shape.I
+    flops_hot = 4.0 * T * H * d * I                          # algorithmic, one launch
+    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops_hot / (hot_ms * 1e-3) / 1e12
+    esz = 2 if shape.dtype == "bf16" else 4
+    stream_bytes = T * (esz * (H * d + 2 * I) + 8)           # a, g, u, r, r_next read once
+    workload = f"{shape.name}:T={T}"
+    traffic = traffic_for(workload)
+    value = T * 1.0 / (ms_step * 1e-3) if n_layers == 1 else T / (ms_step * 1e-3)
+    rec = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": shape.dtype, "data": "synthetic (seeded generator, inputs resident in HBM)",
+        "config": {"workload": shape.name, "T": T, "hidden": shape.hidden, "H": H, "G": shape.G,
+                   "d": d, "I": I, "layers": n_layers},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic},
+        "hot_kernel_ms": hot_ms,
+        "mfma_frac_whole_step": flops_hot * n_layers / (ms_step * 1e-3) / 1e12 / peak,
+        "hot_stream_gbs": stream_bytes / (hot_ms * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline and n_layers == 1:
+        rec["cpu_baseline"] = cpu_baseline(L0)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+"""ctypes binding of libhna (include/hna.h).
+
+Argument marshalling only: tensors become device pointers, the stream is
+torch's current HIP stream, and output / workspace buffers are allocated with
+torch.  Every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or the call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhna.so")
+
+HNA_OK = 0
+HNA_ERR_INVALID_ARG = -1
+HNA_ERR_UNSUPPORTED = -2
+HNA_ERR_ALIGNMENT = -3
+HNA_ERR_WORKSPACE = -4
+HNA_ERR_HIP = -5
+HNA_F32 = 0
+HNA_BF16 = 1
+HNA_ACCUMULATE = 1
+
+EXPORTED = [
+    "hna_abi_version", "hna_status_string", "hna_last_error", "hna_folded_bytes",
+    "hna_fold_workspace_bytes", "hna_fold_up_weights", "hna_down_col_sqnorm",
+    "hna_up_workspace_bytes", "hna_affinity_up", "hna_finalize_up",
+    "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine",
+]
+
+
+class hna_dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("hidden", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("d", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class hna_down_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("I", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class HnaError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({msg})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhna.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m head_neuron_affinity_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    dp = ctypes.POINTER(hna_dims)
+    ddp = ctypes.POINTER(hna_down_dims)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "hna_abi_version": (ctypes.c_int, []),
+        "hna_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "hna_last_error": (ctypes.c_char_p, []),
+        "hna_folded_bytes": (sz, [dp]),
+        "hna_fold_workspace_bytes": (sz, [dp]),
+        "hna_fold_up_weights": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, sz, vp, sz, vp]),
+        "hna_down_col_sqnorm": (ctypes.c_int, [dp, vp, vp, vp]),
+        "hna_up_workspace_bytes": (sz, [dp]),
+        "hna_affinity_up": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, ip, vp, sz, vp]),
+        "hna_finalize_up": (ctypes.c_int, [dp, vp, f32, ctypes.c_int, vp, sz, vp, vp, vp, vp]),
+        "hna_down_workspace_bytes": (sz, [ddp]),
+        "hna_down_weight_norms": (ctypes.c_int, [ddp, vp, vp, vp, vp, vp, ip, vp, vp, sz, vp]),
+        "hna_down_combine": (ctypes.c_int, [i32, i32, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().hna_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().hna_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != HNA_OK:
+        raise HnaError(status, where, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HNA_BF16
+    if t.dtype == torch.float32:
+        return HNA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32 only")
+
+
+def _map(group_of_head: Sequence[int]):
+    arr = (ctypes.c_int32 * len(group_of_head))(*[int(x) for x in group_of_head])
+    return arr
+
+
+def make_dims(T: int, hidden: int, H: int, G: int, d: int, I: int, dtype: int) -> hna_dims:
+    return hna_dims(int(T), int(hidden), int(H), int(G), int(d), int(I), int(dtype))
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ calls
+def folded_bytes(dims: hna_dims) -> int:
+    n = lib().hna_folded_bytes(ctypes.byref(dims))
+    if n == 0:
+        _check(HNA_ERR_INVALID_ARG, "hna_folded_bytes")
+    return n
+
+
+def fold_up_weights(dims: hna_dims, W_o, gamma, W_gate, W_up, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """M_h = W_o^(h)T diag(gamma) [W_gate; W_up]^T in the kernel's layout (opaque bytes)."""
+    _need_cuda(W_o, gamma, W_gate, W_up)
+    L = lib()
+    nb = folded_bytes(dims)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=W_o.device)
+    wsb = L.hna_fold_workspace_bytes(ctypes.byref(dims))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=W_o.device)
+    _check(L.hna_fold_up_weights(ctypes.byref(dims), _ptr(W_o), _ptr(gamma), _ptr(W_gate),
+                                 _ptr(W_up), _ptr(out), out.numel() * out.element_size(),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(W_o.device)), "hna_fold_up_weights")
+    return out
+
+
+def down_col_sqnorm(dims: hna_dims, W_down, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need_cuda(W_down)
+    if out is None:
+        out = torch.empty(dims.I, dtype=torch.float32, device=W_down.device)
+    _check(lib().hna_down_col_sqnorm(ctypes.byref(dims), _ptr(W_down), _ptr(out),
+                                     _stream(W_down.device)), "hna_down_col_sqnorm")
+    return out
+
+
+def up_workspace_bytes(dims: hna_dims) -> int:
+    return int(lib().hna_up_workspace_bytes(ctypes.byref(dims)))
+
+
+def affinity_up(dims: hna_dims, a, g, u, r, r_next, M, group_of_head,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The hot pass; returns the workspace holding the partial sums."""
+    _need_cuda(a, g, u, r, r_next, M)
+    L = lib()
+    wsb = L.hna_up_workspace_bytes(ctypes.byref(dims))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=a.device)
+    _check(L.hna_affinity_up(ctypes.byref(dims), _ptr(a), _ptr(g), _ptr(u), _ptr(r), _ptr(r_next),
+                             _ptr(M), _map(group_of_head), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(a.device)),
+           "hna_affinity_up")
+    return workspace
+
+
+def finalize_up(dims: hna_dims, wd_sq, workspace, scale: float, accumulate: bool = False,
+                S_fo=None, S_add=None, c_down=None, want_c: bool = True):
+    _need_cuda(wd_sq, workspace)
+    dev = wd_sq.device
+    if S_fo is None:
+        S_fo = torch.empty((dims.G, dims.I), dtype=torch.float32, device=dev)
+    if S_add is None:
+        S_add = torch.empty((dims.G, dims.I), dtype=torch.float32, device=dev)
+    if c_down is None and want_c:
+        c_down = torch.empty(dims.I, dtype=torch.float32, device=dev)
+    _check(lib().hna_finalize_up(ctypes.byref(dims), _ptr(wd_sq), float(scale),
+                                 HNA_ACCUMULATE if accumulate else 0, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _ptr(S_fo),
+                                 _ptr(S_add), _ptr(c_down), _stream(dev)), "hna_finalize_up")
+    return S_fo, S_add, c_down
+
+
+def down_workspace_bytes(ddims: hna_down_dims) -> int:
+    return int(lib().hna_down_workspace_bytes(ctypes.byref(ddims)))
+
+
+def down_weight_norms(ddims: hna_down_dims, W_q, W_k, W_v, gamma_next, W_down, group_of_head_next,
+                      out=None, workspace=None) -> torch.Tensor:
+    _need_cuda(W_q, W_k, W_v, gamma_next, W_down)
+    L = lib()
+    dev = W_q.device
+    if out is None:
+        out = torch.empty((ddims.G, ddims.I), dtype=torch.float32, device=dev)
+    wsb = L.hna_down_workspace_bytes(ctypes.byref(ddims))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(L.hna_down_weight_norms(ctypes.byref(ddims), _ptr(W_q), _ptr(W_k), _ptr(W_v),
+                                   _ptr(gamma_next), _ptr(W_down), _map(group_of_head_next),
+                                   _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(dev)),
+           "hna_down_weight_norms")
+    return out
+
+
+def down_combine(c_down, n, out=None) -> torch.Tensor:
+    _need_cuda(c_down, n)
+    G, I = n.shape
+    if out is None:
+        out = torch.empty((I, G), dtype=torch.float32, device=n.device)
+    _check(lib().hna_down_combine(int(I), int(G), _ptr(c_down), _ptr(n), _ptr(out),
+                                  _stream(n.device)), "hna_down_combine")
+    return out

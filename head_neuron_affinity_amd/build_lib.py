@@ -1,0 +1,55 @@
+"""Build libhna.so (gfx950 only) from csrc/ with hipcc, in the package directory."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_PATH = os.path.join(PKG_DIR, "libhna.so")
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
+
+SOURCES = ["hna_api.hip", "k_affinity.hip", "k_gemm.hip", "k_small.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 VALU ops are disabled on purpose: only scalar fp32 VALU code.
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(line for line in (r.stderr or "").splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in line)
+    if r.returncode != 0:
+        raise RuntimeError("command failed: " + " ".join(cmd) + "\n" + err)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libhna.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        jobs.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        for msg in ex.map(_run, jobs):
+            if verbose and msg.strip():
+                print(msg, file=sys.stderr)
+    tmp = LIB_PATH + ".tmp"
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}", file=sys.stderr)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,373 @@
+// C ABI of libhna: argument validation, workspace sizing and kernel dispatch.
+// Every check runs on the host before anything is enqueued; failures return a
+// negative status and leave a thread-local message (see include/hna.h).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/hna.h"
+#include "hna_internal.h"
+
+using namespace hna;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(HNA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = std::getenv("HNA_DEBUG_SYNC");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+int finish(hipError_t e, hipStream_t st, const char* where) {
+  if (e != hipSuccess) return hip_fail(e, where);
+  if (debug_sync()) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, where);
+  }
+  g_last_error.clear();
+  return HNA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int esize_of(int dtype) { return dtype == HNA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                               \
+  do {                                                                               \
+    if (!(p)) return fail(HNA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);            \
+    if (!aligned16(p)) return fail(HNA_ERR_ALIGNMENT, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+int check_dtype(const char* fn, int dtype) {
+  if (dtype != HNA_F32 && dtype != HNA_BF16)
+    return fail(HNA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  return HNA_OK;
+}
+
+int check_heads(const char* fn, int hidden, int H, int G, int d) {
+  if (hidden < 1 || H < 1 || G < 1 || d < 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: dimensions must be positive (hidden=%d H=%d G=%d d=%d)",
+                fn, hidden, H, G, d);
+  if (H % G != 0)
+    return fail(HNA_ERR_INVALID_ARG, "%s: H=%d is not a multiple of G=%d", fn, H, G);
+  if (H > kMaxHeads) return fail(HNA_ERR_UNSUPPORTED, "%s: H=%d > %d", fn, H, kMaxHeads);
+  if (d % 16 != 0 || d > 128)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: head dim d=%d must be a multiple of 16 and <= 128", fn, d);
+  if (hidden % 8 != 0)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: hidden=%d must be a multiple of 8", fn, hidden);
+  return HNA_OK;
+}
+
+int check_dims(const char* fn, const hna_dims* dm) {
+  if (!dm) return fail(HNA_ERR_INVALID_ARG, "%s: dims is NULL", fn);
+  int rc = check_dtype(fn, dm->dtype);
+  if (rc) return rc;
+  if (dm->T < 0) return fail(HNA_ERR_INVALID_ARG, "%s: T=%lld < 0", fn, (long long)dm->T);
+  if (dm->I < 1) return fail(HNA_ERR_INVALID_ARG, "%s: I=%d < 1", fn, dm->I);
+  if (dm->T > ((int64_t)1 << 40))
+    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld too large", fn, (long long)dm->T);
+  if (dm->I > (1 << 26)) return fail(HNA_ERR_UNSUPPORTED, "%s: I=%d too large", fn, dm->I);
+  return check_heads(fn, dm->hidden, dm->H, dm->G, dm->d);
+}
+
+int check_map(const char* fn, const int32_t* map, int H, int G) {
+  if (!map) return fail(HNA_ERR_INVALID_ARG, "%s: group map is NULL", fn);
+  for (int h = 0; h < H; ++h)
+    if (map[h] < 0 || map[h] >= G)
+      return fail(HNA_ERR_INVALID_ARG, "%s: group_of_head[%d]=%d outside [0, %d)", fn, h, map[h], G);
+  return HNA_OK;
+}
+
+size_t fold_ws_bytes(const hna_dims* dm) {
+  return align256((size_t)dm->H * dm->d * dm->hidden * esize_of(dm->dtype));
+}
+
+size_t up_ws_bytes(const hna_dims* dm) {
+  const UpGeometry g = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  return align256(g.part_floats * sizeof(float));
+}
+
+size_t down_ws_transposed(const hna_down_dims* dm) {
+  return align256((size_t)dm->I * dm->hidden * esize_of(dm->dtype));
+}
+size_t down_ws_bytes(const hna_down_dims* dm) {
+  return down_ws_transposed(dm) + align256((size_t)(dm->H + 2 * dm->G) * dm->I * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hna_abi_version(void) { return HNA_ABI_VERSION; }
+
+const char* hna_status_string(int status) {
+  switch (status) {
+    case HNA_OK: return "HNA_OK";
+    case HNA_ERR_INVALID_ARG: return "HNA_ERR_INVALID_ARG";
+    case HNA_ERR_UNSUPPORTED: return "HNA_ERR_UNSUPPORTED";
+    case HNA_ERR_ALIGNMENT: return "HNA_ERR_ALIGNMENT";
+    case HNA_ERR_WORKSPACE: return "HNA_ERR_WORKSPACE";
+    case HNA_ERR_HIP: return "HNA_ERR_HIP";
+    default: return "HNA_ERR_UNKNOWN";
+  }
+}
+
+const char* hna_last_error(void) { return g_last_error.c_str(); }
+
+size_t hna_folded_bytes(const hna_dims* dm) {
+  if (check_dims("hna_folded_bytes", dm)) return 0;
+  return (size_t)dm->H * dm->d * 2 * round_up(dm->I, 32) * esize_of(dm->dtype);
+}
+
+size_t hna_fold_workspace_bytes(const hna_dims* dm) {
+  if (check_dims("hna_fold_workspace_bytes", dm)) return 0;
+  return fold_ws_bytes(dm);
+}
+
+int hna_fold_up_weights(const hna_dims* dm, const void* W_o, const float* gamma,
+                        const void* W_gate, const void* W_up, void* M, size_t M_bytes,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "hna_fold_up_weights";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  REQUIRE_PTR(W_o);
+  REQUIRE_PTR(gamma);
+  REQUIRE_PTR(W_gate);
+  REQUIRE_PTR(W_up);
+  REQUIRE_PTR(M);
+  REQUIRE_PTR(workspace);
+  const size_t need_m = hna_folded_bytes(dm);
+  if (M_bytes < need_m)
+    return fail(HNA_ERR_WORKSPACE, "%s: M has %zu bytes, needs %zu", fn, M_bytes, need_m);
+  const size_t need_ws = fold_ws_bytes(dm);
+  if (workspace_bytes < need_ws)
+    return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need_ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int Hd = dm->H * dm->d;
+  hipError_t e = launch_transpose(W_o, workspace, dm->hidden, Hd, esize_of(dm->dtype), st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  GemmParams p{};
+  p.X = workspace;
+  p.Y[0] = W_gate;
+  p.Y[1] = W_up;
+  p.s = gamma;
+  p.ldx = dm->hidden;
+  p.ldy = dm->hidden;
+  p.Mrows = Hd;
+  p.N = round_up(dm->I, 32);
+  p.Nvalid = dm->I;
+  p.K = dm->hidden;
+  p.M = M;
+  p.d = dm->d;
+  p.KB = p.N / 32;
+  p.S = dm->d / 16;
+  dim3 grid((p.N + 127) / 128, (Hd + 127) / 128, 2);
+  return finish(launch_gemm(p, dm->dtype, kEpiFold, grid, st), st, fn);
+}
+
+int hna_down_col_sqnorm(const hna_dims* dm, const void* W_down, float* wd_sq, void* stream) {
+  const char* fn = "hna_down_col_sqnorm";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  REQUIRE_PTR(W_down);
+  REQUIRE_PTR(wd_sq);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_col_sqnorm(W_down, dm->hidden, dm->I, dm->dtype, wd_sq, st), st, fn);
+}
+
+size_t hna_up_workspace_bytes(const hna_dims* dm) {
+  if (check_dims("hna_up_workspace_bytes", dm)) return 0;
+  return up_ws_bytes(dm);
+}
+
+int hna_affinity_up(const hna_dims* dm, const void* a, const void* g, const void* u,
+                    const float* r, const float* r_next, const void* M,
+                    const int32_t* group_of_head, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "hna_affinity_up";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  rc = check_map(fn, group_of_head, dm->H, dm->G);
+  if (rc) return rc;
+  REQUIRE_PTR(M);
+  const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  if (geo.lds_bytes > (size_t)kLdsBytes)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: needs %zu bytes of LDS (G=%d, d=%d) > %d", fn,
+                geo.lds_bytes, dm->G, dm->d, kLdsBytes);
+  if (dm->T == 0) {
+    g_last_error.clear();
+    return HNA_OK;
+  }
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(g);
+  REQUIRE_PTR(u);
+  REQUIRE_PTR(r);
+  if (r_next && !aligned16(r_next))
+    return fail(HNA_ERR_ALIGNMENT, "%s: r_next is not 16-byte aligned", fn);
+  REQUIRE_PTR(workspace);
+  const size_t need = up_ws_bytes(dm);
+  if (workspace_bytes < need)
+    return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  UpParams p{};
+  p.a = a;
+  p.g = g;
+  p.u = u;
+  p.r = r;
+  p.r_next = r_next;
+  p.M = M;
+  p.part = static_cast<float*>(workspace);
+  p.T = dm->T;
+  p.H = dm->H;
+  p.G = dm->G;
+  p.d = dm->d;
+  p.I = dm->I;
+  p.I32 = geo.I32;
+  p.n_tt = geo.n_tt;
+  p.n_kt = geo.n_kt;
+  p.n_chunks = geo.n_chunks;
+  p.n_ktg = geo.n_ktg;
+  p.n_st = geo.n_st;
+  int n = 0;
+  for (int gg = 0; gg < dm->G; ++gg)
+    for (int h = 0; h < dm->H; ++h)
+      if (group_of_head[h] == gg) {
+        p.head_order[n] = (int8_t)h;
+        p.head_group[n] = (int8_t)gg;
+        ++n;
+      }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_affinity_up(p, dm->dtype, geo.lds_bytes, geo.grid, st), st, fn);
+}
+
+int hna_finalize_up(const hna_dims* dm, const float* wd_sq, float scale, int flags,
+                    const void* workspace, size_t workspace_bytes, float* S_fo, float* S_add,
+                    float* c_down, void* stream) {
+  const char* fn = "hna_finalize_up";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  if (flags & ~HNA_ACCUMULATE) return fail(HNA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+  REQUIRE_PTR(wd_sq);
+  REQUIRE_PTR(S_fo);
+  REQUIRE_PTR(S_add);
+  if (c_down && !aligned16(c_down))
+    return fail(HNA_ERR_ALIGNMENT, "%s: c_down is not 16-byte aligned", fn);
+  const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  if (geo.n_chunks > 0) {
+    REQUIRE_PTR(workspace);
+    const size_t need = up_ws_bytes(dm);
+    if (workspace_bytes < need)
+      return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_finalize_up(static_cast<const float*>(workspace), geo.n_chunks, dm->G,
+                                   dm->I, geo.I32, wd_sq, scale, flags & HNA_ACCUMULATE, S_fo,
+                                   S_add, c_down, st),
+                st, fn);
+}
+
+size_t hna_down_workspace_bytes(const hna_down_dims* dm) {
+  if (!dm || check_dtype("hna_down_workspace_bytes", dm->dtype) ||
+      check_heads("hna_down_workspace_bytes", dm->hidden, dm->H, dm->G, dm->d) || dm->I < 1)
+    return 0;
+  return down_ws_bytes(dm);
+}
+
+int hna_down_weight_norms(const hna_down_dims* dm, const void* W_q, const void* W_k,
+                          const void* W_v, const float* gamma_next, const void* W_down,
+                          const int32_t* group_of_head_next, float* n, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const char* fn = "hna_down_weight_norms";
+  if (!dm) return fail(HNA_ERR_INVALID_ARG, "%s: dims is NULL", fn);
+  int rc = check_dtype(fn, dm->dtype);
+  if (rc) return rc;
+  rc = check_heads(fn, dm->hidden, dm->H, dm->G, dm->d);
+  if (rc) return rc;
+  if (dm->I < 1) return fail(HNA_ERR_INVALID_ARG, "%s: I=%d < 1", fn, dm->I);
+  rc = check_map(fn, group_of_head_next, dm->H, dm->G);
+  if (rc) return rc;
+  REQUIRE_PTR(W_q);
+  REQUIRE_PTR(W_k);
+  REQUIRE_PTR(W_v);
+  REQUIRE_PTR(gamma_next);
+  REQUIRE_PTR(W_down);
+  REQUIRE_PTR(n);
+  REQUIRE_PTR(workspace);
+  const size_t need = down_ws_bytes(dm);
+  if (workspace_bytes < need)
+    return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int es = esize_of(dm->dtype);
+  hipError_t e = launch_transpose(W_down, workspace, dm->hidden, dm->I, es, st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  float* seg_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + down_ws_transposed(dm));
+  GemmParams p{};
+  p.X = workspace;
+  p.Y[0] = W_q;
+  p.Y[1] = W_k;
+  p.Y[2] = W_v;
+  p.s = gamma_next;
+  p.ldx = dm->hidden;
+  p.ldy = dm->hidden;
+  p.Mrows = dm->I;
+  p.N = dm->d;
+  p.Nvalid = dm->d;
+  p.K = dm->hidden;
+  p.seg_part = seg_part;
+  p.H_next = dm->H;
+  p.G_next = dm->G;
+  p.d_next = dm->d;
+  const int nseg = dm->H + 2 * dm->G;
+  e = launch_gemm(p, dm->dtype, kEpiSegSq, dim3((dm->I + 127) / 128, nseg, 1), st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  // segments of group g': its query heads (ascending), then its k rows, then its v rows
+  int16_t seg_list[3 * kMaxHeads];
+  int16_t start[kMaxHeads + 1];
+  int c = 0;
+  for (int gg = 0; gg < dm->G; ++gg) {
+    start[gg] = (int16_t)c;
+    for (int h = 0; h < dm->H; ++h)
+      if (group_of_head_next[h] == gg) seg_list[c++] = (int16_t)h;
+    seg_list[c++] = (int16_t)(dm->H + gg);
+    seg_list[c++] = (int16_t)(dm->H + dm->G + gg);
+  }
+  start[dm->G] = (int16_t)c;
+  return finish(launch_down_group_sum(seg_part, seg_list, start, dm->G, dm->I, n, st), st, fn);
+}
+
+int hna_down_combine(int32_t I, int32_t G_next, const float* c_down, const float* n,
+                     float* S_down, void* stream) {
+  const char* fn = "hna_down_combine";
+  if (I < 1 || G_next < 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: I=%d and G_next=%d must be positive", fn, I, G_next);
+  REQUIRE_PTR(c_down);
+  REQUIRE_PTR(n);
+  REQUIRE_PTR(S_down);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_down_combine(c_down, n, I, G_next, S_down, st), st, fn);
+}
+
+}  // extern "C"

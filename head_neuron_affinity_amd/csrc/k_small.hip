@@ -1,0 +1,129 @@
+// Small bandwidth-bound kernels around the two matrix-core passes:
+//   * transpose (W_o -> W_o^T and W_down -> W_down^T, so the GEMM reads both
+//     operands along the contracted dimension);
+//   * ||w^d_k||^2, the squared norms of W_down's columns (section 3,
+//     "Affinity scores": the FO score's write-size factor);
+//   * the down edge's group sum n[g', k] over the q/k/v row segments of each
+//     next-layer KV group, and S_down[k, g'] = c_k n[g', k].
+#include "hna_internal.h"
+
+namespace hna {
+namespace {
+
+constexpr int TD = 64;
+
+// out[c][r] = in[r][c]; 64 x 64 tiles through LDS, 256 threads.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in, E* __restrict__ out,
+                                                        int rows, int cols) {
+  __shared__ E tile[TD][TD + 1];
+  const int r0 = blockIdx.y * TD, c0 = blockIdx.x * TD;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < TD; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = in[(int64_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < TD; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) out[(int64_t)c * rows + r] = tile[tx][i];
+  }
+}
+
+// out[k] = sum_r W[r][k]^2 for a row-major [rows, cols] matrix.
+// 64 columns per block, 4 row lanes; the 4 lane sums are added in fixed order.
+template <int BF16>
+__global__ __launch_bounds__(256) void col_sqnorm_kernel(const void* __restrict__ Wv, int rows,
+                                                         int cols, float* __restrict__ out) {
+  __shared__ float part[4][64];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cx;
+  float s = 0.f;
+  if (c < cols) {
+    for (int r = ry; r < rows; r += 4) {
+      float v;
+      if (BF16)
+        v = bf16_bits_to_f32(static_cast<const uint16_t*>(Wv)[(int64_t)r * cols + c]);
+      else
+        v = static_cast<const float*>(Wv)[(int64_t)r * cols + c];
+      s = fmaf(v, v, s);
+    }
+  }
+  part[ry][cx] = s;
+  __syncthreads();
+  if (ry == 0 && c < cols) out[c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
+}
+
+struct SegList {
+  int16_t seg[3 * kMaxHeads];      // segment ids, grouped by next-layer KV group
+  int16_t start[kMaxHeads + 1];    // group g' owns seg[start[g'] .. start[g'+1])
+};
+
+// n[g][k] = sum of seg_part[s][k] over the segments of group g, in list order.
+__global__ __launch_bounds__(256) void down_group_sum_kernel(const float* __restrict__ seg_part,
+                                                             const SegList sl, int G, int I,
+                                                             float* __restrict__ n) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)G * I) return;
+  const int g = (int)(idx / I), k = (int)(idx - (int64_t)g * I);
+  float s = 0.f;
+  for (int i = sl.start[g]; i < sl.start[g + 1]; ++i) s += seg_part[(int64_t)sl.seg[i] * I + k];
+  n[idx] = s;
+}
+
+__global__ __launch_bounds__(256) void down_combine_kernel(const float* __restrict__ c,
+                                                           const float* __restrict__ n, int I,
+                                                           int G, float* __restrict__ S_down) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)G * I) return;
+  const int k = (int)(idx / G), g = (int)(idx - (int64_t)k * G);
+  S_down[idx] = c[k] * n[(int64_t)g * I + k];
+}
+
+}  // namespace
+
+hipError_t launch_transpose(const void* in, void* out, int rows, int cols, int esize,
+                            hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid((cols + TD - 1) / TD, (rows + TD - 1) / TD);
+  if (esize == 2)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), rows, cols);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st,
+                       static_cast<const float*>(in), static_cast<float*>(out), rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_sqnorm(const void* W, int rows, int cols, int dtype, float* out,
+                             hipStream_t st) {
+  if (cols == 0) return hipSuccess;
+  dim3 grid((cols + 63) / 64);
+  if (dtype == 1) hipLaunchKernelGGL(col_sqnorm_kernel<1>, grid, dim3(256), 0, st, W, rows, cols, out);
+  else hipLaunchKernelGGL(col_sqnorm_kernel<0>, grid, dim3(256), 0, st, W, rows, cols, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_group_sum(const float* seg_part, const int16_t* seg_list,
+                                 const int16_t* group_start, int G_next, int I, float* n,
+                                 hipStream_t st) {
+  SegList sl{};
+  const int nseg = group_start[G_next];
+  for (int i = 0; i < nseg; ++i) sl.seg[i] = seg_list[i];
+  for (int g = 0; g <= G_next; ++g) sl.start[g] = group_start[g];
+  const int64_t total = (int64_t)G_next * I;
+  hipLaunchKernelGGL(down_group_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     seg_part, sl, G_next, I, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_combine(const float* c, const float* n, int I, int G_next, float* S_down,
+                               hipStream_t st) {
+  const int64_t total = (int64_t)G_next * I;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(down_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     c, n, I, G_next, S_down);
+  return hipGetLastError();
+}
+
+}  // namespace hna

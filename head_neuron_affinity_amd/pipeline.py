@@ -1,0 +1,98 @@
+"""One layer's affinity pass through the C ABI, with buffers allocated once.
+
+The pass follows section 3 ("Affinity scores") of "Affinity-Aware Sharding for
+Delayed Tensor Parallelism": fold the up weights, take ||w^d_k||^2, run the
+hot kernel over the calibration tokens, reduce the partial sums into S_fo and
+S_add (and the down-edge moment), then the down edge's weight norms and
+S_down.  Every step is a libhna call on torch's current stream; this module
+only owns the buffers.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _binding as B
+
+
+class AffinityPass:
+    def __init__(self, T: int, hidden: int, H: int, G: int, d: int, I: int, dtype: torch.dtype,
+                 device="cuda", with_down: bool = True, H_next: Optional[int] = None,
+                 G_next: Optional[int] = None, d_next: Optional[int] = None):
+        dev = torch.device(device)
+        code = B.HNA_BF16 if dtype == torch.bfloat16 else B.HNA_F32
+        self.dims = B.make_dims(T, hidden, H, G, d, I, code)
+        self.T = T
+        self.device = dev
+        u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        L = B.lib()
+        import ctypes
+        self.M = torch.empty(B.folded_bytes(self.dims), **u8)
+        self.fold_ws = torch.empty(max(16, L.hna_fold_workspace_bytes(ctypes.byref(self.dims))), **u8)
+        self.up_ws = torch.empty(max(16, B.up_workspace_bytes(self.dims)), **u8)
+        self.wd_sq = torch.empty(I, **f32)
+        self.S_fo = torch.empty((G, I), **f32)
+        self.S_add = torch.empty((G, I), **f32)
+        self.c_down = torch.empty(I, **f32)
+        self.with_down = with_down
+        if with_down:
+            Hn = H if H_next is None else H_next
+            Gn = G if G_next is None else G_next
+            dn = d if d_next is None else d_next
+            self.ddims = B.hna_down_dims(hidden, I, Hn, Gn, dn, code)
+            self.down_ws = torch.empty(max(16, B.down_workspace_bytes(self.ddims)), **u8)
+            self.n_down = torch.empty((Gn, I), **f32)
+            self.S_down = torch.empty((I, Gn), **f32)
+
+    # -- individual steps -------------------------------------------------
+    def fold(self, layer):
+        B.fold_up_weights(self.dims, layer["W_o"], layer["gamma"], layer["W_gate"], layer["W_up"],
+                          out=self.M, workspace=self.fold_ws)
+        B.down_col_sqnorm(self.dims, layer["W_down"], out=self.wd_sq)
+
+    def hot(self, layer, group_of_head: Sequence[int]):
+        B.affinity_up(self.dims, layer["a"], layer["g"], layer["u"], layer["r"],
+                      layer.get("r_next") if self.with_down else None, self.M, group_of_head,
+                      workspace=self.up_ws)
+
+    def finalize(self, scale: float, accumulate: bool = False):
+        B.finalize_up(self.dims, self.wd_sq, self.up_ws, scale, accumulate=accumulate,
+                      S_fo=self.S_fo, S_add=self.S_add,
+                      c_down=self.c_down if self.with_down else None, want_c=self.with_down)
+
+    def down(self, layer, group_of_head_next: Sequence[int]):
+        B.down_weight_norms(self.ddims, layer["W_q"], layer["W_k"], layer["W_v"],
+                            layer["gamma_next"], layer["W_down"], group_of_head_next,
+                            out=self.n_down, workspace=self.down_ws)
+        B.down_combine(self.c_down, self.n_down, out=self.S_down)
+
+    # -- whole pass ---------------------------------------------------------
+    def run(self, layer: Dict[str, torch.Tensor], scale: Optional[float] = None) -> Dict[str, torch.Tensor]:
+        grp = [int(x) for x in layer["group_of_head"].tolist()]
+        self.fold(layer)
+        self.hot(layer, grp)
+        self.finalize(1.0 / max(self.T, 1) if scale is None else scale)
+        out = {"S_fo": self.S_fo, "S_add": self.S_add}
+        if self.with_down:
+            self.down(layer, [int(x) for x in layer["group_of_head_next"].tolist()])
+            out.update({"c_down": self.c_down, "n_down": self.n_down, "S_down": self.S_down})
+        return out
+
+
+def pass_for_layer(layer: Dict[str, torch.Tensor], with_down: bool = True) -> AffinityPass:
+    T, H, d = layer["a"].shape
+    I, hidden = layer["W_gate"].shape
+    G = int(max(layer["group_of_head"].tolist())) + 1
+    kw = {}
+    if with_down:
+        kw = dict(H_next=layer["W_q"].shape[0] // d, G_next=layer["W_k"].shape[0] // d, d_next=d)
+    return AffinityPass(T, hidden, H, G, d, I, layer["a"].dtype, device=layer["a"].device,
+                        with_down=with_down and "W_q" in layer, **kw)
+
+
+def affinity_layer(layer: Dict[str, torch.Tensor], with_down: bool = True) -> Dict[str, torch.Tensor]:
+    """Run the whole pass on one layer dict (tensors on the GPU) and return the scores."""
+    ap = pass_for_layer(layer, with_down=with_down)
+    return ap.run(layer)

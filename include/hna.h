@@ -1,0 +1,183 @@
+/*
+ * hna.h -- C ABI of the head-to-neuron affinity library (gfx950 / MI355X).
+ *
+ * The library computes the calibration scores of "Affinity-Aware Sharding for
+ * Delayed Tensor Parallelism" (E. de Reynal, arXiv:2609.13846), section 3,
+ * paragraph "Affinity scores" and equation (5):
+ *
+ *   p_h      = gamma * (a_h W_o^(h)T) / r        head h's piece of the FFN input
+ *   Delta_hk = silu'(g_k) u_k (p_h . w^g_k) + silu(g_k) (p_h . w^u_k)     (5)
+ *   S_fo[g,k]  = sum_{h in g} E_t[Delta_hk^2] ||w^d_k||^2          [G x I]
+ *   S_add[g,k] = sum_{h in g} E_t[(p_h . w^g_k)^2 + (p_h . w^u_k)^2] [G x I]
+ *   S_down[k,g'] = E_t[alpha_k^2 / r'^2] ||W^qkv_g' (gamma' * w^d_k)||^2
+ *                  with alpha_k = silu(g_k) u_k                     [I x G']
+ *
+ * Conventions shared by every call
+ *   - Matrices are row-major, linear-layer (out, in) order:
+ *       W_o [hidden, H*d]  (head h owns columns h*d .. h*d+d-1)
+ *       W_gate, W_up [I, hidden]  (row k is w^g_k, w^u_k)
+ *       W_down [hidden, I]        (column k is w^d_k)
+ *       W_q [H'*d', hidden], W_k, W_v [G'*d', hidden]  (next layer)
+ *     Activations: a [T, H, d] (token-major), g, u [T, I]; r, r_next [T].
+ *   - dtype HNA_BF16: a, g, u and all weight matrices are bfloat16; HNA_F32:
+ *     they are float32.  gamma, gamma_next, r, r_next, wd_sq and every output
+ *     are float32 in both cases.  Accumulation is float32.
+ *   - Every tensor pointer is a device pointer owned by the caller; the
+ *     library allocates no memory and keeps no state between calls.  Scratch
+ *     space is the caller's workspace.  group maps are host arrays, read
+ *     during the call only.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; nothing synchronises the host except
+ *     when the environment variable HNA_DEBUG_SYNC=1 is set.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     On failure a negative hna_status is returned, a thread-local message
+ *     is available from hna_last_error(), and nothing has been launched.
+ *     Launch failures return HNA_ERR_HIP.  Nothing prints, aborts or throws.
+ *   - Device pointers must be 16-byte aligned (HNA_ERR_ALIGNMENT otherwise).
+ *   - The library is reentrant; its only global mutable state is the
+ *     thread-local error text.  Calls that share a workspace or an output
+ *     must be ordered on one stream by the caller.
+ *
+ * Supported shapes: H <= 128, 1 <= G <= H, H % G == 0, 0 <= group_of_head[h]
+ * < G; d a multiple of 16 with d <= 128; hidden >= 1; I >= 1; T >= 0.
+ * Others return HNA_ERR_UNSUPPORTED.
+ */
+#ifndef HNA_H
+#define HNA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HNA_ABI_VERSION 1
+
+typedef enum hna_status {
+  HNA_OK = 0,
+  HNA_ERR_INVALID_ARG = -1,  /* bad dimension, null pointer, bad map, bad flag */
+  HNA_ERR_UNSUPPORTED = -2,  /* valid but outside the supported shapes/dtypes */
+  HNA_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned */
+  HNA_ERR_WORKSPACE = -4,    /* workspace or output buffer too small */
+  HNA_ERR_HIP = -5           /* the HIP runtime reported an error */
+} hna_status;
+
+typedef enum hna_dtype { HNA_F32 = 0, HNA_BF16 = 1 } hna_dtype;
+
+/* flags for hna_finalize_up */
+enum { HNA_ACCUMULATE = 1 }; /* add into S_fo/S_add/c_down instead of overwriting */
+
+/* Shape of one layer's up edge (heads of layer i -> neurons of layer i). */
+typedef struct hna_dims {
+  int64_t T;       /* calibration tokens in this call */
+  int32_t hidden;  /* residual width */
+  int32_t H;       /* query heads */
+  int32_t G;       /* KV groups */
+  int32_t d;       /* head dim */
+  int32_t I;       /* FFN neurons */
+  int32_t dtype;   /* hna_dtype */
+} hna_dims;
+
+/* Shape of one down edge (neurons of layer i -> KV groups of layer i+1). */
+typedef struct hna_down_dims {
+  int32_t hidden;  /* residual width (shared by both layers) */
+  int32_t I;       /* neurons of layer i (columns of W_down) */
+  int32_t H;       /* query heads of layer i+1 */
+  int32_t G;       /* KV groups of layer i+1 */
+  int32_t d;       /* head dim of layer i+1 */
+  int32_t dtype;   /* hna_dtype of W_q, W_k, W_v, W_down */
+} hna_down_dims;
+
+int hna_abi_version(void);
+const char* hna_status_string(int status);
+/* Message of the calling thread's most recent failure ("" if none). */
+const char* hna_last_error(void);
+
+/* ---------------------------------------------------------------- up edge */
+
+/* Bytes of the folded weight M for `dims` (see hna_fold_up_weights). */
+size_t hna_folded_bytes(const hna_dims* dims);
+/* Bytes of workspace hna_fold_up_weights needs (a transposed copy of W_o). */
+size_t hna_fold_workspace_bytes(const hna_dims* dims);
+
+/*
+ * Weight fold.  Because p_h . w_k = (1/r) a_h . (W_o^(h)T (gamma * w_k)) (the
+ * decomposition of section 3, "Affinity scores", with the two finite sums
+ * exchanged), the folded weights
+ *     M_h = W_o^(h)T diag(gamma) [W_gate; W_up]^T          [H, d, 2I]
+ * turn the per-head pieces into one short contraction over d per token.
+ * Writes M (hna_folded_bytes(dims) bytes, dtype of `dims`) in the internal
+ * layout the affinity kernel reads; callers treat it as opaque.  Float32
+ * accumulation; bf16 output is rounded once at the end.
+ */
+int hna_fold_up_weights(const hna_dims* dims, const void* W_o, const float* gamma,
+                        const void* W_gate, const void* W_up,
+                        void* M, size_t M_bytes,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* wd_sq[k] = ||w^d_k||^2, the squared norm of column k of W_down [hidden, I]. */
+int hna_down_col_sqnorm(const hna_dims* dims, const void* W_down, float* wd_sq,
+                        void* stream);
+
+/* Bytes of workspace hna_affinity_up / hna_finalize_up need for `dims`. */
+size_t hna_up_workspace_bytes(const hna_dims* dims);
+
+/*
+ * The hot pass (equation (5) and the two up scores).  For every token t of
+ * this call, head h and neuron k it forms (p_h . w^g_k, p_h . w^u_k) from a
+ * and M, the operating-point coefficients silu'(g)u/r and silu(g)/r, the
+ * damage Delta_hk, and accumulates sum_t Delta^2, sum_t (p.w^g)^2 + (p.w^u)^2
+ * over the query heads of each KV group, plus sum_t (silu(g)u/r_next)^2 when
+ * r_next is not NULL.  Token-block partial sums go to `workspace`
+ * (>= hna_up_workspace_bytes); nothing of size T x H x I is ever written.
+ *   a [T,H,d], g, u [T,I] (dtype of dims); r [T], r_next [T] or NULL (fp32);
+ *   M from hna_fold_up_weights with the same dims;
+ *   group_of_head: host int32 [H], values in [0, G).
+ * The partial sums are consumed by hna_finalize_up with the same dims and
+ * workspace; T = 0 is allowed and yields zero partial sums.
+ */
+int hna_affinity_up(const hna_dims* dims, const void* a, const void* g, const void* u,
+                    const float* r, const float* r_next, const void* M,
+                    const int32_t* group_of_head,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fixed-order reduction of the partial sums left by hna_affinity_up:
+ *   S_fo[g*I+k]  (+)= scale * wd_sq[k] * sum_t sum_{h in g} Delta^2
+ *   S_add[g*I+k] (+)= scale * sum_t sum_{h in g} ((p.w^g)^2 + (p.w^u)^2)
+ *   c_down[k]    (+)= scale * sum_t (silu(g_k) u_k / r_next)^2   (if not NULL)
+ * `scale` is 1/T_total (the mean over all calibration tokens, possibly fed in
+ * several chunks with HNA_ACCUMULATE).  S_fo, S_add [G, I] and c_down [I]
+ * are fp32; c_down may be NULL (then r_next must have been NULL).  The result
+ * is deterministic: no atomics, fixed summation order.
+ */
+int hna_finalize_up(const hna_dims* dims, const float* wd_sq, float scale, int flags,
+                    const void* workspace, size_t workspace_bytes,
+                    float* S_fo, float* S_add, float* c_down, void* stream);
+
+/* -------------------------------------------------------------- down edge */
+
+/* Bytes of workspace hna_down_weight_norms needs. */
+size_t hna_down_workspace_bytes(const hna_down_dims* dims);
+
+/*
+ * Down-edge weight part (section 3, "Affinity scores"):
+ *   n[g', k] = ||b_g'k||^2,  b_g'k = W^qkv_g' (gamma_next * w^d_k)
+ * where W^qkv_g' stacks the W_q rows of the next-layer query heads h' with
+ * group_of_head_next[h'] = g', then rows g'*d'..g'*d'+d'-1 of W_k and of W_v.
+ * n is fp32 [G', I].  b is never stored.
+ */
+int hna_down_weight_norms(const hna_down_dims* dims, const void* W_q, const void* W_k,
+                          const void* W_v, const float* gamma_next, const void* W_down,
+                          const int32_t* group_of_head_next, float* n,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* S_down[k*G'+g'] = c_down[k] * n[g'*I+k]   (fp32, [I, G']). */
+int hna_down_combine(int32_t I, int32_t G_next, const float* c_down, const float* n,
+                     float* S_down, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HNA_H */

@@ -1,0 +1,183 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point,
+and rejects bad arguments on the host before launching anything.
+
+Every call below fails validation on purpose (fake, never-dereferenced device
+addresses are used only where a check earlier in the argument list fires), so
+no HIP kernel is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import threading
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hna.h")
+
+
+def _lib():
+    import head_neuron_affinity_amd as hna
+    if not os.path.exists(hna.LIB_PATH):
+        pytest.skip("libhna.so not built (run __graft_entry__.build())")
+    return hna
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(hna_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_expected_entry_points():
+    hna = _lib()
+    assert declared_functions() == sorted(hna.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    hna = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", hna.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(hna_[a-z_]+)$", out, flags=re.M))
+    missing = set(declared_functions()) - exported
+    assert not missing, f"declared but not exported: {missing}"
+    L = hna.lib()
+    for name in declared_functions():
+        assert getattr(L, name) is not None
+
+
+def test_version_and_status_strings():
+    hna = _lib()
+    L = hna.lib()
+    assert L.hna_abi_version() == 1
+    assert hna.status_string(0) == "HNA_OK"
+    assert hna.status_string(-4) == "HNA_ERR_WORKSPACE"
+    assert hna.status_string(-99) == "HNA_ERR_UNKNOWN"
+
+
+FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced
+MIS = FAKE + 2          # misaligned
+
+
+def dims(hna, T=256, hidden=64, H=4, G=2, d=16, I=128, dtype=1):
+    return hna.make_dims(T, hidden, H, G, d, I, dtype)
+
+
+def call_up(hna, dm, a=FAKE, g=FAKE, u=FAKE, r=FAKE, rn=None, M=FAKE, grp=(0, 0, 1, 1),
+            ws=FAKE, wsb=1 << 40):
+    L = hna.lib()
+    arr = (ctypes.c_int32 * len(grp))(*grp) if grp is not None else None
+    vp = ctypes.c_void_p
+    return L.hna_affinity_up(ctypes.byref(dm), vp(a), vp(g), vp(u), vp(r), vp(rn) if rn else None,
+                             vp(M), arr, vp(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=4, G=3), -1),          # H not a multiple of G
+    (dict(d=20), -2),              # d not a multiple of 16
+    (dict(d=144), -2),             # d > 128
+    (dict(hidden=60), -2),         # hidden not a multiple of 8
+    (dict(dtype=7), -1),           # unknown dtype
+    (dict(I=0), -1),
+    (dict(T=-1), -1),
+    (dict(H=0), -1),
+    (dict(H=256, G=2), -2),        # too many heads
+])
+def test_bad_dims_rejected(kw, status):
+    hna = _lib()
+    rc = call_up(hna, dims(hna, **kw), grp=tuple([0] * max(1, kw.get("H", 4))))
+    assert rc == status, hna.last_error()
+    assert hna.last_error() != ""
+
+
+def test_null_dims_pointer():
+    hna = _lib()
+    L = hna.lib()
+    assert L.hna_affinity_up(None, None, None, None, None, None, None, None, None, 0, None) == -1
+    assert "dims is NULL" in hna.last_error()
+
+
+def test_bad_group_map():
+    hna = _lib()
+    assert call_up(hna, dims(hna), grp=(0, 0, 2, 1)) == -1
+    assert "group_of_head[2]" in hna.last_error()
+    assert call_up(hna, dims(hna), grp=(0, -1, 1, 1)) == -1
+    assert call_up(hna, dims(hna), grp=None) == -1
+
+
+def test_null_and_misaligned_pointers():
+    hna = _lib()
+    assert call_up(hna, dims(hna), a=0) == -1
+    assert "a is NULL" in hna.last_error()
+    assert call_up(hna, dims(hna), g=MIS) == -3
+    assert "g is not 16-byte aligned" in hna.last_error()
+    assert call_up(hna, dims(hna), M=0) == -1
+    assert call_up(hna, dims(hna), rn=MIS) == -3
+
+
+def test_workspace_too_small():
+    hna = _lib()
+    dm = dims(hna)
+    need = hna.up_workspace_bytes(dm)
+    assert need > 0
+    assert call_up(hna, dm, wsb=need - 1) == -4
+    assert "workspace" in hna.last_error()
+
+
+def test_workspace_sizes_follow_geometry():
+    hna = _lib()
+    # Qwen3-0.6B-shaped layer: 512 token tiles of 128 -> 64 chunks of 8 tiles;
+    # partial sums [64][2G+1][I] fp32.
+    dm = hna.make_dims(65536, 1024, 16, 8, 128, 3072, 1)
+    assert hna.up_workspace_bytes(dm) == 64 * 17 * 3072 * 4
+    assert hna.folded_bytes(dm) == 16 * 128 * 2 * 3072 * 2
+    # ragged neuron count pads to 32; T = 1 is one chunk
+    dm = hna.make_dims(1, 64, 4, 2, 16, 100, 0)
+    assert hna.up_workspace_bytes(dm) == ((5 * 128 * 4 + 255) // 256) * 256
+    assert hna.folded_bytes(dm) == 4 * 16 * 2 * 128 * 4
+    dd = hna.hna_down_dims(1024, 3072, 16, 8, 128, 1)
+    assert hna.down_workspace_bytes(dd) == 3072 * 1024 * 2 + 32 * 3072 * 4
+
+
+def test_lds_limit_reported_unsupported():
+    hna = _lib()
+    # fp32, d = 128 and 32 KV groups need more than 160 KiB of LDS
+    dm = hna.make_dims(256, 4096, 32, 32, 128, 128, 0)
+    rc = call_up(hna, dm, grp=tuple(range(32)))
+    assert rc == -2 and "LDS" in hna.last_error()
+
+
+def test_finalize_and_other_calls_validate():
+    hna = _lib()
+    L = hna.lib()
+    vp = ctypes.c_void_p
+    dm = dims(hna)
+    assert L.hna_finalize_up(ctypes.byref(dm), vp(FAKE), 1.0, 2, vp(FAKE), 1 << 30, vp(FAKE),
+                             vp(FAKE), None, None) == -1        # unknown flag
+    assert L.hna_finalize_up(ctypes.byref(dm), None, 1.0, 0, vp(FAKE), 1 << 30, vp(FAKE),
+                             vp(FAKE), None, None) == -1        # wd_sq NULL
+    assert L.hna_fold_up_weights(ctypes.byref(dm), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                 vp(FAKE), 10, vp(FAKE), 1 << 30, None) == -4  # M too small
+    assert L.hna_down_col_sqnorm(ctypes.byref(dims(hna, d=8)), vp(FAKE), vp(FAKE), None) == -2
+    dd = hna.hna_down_dims(64, 128, 4, 2, 16, 1)
+    grp = (ctypes.c_int32 * 4)(0, 1, 0, 5)
+    assert L.hna_down_weight_norms(ctypes.byref(dd), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                   vp(FAKE), grp, vp(FAKE), vp(FAKE), 1 << 30, None) == -1
+    assert L.hna_down_combine(0, 2, vp(FAKE), vp(FAKE), vp(FAKE), None) == -1
+    assert L.hna_down_combine(8, 2, vp(MIS), vp(FAKE), vp(FAKE), None) == -3
+
+
+def test_error_text_is_thread_local():
+    hna = _lib()
+    call_up(hna, dims(hna, d=20))
+    mine = hna.last_error()
+    seen = []
+
+    def other():
+        seen.append(hna.last_error())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert mine and seen == [""]

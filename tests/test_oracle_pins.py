@@ -304,6 +304,19 @@ def test_down_norms_sum_to_full_projection_norm():
     np.testing.assert_allclose(n.sum(0), full, rtol=1e-12)
 
 
+def test_down_restricted_columns_match_full():
+    L = tiny(H=4, G=2, I=9)
+    ks = [8, 1, 3]
+    c = oracle.down_moment(L["g"], L["u"], L["r_next"])
+    n = oracle.down_weight_norms(L["W_q"], L["W_k"], L["W_v"], L["gamma_next"], L["W_down"],
+                                 L["group_of_head_next"], G_next=2)
+    c_s = oracle.down_moment(L["g"], L["u"], L["r_next"], neurons=ks)
+    n_s = oracle.down_weight_norms(L["W_q"], L["W_k"], L["W_v"], L["gamma_next"], L["W_down"],
+                                   L["group_of_head_next"], G_next=2, neurons=ks)
+    np.testing.assert_allclose(c_s, c[ks], rtol=1e-14)
+    np.testing.assert_allclose(n_s, n[:, ks], rtol=1e-13)
+
+
 def test_down_moment_chunking():
     L = tiny(T=50)
     c1 = oracle.down_moment(L["g"], L["u"], L["r_next"], token_chunk=7)
