@@ -164,14 +164,20 @@ def affinity_up(a, g, u, r, gamma, W_o, W_gate, W_up, W_down, group_of_head,
     return S_fo, S_add
 
 
-def down_moment(g, u, r_next, token_chunk: int = 8192) -> np.ndarray:
-    """c_k = E_t[alpha_k^2 / r'^2] with alpha_k = silu(g_k) u_k (paper section 3)."""
+def down_moment(g, u, r_next, token_chunk: int = 8192,
+                neurons: Optional[Sequence[int]] = None) -> np.ndarray:
+    """c_k = E_t[alpha_k^2 / r'^2] with alpha_k = silu(g_k) u_k (paper section 3).
+
+    ``neurons`` restricts the result to those columns (same arithmetic)."""
     r_next = _f64(r_next)
     T = r_next.shape[0]
     acc = None
     for t0 in range(0, T, token_chunk):
         t1 = min(T, t0 + token_chunk)
         g_c, u_c = _f64(g[t0:t1]), _f64(u[t0:t1])
+        if neurons is not None:
+            ks = np.asarray(neurons, dtype=np.int64)
+            g_c, u_c = g_c[:, ks], u_c[:, ks]
         _, silu, _ = silu_parts(g_c)
         q = silu * u_c / r_next[t0:t1, None]
         s = np.sum(q * q, axis=0)
@@ -189,10 +195,15 @@ def qkv_rows_of_group(group_of_head_next, G_next: int, d_next: int, gp: int):
 
 
 def down_weight_norms(W_q, W_k, W_v, gamma_next, W_down, group_of_head_next,
-                      G_next: Optional[int] = None) -> np.ndarray:
-    """n[g, k] = ||b_gk||^2 with b_gk = W^qkv_g (gamma' * w^d_k) (paper section 3)."""
+                      G_next: Optional[int] = None,
+                      neurons: Optional[Sequence[int]] = None) -> np.ndarray:
+    """n[g, k] = ||b_gk||^2 with b_gk = W^qkv_g (gamma' * w^d_k) (paper section 3).
+
+    ``neurons`` restricts the result to those columns of W_down (same arithmetic)."""
     W_q, W_k, W_v = _f64(W_q), _f64(W_k), _f64(W_v)
     gamma_next, W_down = _f64(gamma_next), _f64(W_down)
+    if neurons is not None:
+        W_down = W_down[:, np.asarray(neurons, dtype=np.int64)]
     grp = np.asarray(group_of_head_next, dtype=np.int64).reshape(-1)
     if G_next is None:
         G_next = int(grp.max()) + 1
