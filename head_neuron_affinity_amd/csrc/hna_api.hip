@@ -260,7 +260,7 @@ int hna_affinity_up(const hna_dims* dm, const void* a, const void* g, const void
         ++n;
       }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return finish(launch_affinity_up(p, dm->dtype, geo.lds_bytes, geo.grid, st), st, fn);
+  return finish(launch_affinity_up(p, dm->dtype, geo.dyn_lds_bytes, geo.grid, st), st, fn);
 }
 
 int hna_finalize_up(const hna_dims* dm, const float* wd_sq, float scale, int flags,

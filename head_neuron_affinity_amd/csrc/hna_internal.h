@@ -63,11 +63,13 @@ struct UpParams {
 struct UpGeometry {
   int I32, n_tt, n_kt, n_chunks, n_ktg, n_cg, n_st, grid;
   size_t part_floats;
-  size_t lds_bytes;
+  size_t lds_bytes;       // total LDS per workgroup (static + dynamic)
+  size_t dyn_lds_bytes;   // dynamic part (per-group accumulators)
+  bool gu_lds;            // g/u tiles staged through LDS (bf16 with I % 8 == 0)
 };
 UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype);
 
-hipError_t launch_affinity_up(const UpParams& p, int dtype, size_t lds_bytes, int grid,
+hipError_t launch_affinity_up(const UpParams& p, int dtype, size_t dyn_lds_bytes, int grid,
                               hipStream_t st);
 hipError_t launch_finalize_up(const float* part, int n_chunks, int G, int I, int I32,
                               const float* wd_sq, float scale, int accumulate, float* S_fo,

@@ -65,23 +65,45 @@ constexpr int pow2_slots(int cpr) { return cpr <= 8 ? 8 : (cpr <= 16 ? 16 : 32);
 // LDS per-token vectors of one tile: 1/r, 1/r^2, 1/r_next.
 constexpr int kTokVec = 3 * kTileTokens;
 
-template <typename E, int S>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (LGKM and export counters untouched).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Async 16-byte global -> LDS copy: lane l writes 16 bytes at dst + 16 l.
+__device__ inline void dma16(const void* src, unsigned char* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst_wave_base, 16, 0, 0);
+}
+
+constexpr int kWaves = 8;             // 2 per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTB = 2;                // 32-token blocks per wave (64 tokens)
+
+template <typename E, int S, bool GULDS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void affinity_up_kernel(const UpParams p) {
   using T = E;
   using Tr = Traits<E>;
   constexpr int Q = Tr::kQuads;
   constexpr int CPS = Tr::kChunksPerStep;
+  constexpr int EPC = 16 / Tr::kBytes;      // elements per 16-byte chunk
   constexpr int CPR = S * CPS;              // 16-byte chunks per row of a_h
   constexpr int SLOTS = pow2_slots(CPR);
   constexpr int ROWB = SLOTS * 16;
   constexpr int BUFB = kTileTokens * ROWB;
-  constexpr int CPT = CPR / 2;              // chunks staged per thread per tile
+  constexpr int DMA_A = kTileTokens * SLOTS / kThreads;   // a-tile copies per thread per step
+  constexpr int DMA_GU = GULDS ? 2 * kTileTokens * 16 / kThreads : 0;
+  constexpr int GU_BYTES = GULDS ? 2 * kTileTokens * 256 : 16;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char* abuf = lds;                                    // [2][128][ROWB]
-  float* tokvec = reinterpret_cast<float*>(lds + 2 * BUFB);     // [2][3][128]
-  float* accl = tokvec + 2 * kTokVec;                           // [2G][256]
+  // Distinct static LDS objects: the compiler can tell a pending copy into one
+  // a-tile buffer (or the g/u tile) from reads of the other buffer.
+  __shared__ __attribute__((aligned(16))) unsigned char abuf0[BUFB];
+  __shared__ __attribute__((aligned(16))) unsigned char abuf1[BUFB];
+  __shared__ __attribute__((aligned(16))) unsigned char gubuf[GU_BYTES];
+  __shared__ __attribute__((aligned(16))) float tokvec[2 * kTokVec];
+  __shared__ __attribute__((aligned(16))) float cbuf[2 * kTileNeurons];
+  extern __shared__ __attribute__((aligned(16))) float accl[];   // [2G][2][128]
 
   // workgroup -> (neuron tile, token chunk); consecutive ids alternate XCDs
   const int id = blockIdx.x;
@@ -93,154 +115,197 @@ void affinity_up_kernel(const UpParams p) {
   if (kt >= p.n_kt || chunk >= p.n_chunks) return;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wn = w & 3, wt = w >> 2;         // neuron block, token half
   const int H = p.H, G = p.G, I = p.I, d = p.d;
   const int64_t NT = p.T;
   const int KB = p.I32 >> 5;
-  const int nb = kt * 4 + w;                 // this wave's block of 32 neurons
+  const int nb = kt * 4 + wn;                // this wave's block of 32 neurons
   const int nbc = nb < KB ? nb : KB - 1;     // clamped so that M reads stay in bounds
   const int k = nb * 32 + (l & 31);
-  const bool kvalid = nb < KB && k < I;
+  const int kc = k < I ? k : I - 1;          // clamped neuron for direct g/u reads
   const T* a = static_cast<const T*>(p.a);
   const T* gp = static_cast<const T*>(p.g);
   const T* up = static_cast<const T*>(p.u);
   const T* M = static_cast<const T*>(p.M);
   const bool want_c = p.r_next != nullptr;
 
-  for (int x = tid; x < 2 * G * 256; x += 256) accl[x] = 0.f;
+  for (int x = tid; x < 2 * G * 2 * kTileNeurons; x += kThreads) accl[x] = 0.f;
 
   const int tt0 = chunk * kTilesPerChunk;
   const int ntile = min(kTilesPerChunk, p.n_tt - tt0);
   const int nsteps = ntile * H;
 
-  uint4 stage[CPT];
-  auto load_stage = [&](int step) {
+  // ---- asynchronous copies into LDS --------------------------------------
+  // a tile of a (token tile, head) step: slot q of the buffer holds row
+  // q / SLOTS, chunk (q % SLOTS) ^ (row % SLOTS); rows past T and unused slots
+  // copy a valid dummy chunk (its contribution is masked by 1/r = 0).
+  auto dma_a = [&](int step, unsigned char* buf) {
     const int ti = step / H;
     const int h = p.head_order[step - ti * H];
     const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
+    const int last = (int)min((int64_t)kTileTokens, NT - t0) - 1;   // last valid row
+    const char* base = reinterpret_cast<const char*>(a + (t0 * H + h) * d);   // wave-uniform
+    const uint32_t row_bytes = (uint32_t)(H * d * Tr::kBytes);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = tid + 256 * c;
-      const int row = q / CPR, col = q - (q / CPR) * CPR;
-      const int64_t t = t0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < NT) v = *reinterpret_cast<const uint4*>(a + ((t * H + h) * d) + col * (16 / Tr::kBytes));
-      stage[c] = v;
+    for (int i = 0; i < DMA_A; ++i) {
+      const int slot0 = (i * kWaves + w) * 64;
+      const int slot_id = slot0 + l;
+      const int row = slot_id / SLOTS, sl = slot_id % SLOTS;
+      int c = sl ^ (row & (SLOTS - 1));
+      c = c < CPR ? c : 0;
+      const int rr = row < last ? row : last;
+      dma16(base + (uint32_t)rr * row_bytes + (uint32_t)(c * 16), buf + slot0 * 16);
     }
   };
-  auto store_stage = [&](int buf) {
+  // g and u tiles (bf16, 128 tokens x 128 neurons each; row = 16 chunks of 8
+  // neurons, chunk c of row r in slot c ^ (r & 4): conflict-free reads).
+  auto dma_gu = [&](int ti) {
+    if constexpr (GULDS) {
+      const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
+      const int last = (int)min((int64_t)kTileTokens, NT - t0) - 1;
+      const int n0 = kt * kTileNeurons;
+      const char* gbase = reinterpret_cast<const char*>(gp + t0 * I);     // wave-uniform
+      const char* ubase = reinterpret_cast<const char*>(up + t0 * I);
+      const uint32_t row_bytes = (uint32_t)I * 2u;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = tid + 256 * c;
-      const int row = q / CPR, col = q - (q / CPR) * CPR;
-      const int off = row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4);
-      *reinterpret_cast<uint4*>(abuf + buf * BUFB + off) = stage[c];
+      for (int i = 0; i < DMA_GU; ++i) {
+        const int slot0 = (i * kWaves + w) * 64;   // slot index over [g tile | u tile]
+        const int which = slot0 >= kTileTokens * 16;
+        const int slot_id = slot0 + l - which * kTileTokens * 16;
+        const int row = slot_id >> 4, sl = slot_id & 15;
+        const int c = sl ^ (row & 4);
+        const int rr = row < last ? row : last;
+        int n = n0 + c * 8;
+        n = n + 8 <= I ? n : I - 8;
+        dma16((which ? ubase : gbase) + (uint32_t)rr * row_bytes + (uint32_t)n * 2u,
+              gubuf + slot0 * 16);
+      }
     }
   };
-  auto stage_tokvec = [&](int ti, int buf) {
+  auto stage_tokvec = [&](int ti, int tb) {
     if (tid < kTileTokens) {
       const int64_t t = (int64_t)(tt0 + ti) * kTileTokens + tid;
       float ri = 0.f, rn = 0.f;
       if (t < NT) {
-        ri = 1.0f / p.r[t];
-        if (want_c) rn = 1.0f / p.r_next[t];
+        ri = __builtin_amdgcn_rcpf(p.r[t]);
+        if (want_c) rn = __builtin_amdgcn_rcpf(p.r_next[t]);
       }
-      float* tv = tokvec + buf * kTokVec;
+      float* tv = tokvec + tb * kTokVec;
       tv[tid] = ri;
       tv[kTileTokens + tid] = ri * ri;
       tv[2 * kTileTokens + tid] = rn;
     }
   };
 
-  // prologue: first (tile, head) in LDS buffer 0
-  load_stage(0);
-  stage_tokvec(0, 0);
-  store_stage(0);
-  __syncthreads();
-
-  f32x16 accG[4], accU[4];
-  float coefA[4][16], coefB[4][16];
-  float fo_run[4] = {0.f, 0.f, 0.f, 0.f}, add_run[4] = {0.f, 0.f, 0.f, 0.f};
+  // ---- registers ------------------------------------------------------------
+  f32x16 accG[kTB], accU[kTB];
+  float coefA[kTB][16], coefB[kTB][16];
+  float fo_run[kTB], add_run[kTB];
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = add_run[tb] = 0.f;
   float c_acc = 0.f;
-  const int64_t slab = (int64_t)64 * 8;            // elements per (h, kb, gu, s)
-  const T* Mw = M + (int64_t)nbc * 2 * S * slab + l * 8;
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const int ti = step / H, hi = step - ti * H;
-    const int h = p.head_order[hi];
-    const int grp = p.head_group[hi];
-    const bool has_next = step + 1 < nsteps;
-    if (has_next) load_stage(step + 1);
-
-    if (hi == 0) {
-      // operating-point coefficients of this tile, shared by all heads
-      const float* tv = tokvec + (ti & 1) * kTokVec;
-      const int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
+  constexpr int kSlabBytes = 64 * 8 * Tr::kBytes;      // one (h, kb, gu, s) fragment slab
+  const char* Mbytes = reinterpret_cast<const char*>(M);
+  const uint32_t mlane = (uint32_t)l * 8u * Tr::kBytes;
+  // M fragments stream through a ring of D register slots: K-step s of a
+  // step uses slot s % D, and right after its MFMAs the slot is refilled with
+  // the K-step D positions later (in this step or the next one).
+  constexpr int D = (S % 2 == 0) ? S / 2 : S;
+  constexpr int NM = 2 * D * Q;   // M loads that may be outstanding at a step boundary
+  uint4 mreg[D][2][Q];
+  auto load_m = [&](int slot, int s, int h) {
+    // wave-uniform base of (h, this wave's neuron block), per-lane 32-bit offset
+    const char* Mh = Mbytes + ((int64_t)h * KB + nbc) * 2 * S * kSlabBytes;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = tb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-          const int64_t t = tbase + row;
-          float A = 0.f, B = 0.f;
-          if (kvalid && t < NT) {
-            const float gv = load_elem(gp, t * I + k);
-            const float uv = load_elem(up, t * I + k);
-            const float ri = tv[row];
-            const float sg = 1.0f / (1.0f + __expf(-gv));   // logistic sigma(g)
-            const float silu = gv * sg;
-            const float dsilu = fmaf(silu, 1.0f - sg, sg);   // sigma (1 + g (1 - sigma))
-            A = dsilu * uv * ri;
-            B = silu * ri;
-            if (want_c) {
-              const float al = silu * uv * tv[2 * kTileTokens + row];
-              c_acc = fmaf(al, al, c_acc);
-            }
-          }
-          coefA[tb][v] = A;
-          coefB[tb][v] = B;
-        }
-      }
+    for (int qq = 0; qq < Q; ++qq) {
+      mreg[slot][0][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + s * kSlabBytes + qq * 16);
+      mreg[slot][1][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + (S + s) * kSlabBytes + qq * 16);
     }
-    if (hi == H - 1 && ti + 1 < ntile) stage_tokvec(ti + 1, (ti + 1) & 1);
+  };
+  const int row0 = wt * 64;                            // first token row of this wave
 
-    // a_h (128 x d) . M_h (d x [32 gate | 32 up]) on the matrix cores
+  // operating-point coefficients of tile ti (shared by all heads)
+  auto coefficients = [&](int ti) {
+    const float* tv = tokvec + (ti & 1) * kTokVec;
+    const int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
+    const int nl = wn * 32 + (l & 31);                  // neuron within the tile
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < kTB; ++tb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = row0 + tb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+        float gv, uv;
+        if constexpr (GULDS) {
+          const int off = row * 256 + (((nl >> 3) ^ (row & 4)) << 4) + (nl & 7) * 2;
+          gv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(gubuf + off));
+          uv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(gubuf + kTileTokens * 256 + off));
+        } else {
+          const int last = (int)min((int64_t)kTileTokens, NT - tbase) - 1;
+          const int rr = row < last ? row : last;
+          const uint32_t off = (uint32_t)rr * (uint32_t)I + (uint32_t)kc;
+          gv = load_elem(gp + tbase * I, off);
+          uv = load_elem(up + tbase * I, off);
+        }
+        const float ri = tv[row];
+        const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * gv);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + e);     // logistic sigma(g)
+        const float silu = gv * sg;
+        const float dsilu = fmaf(silu, 1.0f - sg, sg);         // sigma (1 + g (1 - sigma))
+        coefA[tb][v] = dsilu * uv * ri;
+        coefB[tb][v] = silu * ri;
+        const float al = silu * uv * tv[2 * kTileTokens + row];
+        c_acc = fmaf(al, al, c_acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // one (token tile, head) step reading a-tile buffer `ab`
+  auto step_body = [&](int step, const unsigned char* ab, unsigned char* ab_next) {
+    const int ti = step / H, hi = step - ti * H;
+    const int grp = p.head_group[hi];
+    const int h = p.head_order[hi];
+    const bool has_next = step + 1 < nsteps;
+    // head of the next step (the last step refills with its own head: the
+    // loads stay in bounds and are simply not used)
+    const int hn = has_next ? p.head_order[(hi + 1) % H] : h;
+    if (has_next) dma_a(step + 1, ab_next);
+    const bool gu_now = GULDS && hi == 0 && ti + 1 < ntile;
+    if (gu_now) dma_gu(ti + 1);
+    if (hi == 0 && ti + 1 < ntile) stage_tokvec(ti + 1, (ti + 1) & 1);
+
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
       accG[tb] = f32x16{};
       accU[tb] = f32x16{};
     }
-    const unsigned char* ab = abuf + buf * BUFB;
-    const T* Mh = Mw + (int64_t)h * KB * 2 * S * slab;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      uint4 bg[Q], bu[Q];
 #pragma unroll
-      for (int qq = 0; qq < Q; ++qq) {
-        bg[qq] = *reinterpret_cast<const uint4*>(Mh + s * slab + qq * (16 / Tr::kBytes));
-        bu[qq] = *reinterpret_cast<const uint4*>(Mh + (S + s) * slab + qq * (16 / Tr::kBytes));
-      }
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int row = tb * 32 + (l & 31);
+      for (int tb = 0; tb < kTB; ++tb) {
+        const int row = row0 + tb * 32 + (l & 31);
         uint4 af[Q];
 #pragma unroll
         for (int qq = 0; qq < Q; ++qq) {
           const int col = s * CPS + (l >> 5) * Q + qq;
           af[qq] = *reinterpret_cast<const uint4*>(ab + row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4));
         }
-        mma(accG[tb], af, bg);
-        mma(accU[tb], af, bu);
+        mma(accG[tb], af, mreg[s % D][0]);
+        mma(accU[tb], af, mreg[s % D][1]);
       }
+      if (s + D < S) load_m(s % D, s + D, h);
+      else load_m(s % D, s + D - S, hn);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // fused epilogue: eq. (5), its square, and the ADD terms
+    __builtin_amdgcn_sched_barrier(0);
     const float* r2 = tokvec + (ti & 1) * kTokVec + kTileTokens;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < kTB; ++tb) {
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
-        const float4 rr = *reinterpret_cast<const float4*>(r2 + tb * 32 + 8 * vq + 4 * (l >> 5));
+        const float4 rr = *reinterpret_cast<const float4*>(r2 + row0 + tb * 32 + 8 * vq + 4 * (l >> 5));
         const float rv[4] = {rr.x, rr.y, rr.z, rr.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -254,23 +319,57 @@ void affinity_up_kernel(const UpParams p) {
       }
     }
     if (hi == H - 1 || p.head_group[hi + 1] != grp) {
-      accl[grp * 256 + tid] += (fo_run[0] + fo_run[1]) + (fo_run[2] + fo_run[3]);
-      accl[(G + grp) * 256 + tid] += (add_run[0] + add_run[1]) + (add_run[2] + add_run[3]);
+      // lanes l and l + 32 hold the same neuron: lane l < 32 keeps the FO sum,
+      // lane l + 32 the ADD sum, each combined with its partner's
+      float fo = fo_run[0], ad = add_run[0];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) fo_run[tb] = add_run[tb] = 0.f;
+      for (int tb = 1; tb < kTB; ++tb) { fo += fo_run[tb]; ad += add_run[tb]; }
+      const float mine = l < 32 ? fo : ad;
+      const float theirs = __shfl_xor(l < 32 ? ad : fo, 32);
+      accl[(((l < 32 ? 0 : G) + grp) * 2 + wt) * kTileNeurons + wn * 32 + (l & 31)] += mine + theirs;
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = add_run[tb] = 0.f;
     }
-    if (has_next) store_stage(buf ^ 1);
-    __syncthreads();
+    // publish the next a tile (unless the next step opens a new token tile,
+    // whose coefficient phase waits and synchronises instead)
+    if (has_next && hi + 1 < H) {
+      if (gu_now) __builtin_amdgcn_s_waitcnt(vm_wait(NM + DMA_GU));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(NM));
+      __syncthreads();
+    }
+  };
+
+  // ---- prologue ------------------------------------------------------------
+  dma_a(0, abuf0);
+  dma_gu(0);
+  stage_tokvec(0, 0);
+#pragma unroll
+  for (int s = 0; s < D; ++s) load_m(s, s, p.head_order[0]);
+
+  for (int step = 0; step < nsteps; ++step) {
+    if (step % H == 0) {
+      // new token tile: its a tile, g/u tile and token vectors must be in LDS
+      __builtin_amdgcn_s_waitcnt(vm_wait(NM));
+      __syncthreads();
+      coefficients(step / H);
+      __syncthreads();   // g/u tile fully read before it is refilled
+    }
+    if ((step & 1) == 0) step_body(step, abuf0, abuf1);
+    else step_body(step, abuf1, abuf0);
   }
 
-  // lanes l and l+32 hold the same neuron: combine and write the partial sums
+  // write this workgroup's partial sums (token halves added in fixed order)
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));   // drain the last (unused) M refills
   c_acc += __shfl_xor(c_acc, 32);
-  if (l < 32 && nb < KB) {
-    const int kk = nb * 32 + l;
+  if (l < 32) cbuf[wt * kTileNeurons + wn * 32 + l] = c_acc;
+  __syncthreads();
+  if (wt == 0 && l < 32 && nb < KB) {
+    const int kk = nb * 32 + l, nl = wn * 32 + l;
     float* out = p.part + (int64_t)chunk * (2 * G + 1) * p.I32;
     for (int gg = 0; gg < 2 * G; ++gg)
-      out[(int64_t)gg * p.I32 + kk] = accl[gg * 256 + tid] + accl[gg * 256 + tid + 32];
-    out[(int64_t)2 * G * p.I32 + kk] = c_acc;
+      out[(int64_t)gg * p.I32 + kk] =
+          accl[(gg * 2 + 0) * kTileNeurons + nl] + accl[(gg * 2 + 1) * kTileNeurons + nl];
+    out[(int64_t)2 * G * p.I32 + kk] = cbuf[nl] + cbuf[kTileNeurons + nl];
   }
 }
 
@@ -300,27 +399,27 @@ __global__ __launch_bounds__(256) void finalize_up_kernel(const float* __restric
   *dst = accumulate ? *dst + (float)v : (float)v;
 }
 
-template <typename T, int S>
+template <typename T, int S, bool GULDS>
 hipError_t launch_typed(const UpParams& p, size_t lds, int grid, hipStream_t st) {
-  auto fn = affinity_up_kernel<T, S>;
+  auto fn = affinity_up_kernel<T, S, GULDS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, st, p);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, st, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool GULDS>
 hipError_t launch_by_steps(const UpParams& p, size_t lds, int grid, hipStream_t st) {
   switch (p.d / 16) {
-    case 1: return launch_typed<T, 1>(p, lds, grid, st);
-    case 2: return launch_typed<T, 2>(p, lds, grid, st);
-    case 3: return launch_typed<T, 3>(p, lds, grid, st);
-    case 4: return launch_typed<T, 4>(p, lds, grid, st);
-    case 5: return launch_typed<T, 5>(p, lds, grid, st);
-    case 6: return launch_typed<T, 6>(p, lds, grid, st);
-    case 7: return launch_typed<T, 7>(p, lds, grid, st);
-    case 8: return launch_typed<T, 8>(p, lds, grid, st);
+    case 1: return launch_typed<T, 1, GULDS>(p, lds, grid, st);
+    case 2: return launch_typed<T, 2, GULDS>(p, lds, grid, st);
+    case 3: return launch_typed<T, 3, GULDS>(p, lds, grid, st);
+    case 4: return launch_typed<T, 4, GULDS>(p, lds, grid, st);
+    case 5: return launch_typed<T, 5, GULDS>(p, lds, grid, st);
+    case 6: return launch_typed<T, 6, GULDS>(p, lds, grid, st);
+    case 7: return launch_typed<T, 7, GULDS>(p, lds, grid, st);
+    case 8: return launch_typed<T, 8, GULDS>(p, lds, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -340,16 +439,21 @@ UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype) {
   g.part_floats = (size_t)g.n_chunks * (2 * G + 1) * g.I32;
   const int cpr = (d / 16) * (dtype == 1 ? 2 : 4);
   const int slots = pow2_slots(cpr);
-  g.lds_bytes = (size_t)2 * kTileTokens * slots * 16 + (size_t)2 * kTokVec * 4 +
-                (size_t)2 * G * 256 * 4;
+  const bool gulds = dtype == 1 && I % 8 == 0;
+  g.gu_lds = gulds;
+  g.dyn_lds_bytes = (size_t)2 * G * 2 * kTileNeurons * 4;
+  g.lds_bytes = (size_t)2 * kTileTokens * slots * 16 + (gulds ? 2 * kTileTokens * 256 : 16) +
+                (size_t)2 * kTokVec * 4 + (size_t)2 * kTileNeurons * 4 + g.dyn_lds_bytes;
   return g;
 }
 
-hipError_t launch_affinity_up(const UpParams& p, int dtype, size_t lds_bytes, int grid,
+hipError_t launch_affinity_up(const UpParams& p, int dtype, size_t dyn_lds_bytes, int grid,
                               hipStream_t st) {
   if (grid == 0) return hipSuccess;
-  return dtype == 1 ? launch_by_steps<__bf16>(p, lds_bytes, grid, st)
-                    : launch_by_steps<float>(p, lds_bytes, grid, st);
+  if (dtype == 1)
+    return p.I % 8 == 0 ? launch_by_steps<__bf16, true>(p, dyn_lds_bytes, grid, st)
+                        : launch_by_steps<__bf16, false>(p, dyn_lds_bytes, grid, st);
+  return launch_by_steps<float, false>(p, dyn_lds_bytes, grid, st);
 }
 
 hipError_t launch_finalize_up(const float* part, int n_chunks, int G, int I, int I32,
