@@ -52,8 +52,11 @@ def traffic_for(workload: str):
 
 
 def cpu_baseline(layer_gpu, budget_s: float = 12.0):
-    """Time the float64 oracle on the first tokens of the same layer."""
-    import numpy as np
+    """Time the float64 oracle on the first tokens of the same layer.
+
+    A 1024-token calibration run gives the cost per token; the timed sample is
+    then sized to take roughly `budget_s` seconds (more where the per-token cost
+    grows with the sample)."""
     import torch
     import oracle
     try:
@@ -73,20 +76,33 @@ def cpu_baseline(layer_gpu, budget_s: float = 12.0):
                 out[k] = v
         return out
 
-    T0 = 64
-    s = sample(T0)
-    t = time.perf_counter()
-    oracle.affinity_layer(s)
-    dt0 = time.perf_counter() - t
-    # down-edge weight norms are a per-layer fixed cost; the rest scales with T
-    T1 = int(min(max(T0 * budget_s / max(dt0, 1e-3), 128), 8192, layer_gpu["a"].shape[0]))
-    s = sample(T1)
-    t = time.perf_counter()
-    oracle.affinity_layer(s)
-    dt = time.perf_counter() - t
+    def run(T):
+        s = sample(T)
+        t = time.perf_counter()
+        oracle.affinity_layer(s)
+        return time.perf_counter() - t
+
+    Tmax = layer_gpu["a"].shape[0]
+    tc = min(1024, Tmax)
+    per_tok = max(run(tc) / tc, 1e-6)      # includes the fixed cost: sizes T1 conservatively
+    T1 = int(budget_s / per_tok) // 128 * 128
+    T1 = max(min(T1, Tmax), min(128, Tmax))
+    dt = run(T1)
     return {"value": T1 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {T1} tokens of the same synthetic layer, whole pass "
+            "sample": f"first {T1} of the {Tmax} tokens of the same synthetic layer, whole pass "
                       f"(S_fo, S_add, S_down) in float64 numpy, {dt:.1f} s"}
+
+
+def copy_probe(mib: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def build_inputs(config: int, T=None):
@@ -102,6 +118,8 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="workload: 1, 2, 3 (28-layer stack) or 4")
     ap.add_argument("--tokens", type=int, default=None, help="override T (not for reported numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain copy of this many MiB (counter scaling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -114,6 +132,8 @@ def main():
     import head_neuron_affinity_amd as hna
 
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     shape = synth.layer_shape(args.config)
     if args.tokens:
         shape = shape.with_tokens(args.tokens)
