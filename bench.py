@@ -51,12 +51,9 @@ def traffic_for(workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(layer_gpu, budget_s: float = 12.0):
-    """Time the float64 oracle on the first tokens of the same layer.
-
-    A 1024-token calibration run gives the cost per token; the timed sample is
-    then sized to take roughly `budget_s` seconds (more where the per-token cost
-    grows with the sample)."""
+def cpu_baseline(layer_gpu):
+    """Time the float64 oracle on the first 4096 tokens of the same layer (one
+    token chunk of the oracle; its cost is linear in the token count)."""
     import torch
     import oracle
     try:
@@ -83,10 +80,7 @@ def cpu_baseline(layer_gpu, budget_s: float = 12.0):
         return time.perf_counter() - t
 
     Tmax = layer_gpu["a"].shape[0]
-    tc = min(1024, Tmax)
-    per_tok = max(run(tc) / tc, 1e-6)      # includes the fixed cost: sizes T1 conservatively
-    T1 = int(budget_s / per_tok) // 128 * 128
-    T1 = max(min(T1, Tmax), min(128, Tmax))
+    T1 = min(4096, Tmax)                    # one token chunk of the oracle
     dt = run(T1)
     return {"value": T1 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {T1} of the {Tmax} tokens of the same synthetic layer, whole pass "
@@ -156,6 +150,7 @@ def main():
             P.hot(L, grps[i])
             if ev is not None and i == 0:
                 ev[1].record(stream)
+            P.add(L, grps[i])
             P.finalize(1.0 / T)
             if n_layers == 1 or i + 1 < n_layers:
                 P.down(L, grps_n[i])

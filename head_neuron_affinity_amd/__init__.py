@@ -7,14 +7,14 @@ ctypes binding: PyTorch provides device memory and streams only.
 """
 from ._binding import (HnaError, HNA_BF16, HNA_F32, HNA_ACCUMULATE, hna_dims, hna_down_dims,
                        make_dims, lib, LIB_PATH, EXPORTED, fold_up_weights, down_col_sqnorm,
-                       affinity_up, finalize_up, down_weight_norms, down_combine,
+                       affinity_up, affinity_add, finalize_up, down_weight_norms, down_combine,
                        up_workspace_bytes, down_workspace_bytes, folded_bytes, status_string,
                        last_error)
 from .pipeline import AffinityPass, pass_for_layer, affinity_layer
 
 __all__ = [
     "HnaError", "HNA_BF16", "HNA_F32", "HNA_ACCUMULATE", "hna_dims", "hna_down_dims", "make_dims",
-    "lib", "LIB_PATH", "EXPORTED", "fold_up_weights", "down_col_sqnorm", "affinity_up",
+    "lib", "LIB_PATH", "EXPORTED", "fold_up_weights", "down_col_sqnorm", "affinity_up", "affinity_add",
     "finalize_up", "down_weight_norms", "down_combine", "up_workspace_bytes",
     "down_workspace_bytes", "folded_bytes", "status_string", "last_error", "AffinityPass",
     "pass_for_layer", "affinity_layer",

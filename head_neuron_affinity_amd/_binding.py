@@ -30,7 +30,7 @@ HNA_ACCUMULATE = 1
 EXPORTED = [
     "hna_abi_version", "hna_status_string", "hna_last_error", "hna_folded_bytes",
     "hna_fold_workspace_bytes", "hna_fold_up_weights", "hna_down_col_sqnorm",
-    "hna_up_workspace_bytes", "hna_affinity_up", "hna_finalize_up",
+    "hna_up_workspace_bytes", "hna_affinity_up", "hna_affinity_add", "hna_finalize_up",
     "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine",
 ]
 
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "hna_down_col_sqnorm": (ctypes.c_int, [dp, vp, vp, vp]),
         "hna_up_workspace_bytes": (sz, [dp]),
         "hna_affinity_up": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, ip, vp, sz, vp]),
+        "hna_affinity_add": (ctypes.c_int, [dp, vp, vp, vp, ip, vp, sz, vp]),
         "hna_finalize_up": (ctypes.c_int, [dp, vp, f32, ctypes.c_int, vp, sz, vp, vp, vp, vp]),
         "hna_down_workspace_bytes": (sz, [ddp]),
         "hna_down_weight_norms": (ctypes.c_int, [ddp, vp, vp, vp, vp, vp, ip, vp, vp, sz, vp]),
@@ -188,6 +189,16 @@ def affinity_up(dims: hna_dims, a, g, u, r, r_next, M, group_of_head,
                              _ptr(M), _map(group_of_head), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(a.device)),
            "hna_affinity_up")
+    return workspace
+
+
+def affinity_add(dims: hna_dims, a, r, M, group_of_head, workspace: torch.Tensor) -> torch.Tensor:
+    """The ADD score through per-head Gram matrices, into the same workspace."""
+    _need_cuda(a, r, M, workspace)
+    _check(lib().hna_affinity_add(ctypes.byref(dims), _ptr(a), _ptr(r), _ptr(M),
+                                  _map(group_of_head), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(a.device)),
+           "hna_affinity_add")
     return workspace
 
 

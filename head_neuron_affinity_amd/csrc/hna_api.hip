@@ -90,7 +90,7 @@ int check_dims(const char* fn, const hna_dims* dm) {
   if (dm->I < 1) return fail(HNA_ERR_INVALID_ARG, "%s: I=%d < 1", fn, dm->I);
   if (dm->T > ((int64_t)1 << 40))
     return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld too large", fn, (long long)dm->T);
-  if (dm->I > (1 << 26)) return fail(HNA_ERR_UNSUPPORTED, "%s: I=%d too large", fn, dm->I);
+  if (dm->I > (1 << 22)) return fail(HNA_ERR_UNSUPPORTED, "%s: I=%d too large", fn, dm->I);
   return check_heads(fn, dm->hidden, dm->H, dm->G, dm->d);
 }
 
@@ -107,8 +107,7 @@ size_t fold_ws_bytes(const hna_dims* dm) {
 }
 
 size_t up_ws_bytes(const hna_dims* dm) {
-  const UpGeometry g = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
-  return align256(g.part_floats * sizeof(float));
+  return up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype).ws_bytes;
 }
 
 size_t down_ws_transposed(const hna_down_dims* dm) {
@@ -216,8 +215,8 @@ int hna_affinity_up(const hna_dims* dm, const void* a, const void* g, const void
   REQUIRE_PTR(M);
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
   if (geo.lds_bytes > (size_t)kLdsBytes)
-    return fail(HNA_ERR_UNSUPPORTED, "%s: needs %zu bytes of LDS (G=%d, d=%d) > %d", fn,
-                geo.lds_bytes, dm->G, dm->d, kLdsBytes);
+    return fail(HNA_ERR_UNSUPPORTED, "%s: needs %zu bytes of LDS (G=%d, d=%d, dtype %d) > %d",
+                fn, geo.lds_bytes, dm->G, dm->d, dm->dtype, kLdsBytes);
   if (dm->T == 0) {
     g_last_error.clear();
     return HNA_OK;
@@ -232,14 +231,17 @@ int hna_affinity_up(const hna_dims* dm, const void* a, const void* g, const void
   const size_t need = up_ws_bytes(dm);
   if (workspace_bytes < need)
     return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
   UpParams p{};
   p.a = a;
   p.g = g;
   p.u = u;
   p.r = r;
-  p.r_next = r_next;
+  p.r_next = r_next ? r_next : r;
+  p.want_c = r_next ? 1 : 0;
   p.M = M;
-  p.part = static_cast<float*>(workspace);
+  p.part = reinterpret_cast<float*>(ws);
   p.T = dm->T;
   p.H = dm->H;
   p.G = dm->G;
@@ -259,8 +261,64 @@ int hna_affinity_up(const hna_dims* dm, const void* a, const void* g, const void
         p.head_group[n] = (int8_t)gg;
         ++n;
       }
+  // FO sums and the down-edge moment
+  return finish(launch_affinity_up(p, geo, dm->dtype, st), st, fn);
+}
+
+int hna_affinity_add(const hna_dims* dm, const void* a, const float* r, const void* M,
+                     const int32_t* group_of_head, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const char* fn = "hna_affinity_add";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  rc = check_map(fn, group_of_head, dm->H, dm->G);
+  if (rc) return rc;
+  REQUIRE_PTR(M);
+  if (dm->T == 0) {
+    g_last_error.clear();
+    return HNA_OK;
+  }
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(r);
+  REQUIRE_PTR(workspace);
+  const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  if (workspace_bytes < geo.ws_bytes)
+    return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes,
+                geo.ws_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return finish(launch_affinity_up(p, dm->dtype, geo.dyn_lds_bytes, geo.grid, st), st, fn);
+  char* ws = static_cast<char*>(workspace);
+  QuadParams qp{};
+  int n = 0;
+  for (int gg = 0; gg < dm->G; ++gg) {
+    qp.group_start[gg] = (int16_t)n;
+    for (int h = 0; h < dm->H; ++h)
+      if (group_of_head[h] == gg) qp.head_order[n++] = (int8_t)h;
+  }
+  qp.group_start[dm->G] = (int16_t)n;
+  // C_h = sum_t a_th a_th^T / r_t^2 per head, in token-chunk partial sums
+  GramParams gp{};
+  gp.a = a;
+  gp.r = r;
+  gp.part = reinterpret_cast<float*>(ws + geo.off_gram_part);
+  gp.T = dm->T;
+  gp.H = dm->H;
+  gp.d = dm->d;
+  gp.n_gc = geo.n_gc;
+  gp.chunk_tokens = geo.gram_chunk;
+  hipError_t e = launch_gram(gp, dm->dtype, st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  float* C = reinterpret_cast<float*>(ws + geo.off_gram);
+  e = launch_gram_reduce(gp.part, geo.n_gc, (int64_t)dm->H * dm->d * dm->d, C, st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  // ADD[g][k] = sum_{h in g} (m^g_hk . C_h m^g_hk + m^u_hk . C_h m^u_hk)
+  qp.C = C;
+  qp.M = M;
+  qp.add = reinterpret_cast<float*>(ws + geo.off_add);
+  qp.H = dm->H;
+  qp.G = dm->G;
+  qp.d = dm->d;
+  qp.KB = geo.I32 / 32;
+  return finish(launch_quad(qp, dm->dtype, st), st, fn);
 }
 
 int hna_finalize_up(const hna_dims* dm, const float* wd_sq, float scale, int flags,
@@ -283,9 +341,11 @@ int hna_finalize_up(const hna_dims* dm, const float* wd_sq, float scale, int fla
       return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return finish(launch_finalize_up(static_cast<const float*>(workspace), geo.n_chunks, dm->G,
-                                   dm->I, geo.I32, wd_sq, scale, flags & HNA_ACCUMULATE, S_fo,
-                                   S_add, c_down, st),
+  const char* ws = static_cast<const char*>(workspace);
+  return finish(launch_finalize_up(reinterpret_cast<const float*>(ws),
+                                   reinterpret_cast<const float*>(ws + geo.off_add), geo.n_chunks,
+                                   dm->G, dm->I, geo.I32, wd_sq, scale, flags & HNA_ACCUMULATE,
+                                   S_fo, S_add, c_down, st),
                 st, fn);
 }
 

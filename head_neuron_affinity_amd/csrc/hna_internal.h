@@ -38,42 +38,90 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// MFMA helpers shared by the kernels that consume folded-layout fragments.
+// bf16: one 32x32x16 MFMA per 16-wide step of the contraction.
+__device__ inline void mma(f32x16& c, const uint4 (&a)[1], const uint4 (&b)[1]) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                              __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+}
+// f32: eight 32x32x2 MFMAs per 16-wide step; MFMA e pairs element e of the
+// lower lane half (index 16s+e of the step) with element e of the upper half
+// (16s+8+e), so both operands use the same per-lane element order as bf16.
+__device__ inline void mma(f32x16& c, const uint4 (&a)[2], const uint4 (&b)[2]) {
+  const float af[8] = {__uint_as_float(a[0].x), __uint_as_float(a[0].y), __uint_as_float(a[0].z),
+                       __uint_as_float(a[0].w), __uint_as_float(a[1].x), __uint_as_float(a[1].y),
+                       __uint_as_float(a[1].z), __uint_as_float(a[1].w)};
+  const float bf[8] = {__uint_as_float(b[0].x), __uint_as_float(b[0].y), __uint_as_float(b[0].z),
+                       __uint_as_float(b[0].w), __uint_as_float(b[1].x), __uint_as_float(b[1].y),
+                       __uint_as_float(b[1].z), __uint_as_float(b[1].w)};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], c, 0, 0, 0);
+}
+
 // ------------------------------------------------------------- affinity pass
-constexpr int kTileTokens = 128;   // tokens per tile (4 MFMA row blocks of 32)
+constexpr int kTileTokens = 128;   // tokens per tile
 constexpr int kTileNeurons = 128;  // neurons per workgroup (4 waves x 32)
 constexpr int kTilesPerChunk = 8;  // token tiles accumulated by one workgroup
 constexpr int kSuperKt = 4;        // neuron tiles per XCD super-tile
 constexpr int kSuperChunks = 8;    // token chunks per XCD super-tile
+constexpr int kGramStage = 64;     // tokens per LDS stage of the Gram kernel
 
 struct UpParams {
   const void* a;
   const void* g;
   const void* u;
   const float* r;
-  const float* r_next;
+  const float* r_next;    // r when the down moment is not wanted (want_c = 0)
   const void* M;
-  float* part;          // [n_chunks][2G+1][I32]
+  float* part;            // [n_chunks][G+1][I32]: per-group FO sums, then the down moment
   int64_t T;
   int H, G, d, I, I32;
   int n_tt, n_kt, n_chunks, n_ktg, n_st;
+  int want_c;
   int8_t head_order[kMaxHeads];  // heads sorted by KV group (stable)
   int8_t head_group[kMaxHeads];  // group of head_order[i]
 };
 
+// Gram matrices C_h = sum_t a_th a_th^T / r_t^2 ([H, d, d] fp32), in partial
+// sums over token chunks.
+struct GramParams {
+  const void* a;
+  const float* r;
+  float* part;            // [n_gc][H][d][d]
+  int64_t T;
+  int H, d, n_gc;
+  int64_t chunk_tokens;   // multiple of kGramStage
+};
+
+// add[g][k] = sum_{h in g} sum_{gate, up} m_hk^T C_h m_hk, m_hk = column k of M_h.
+struct QuadParams {
+  const float* C;         // [H][d][d]
+  const void* M;          // folded weights
+  float* add;             // [G][KB * 32]
+  int H, G, d, KB;
+  int8_t head_order[kMaxHeads];       // heads sorted by KV group
+  int16_t group_start[kMaxHeads + 1]; // group g owns head_order[group_start[g] .. group_start[g+1])
+};
+
 struct UpGeometry {
   int I32, n_tt, n_kt, n_chunks, n_ktg, n_cg, n_st, grid;
-  size_t part_floats;
-  size_t lds_bytes;       // total LDS per workgroup (static + dynamic)
-  size_t dyn_lds_bytes;   // dynamic part (per-group accumulators)
-  bool gu_lds;            // g/u tiles staged through LDS (bf16 with I % 8 == 0)
+  int n_gc;               // token chunks of the Gram kernel
+  int64_t gram_chunk;     // tokens per Gram chunk
+  bool gu_lds;            // g/u staged in LDS (bf16 with I % 8 == 0)
+  size_t part_bytes, gram_part_bytes, gram_bytes, add_bytes, ws_bytes;
+  size_t lds_bytes, dyn_lds_bytes;
+  // byte offsets of the regions inside the workspace
+  size_t off_gram_part, off_gram, off_add;
 };
 UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype);
 
-hipError_t launch_affinity_up(const UpParams& p, int dtype, size_t dyn_lds_bytes, int grid,
-                              hipStream_t st);
-hipError_t launch_finalize_up(const float* part, int n_chunks, int G, int I, int I32,
-                              const float* wd_sq, float scale, int accumulate, float* S_fo,
-                              float* S_add, float* c_down, hipStream_t st);
+hipError_t launch_affinity_up(const UpParams& p, const UpGeometry& geo, int dtype, hipStream_t st);
+hipError_t launch_finalize_up(const float* part, const float* add, int n_chunks, int G, int I,
+                              int I32, const float* wd_sq, float scale, int accumulate,
+                              float* S_fo, float* S_add, float* c_down, hipStream_t st);
+hipError_t launch_gram(const GramParams& p, int dtype, hipStream_t st);
+hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, float* C, hipStream_t st);
+hipError_t launch_quad(const QuadParams& p, int dtype, hipStream_t st);
 
 // --------------------------------------------------------------- small kernels
 hipError_t launch_transpose(const void* in, void* out, int rows, int cols, int esize,

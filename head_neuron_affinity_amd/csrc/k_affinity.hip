@@ -1,26 +1,31 @@
-// The hot pass: first-order damage (eq. 5) and the FO / ADD up scores of
+// The hot pass: first-order damage (eq. 5) and the FO up score of
 // "Affinity-Aware Sharding for Delayed Tensor Parallelism", section 3,
 // paragraph "Affinity scores", plus the token moment of the down edge.
+// (The ADD score is linear in per-head Gram matrices and is formed from them
+// in k_gram.hip; this kernel does not touch it.)
 //
-// Work decomposition (gfx950, wave64, 1 wave per SIMD):
-//   * a workgroup owns 128 neurons (4 waves x 32) and a chunk of up to 8
-//     consecutive token tiles of 128 tokens;
+// Work decomposition (gfx950, wave64, 8 waves = 2 per SIMD):
+//   * a workgroup owns 128 neurons and a chunk of up to 8 consecutive token
+//     tiles of 128 tokens; wave w covers 64 tokens (w >> 2) x 32 neurons
+//     (w & 3);
 //   * per token tile each lane computes, once, the operating-point
-//     coefficients A = silu'(g) u / r and B = silu(g) / r for the 64 (t, k)
+//     coefficients A = silu'(g) u / r and B = silu(g) / r for the 32 (t, k)
 //     pairs it holds in the MFMA C layout, and the down-edge moment;
-//   * then for every head h (in KV-group order) the wave runs a 128 x 32 x d
-//     contraction a_h . M_h on the matrix cores for gate and up columns
-//     (8 MFMA 32x32 tiles), giving (p_h.w^g_k, p_h.w^u_k) * r in registers;
-//   * the epilogue forms Delta = A Pg + B Pu and accumulates Delta^2 and
-//     (Pg^2 + Pu^2) / r^2 into per-lane running sums; when the KV group
-//     changes the sums are added to a per-(group, lane) LDS slot;
+//   * then for every head h (in KV-group order) the wave runs a 64 x 32 x d
+//     contraction a_h . M_h on the matrix cores for gate and up columns,
+//     giving r * (p_h.w^g_k, p_h.w^u_k) in registers;
+//   * the epilogue forms Delta = A Pg + B Pu and accumulates Delta^2 into
+//     per-lane running sums (three VALU operations per pair); when the KV
+//     group changes the sums are added to a per-(group, lane) LDS slot.  The
+//     two waves of a SIMD overlap one's epilogue with the other's MFMAs;
 //   * nothing of size T x H x I leaves registers: each workgroup writes one
-//     [2G+1, 128] block of fp32 partial sums, reduced later in fixed order.
-// The head's a tile is double-buffered in LDS (XOR-swizzled 16-byte chunks,
-// conflict-free fragment reads); the folded weights stream straight from
-// global memory in fragment order.  Workgroups are mapped to XCDs so that the
-// 32 concurrent workgroups of one XCD cover 4 neuron tiles x 8 token chunks
-// and share a and M in that XCD's L2.
+//     [G+1, 128] block of fp32 partial sums, reduced later in fixed order.
+// The head's a tile is double-buffered in LDS by asynchronous LDS DMA
+// (XOR-swizzled 16-byte chunks, conflict-free fragment reads); the g/u tile
+// of the next token tile is copied the same way; the folded weights stream
+// straight from global memory into a register ring in fragment order.
+// Workgroups are mapped to XCDs so that the 32 concurrent workgroups of one
+// XCD cover 4 neuron tiles x 8 token chunks and share a and M in that XCD's L2.
 #include "hna_internal.h"
 
 namespace hna {
@@ -38,23 +43,6 @@ template <> struct Traits<float> {
   static constexpr int kQuads = 2;          // 32 bytes per lane per fragment
 };
 
-__device__ inline void mma(f32x16& c, const uint4 (&a)[1], const uint4 (&b)[1]) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                              __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
-}
-// fp32: eight K=2 MFMAs.  MFMA e pairs element e of the lower lane half
-// (d index 16s+e) with element e of the upper half (16s+8+e).
-__device__ inline void mma(f32x16& c, const uint4 (&a)[2], const uint4 (&b)[2]) {
-  const float af[8] = {__uint_as_float(a[0].x), __uint_as_float(a[0].y), __uint_as_float(a[0].z),
-                       __uint_as_float(a[0].w), __uint_as_float(a[1].x), __uint_as_float(a[1].y),
-                       __uint_as_float(a[1].z), __uint_as_float(a[1].w)};
-  const float bf[8] = {__uint_as_float(b[0].x), __uint_as_float(b[0].y), __uint_as_float(b[0].z),
-                       __uint_as_float(b[0].w), __uint_as_float(b[1].x), __uint_as_float(b[1].y),
-                       __uint_as_float(b[1].z), __uint_as_float(b[1].w)};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], c, 0, 0, 0);
-}
-
 __device__ inline float load_elem(const __bf16* p, int64_t i) {
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
@@ -62,8 +50,8 @@ __device__ inline float load_elem(const float* p, int64_t i) { return p[i]; }
 
 constexpr int pow2_slots(int cpr) { return cpr <= 8 ? 8 : (cpr <= 16 ? 16 : 32); }
 
-// LDS per-token vectors of one tile: 1/r, 1/r^2, 1/r_next.
-constexpr int kTokVec = 3 * kTileTokens;
+// LDS per-token vectors of one tile: 1/r, 1/r_next.
+constexpr int kTokVec = 2 * kTileTokens;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (LGKM and export counters untouched).
@@ -71,9 +59,19 @@ constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Async 16-byte global -> LDS copy: lane l writes 16 bytes at dst + 16 l.
-__device__ inline void dma16(const void* src, unsigned char* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst_wave_base, 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zeros (hardware range check), so tile edges need no clamping.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000 /* 32-bit data format, no swizzle */);
+}
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;   // offset past any resource: reads zeros
+
+// Asynchronous 16-byte buffer -> LDS copy: lane l copies the 16 bytes at
+// voff + soff and writes them at dst + 16 l.  Only voff is range checked.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                             unsigned char* dst_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst_wave_base, 16, voff, soff, 0, 0);
 }
 
 constexpr int kWaves = 8;             // 2 per SIMD
@@ -103,7 +101,7 @@ void affinity_up_kernel(const UpParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char gubuf[GU_BYTES];
   __shared__ __attribute__((aligned(16))) float tokvec[2 * kTokVec];
   __shared__ __attribute__((aligned(16))) float cbuf[2 * kTileNeurons];
-  extern __shared__ __attribute__((aligned(16))) float accl[];   // [2G][2][128]
+  extern __shared__ __attribute__((aligned(16))) float accl[];   // [G][2][128] FO sums
 
   // workgroup -> (neuron tile, token chunk); consecutive ids alternate XCDs
   const int id = blockIdx.x;
@@ -127,9 +125,9 @@ void affinity_up_kernel(const UpParams p) {
   const T* gp = static_cast<const T*>(p.g);
   const T* up = static_cast<const T*>(p.u);
   const T* M = static_cast<const T*>(p.M);
-  const bool want_c = p.r_next != nullptr;
+  const bool want_c = p.want_c != 0;
 
-  for (int x = tid; x < 2 * G * 2 * kTileNeurons; x += kThreads) accl[x] = 0.f;
+  for (int x = tid; x < G * 2 * kTileNeurons; x += kThreads) accl[x] = 0.f;
 
   const int tt0 = chunk * kTilesPerChunk;
   const int ntile = min(kTilesPerChunk, p.n_tt - tt0);
@@ -137,48 +135,49 @@ void affinity_up_kernel(const UpParams p) {
 
   // ---- asynchronous copies into LDS --------------------------------------
   // a tile of a (token tile, head) step: slot q of the buffer holds row
-  // q / SLOTS, chunk (q % SLOTS) ^ (row % SLOTS); rows past T and unused slots
-  // copy a valid dummy chunk (its contribution is masked by 1/r = 0).
+  // q / SLOTS, chunk (q % SLOTS) ^ (row % SLOTS).  A wave copies 64
+  // consecutive slots (64 / SLOTS whole rows); rows past T and unused slots
+  // read zeros through the buffer range check.
   auto dma_a = [&](int step, unsigned char* buf) {
     const int ti = step / H;
     const int h = p.head_order[step - ti * H];
     const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
-    const int last = (int)min((int64_t)kTileTokens, NT - t0) - 1;   // last valid row
-    const char* base = reinterpret_cast<const char*>(a + (t0 * H + h) * d);   // wave-uniform
+    const int rows = (int)min((int64_t)kTileTokens, NT - t0);
     const uint32_t row_bytes = (uint32_t)(H * d * Tr::kBytes);
+    const auto rs = buffer_rsrc(a + (t0 * H + h) * d,
+                                (uint32_t)(rows - 1) * row_bytes + (uint32_t)(d * Tr::kBytes));
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
       const int slot0 = (i * kWaves + w) * 64;
-      const int slot_id = slot0 + l;
-      const int row = slot_id / SLOTS, sl = slot_id % SLOTS;
-      int c = sl ^ (row & (SLOTS - 1));
-      c = c < CPR ? c : 0;
-      const int rr = row < last ? row : last;
-      dma16(base + (uint32_t)rr * row_bytes + (uint32_t)(c * 16), buf + slot0 * 16);
+      const int row0 = slot0 / SLOTS;                       // wave-uniform
+      const int row = row0 + l / SLOTS, sl = l % SLOTS;
+      const int c = sl ^ (row & (SLOTS - 1));
+      // the whole offset goes in voff: the range check does not cover soff
+      const uint32_t voff = c < CPR ? (uint32_t)row * row_bytes + (uint32_t)(c * 16) : kOutOfRange;
+      dma16(rs, voff, 0u, buf + slot0 * 16);
     }
   };
   // g and u tiles (bf16, 128 tokens x 128 neurons each; row = 16 chunks of 8
-  // neurons, chunk c of row r in slot c ^ (r & 4): conflict-free reads).
+  // neurons, chunk c of row r in slot c ^ (r & 4): conflict-free reads).  A
+  // wave copies 4 whole rows per instruction; rows past T read zeros.
   auto dma_gu = [&](int ti) {
     if constexpr (GULDS) {
       const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
-      const int last = (int)min((int64_t)kTileTokens, NT - t0) - 1;
+      const int rows = (int)min((int64_t)kTileTokens, NT - t0);
       const int n0 = kt * kTileNeurons;
-      const char* gbase = reinterpret_cast<const char*>(gp + t0 * I);     // wave-uniform
-      const char* ubase = reinterpret_cast<const char*>(up + t0 * I);
       const uint32_t row_bytes = (uint32_t)I * 2u;
+      const uint32_t bytes = (uint32_t)rows * row_bytes - (uint32_t)n0 * 2u;
+      const auto rg = buffer_rsrc(gp + t0 * I + n0, bytes);
+      const auto ru = buffer_rsrc(up + t0 * I + n0, bytes);
 #pragma unroll
       for (int i = 0; i < DMA_GU; ++i) {
         const int slot0 = (i * kWaves + w) * 64;   // slot index over [g tile | u tile]
         const int which = slot0 >= kTileTokens * 16;
-        const int slot_id = slot0 + l - which * kTileTokens * 16;
-        const int row = slot_id >> 4, sl = slot_id & 15;
-        const int c = sl ^ (row & 4);
-        const int rr = row < last ? row : last;
-        int n = n0 + c * 8;
-        n = n + 8 <= I ? n : I - 8;
-        dma16((which ? ubase : gbase) + (uint32_t)rr * row_bytes + (uint32_t)n * 2u,
-              gubuf + slot0 * 16);
+        const int row0 = (slot0 - which * kTileTokens * 16) >> 4;
+        const int row = row0 + (l >> 4);
+        const int c = (l & 15) ^ (row & 4);
+        const uint32_t voff = (uint32_t)row * row_bytes + (uint32_t)(c * 16);
+        dma16(which ? ru : rg, voff, 0u, gubuf + slot0 * 16);
       }
     }
   };
@@ -192,17 +191,16 @@ void affinity_up_kernel(const UpParams p) {
       }
       float* tv = tokvec + tb * kTokVec;
       tv[tid] = ri;
-      tv[kTileTokens + tid] = ri * ri;
-      tv[2 * kTileTokens + tid] = rn;
+      tv[kTileTokens + tid] = rn;
     }
   };
 
   // ---- registers ------------------------------------------------------------
   f32x16 accG[kTB], accU[kTB];
   float coefA[kTB][16], coefB[kTB][16];
-  float fo_run[kTB], add_run[kTB];
+  float fo_run[kTB];
 #pragma unroll
-  for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = add_run[tb] = 0.f;
+  for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
   float c_acc = 0.f;
   constexpr int kSlabBytes = 64 * 8 * Tr::kBytes;      // one (h, kb, gu, s) fragment slab
   const char* Mbytes = reinterpret_cast<const char*>(M);
@@ -253,7 +251,7 @@ void affinity_up_kernel(const UpParams p) {
         const float dsilu = fmaf(silu, 1.0f - sg, sg);         // sigma (1 + g (1 - sigma))
         coefA[tb][v] = dsilu * uv * ri;
         coefB[tb][v] = silu * ri;
-        const float al = silu * uv * tv[2 * kTileTokens + row];
+        const float al = silu * uv * tv[kTileTokens + row];
         c_acc = fmaf(al, al, c_acc);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -298,37 +296,26 @@ void affinity_up_kernel(const UpParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // fused epilogue: eq. (5), its square, and the ADD terms
+    // fused epilogue: eq. (5) and its square
     __builtin_amdgcn_sched_barrier(0);
-    const float* r2 = tokvec + (ti & 1) * kTokVec + kTileTokens;
 #pragma unroll
     for (int tb = 0; tb < kTB; ++tb) {
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const float4 rr = *reinterpret_cast<const float4*>(r2 + row0 + tb * 32 + 8 * vq + 4 * (l >> 5));
-        const float rv[4] = {rr.x, rr.y, rr.z, rr.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = vq * 4 + i;
-          const float pg = accG[tb][v], pu = accU[tb][v];
-          const float dl = fmaf(coefA[tb][v], pg, coefB[tb][v] * pu);
-          fo_run[tb] = fmaf(dl, dl, fo_run[tb]);
-          const float q2 = fmaf(pg, pg, pu * pu);
-          add_run[tb] = fmaf(q2, rv[i], add_run[tb]);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const float pg = accG[tb][v], pu = accU[tb][v];
+        const float dl = fmaf(coefA[tb][v], pg, coefB[tb][v] * pu);
+        fo_run[tb] = fmaf(dl, dl, fo_run[tb]);
       }
     }
     if (hi == H - 1 || p.head_group[hi + 1] != grp) {
-      // lanes l and l + 32 hold the same neuron: lane l < 32 keeps the FO sum,
-      // lane l + 32 the ADD sum, each combined with its partner's
-      float fo = fo_run[0], ad = add_run[0];
+      // lanes l and l + 32 hold the same neuron (other token rows)
+      float fo = fo_run[0];
 #pragma unroll
-      for (int tb = 1; tb < kTB; ++tb) { fo += fo_run[tb]; ad += add_run[tb]; }
-      const float mine = l < 32 ? fo : ad;
-      const float theirs = __shfl_xor(l < 32 ? ad : fo, 32);
-      accl[(((l < 32 ? 0 : G) + grp) * 2 + wt) * kTileNeurons + wn * 32 + (l & 31)] += mine + theirs;
+      for (int tb = 1; tb < kTB; ++tb) fo += fo_run[tb];
+      fo += __shfl_xor(fo, 32);
+      if (l < 32) accl[(grp * 2 + wt) * kTileNeurons + wn * 32 + l] += fo;
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = add_run[tb] = 0.f;
+      for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
     }
     // publish the next a tile (unless the next step opens a new token tile,
     // whose coefficient phase waits and synchronises instead)
@@ -365,16 +352,17 @@ void affinity_up_kernel(const UpParams p) {
   __syncthreads();
   if (wt == 0 && l < 32 && nb < KB) {
     const int kk = nb * 32 + l, nl = wn * 32 + l;
-    float* out = p.part + (int64_t)chunk * (2 * G + 1) * p.I32;
-    for (int gg = 0; gg < 2 * G; ++gg)
+    float* out = p.part + (int64_t)chunk * (G + 1) * p.I32;
+    for (int gg = 0; gg < G; ++gg)
       out[(int64_t)gg * p.I32 + kk] =
           accl[(gg * 2 + 0) * kTileNeurons + nl] + accl[(gg * 2 + 1) * kTileNeurons + nl];
-    out[(int64_t)2 * G * p.I32 + kk] = cbuf[nl] + cbuf[kTileNeurons + nl];
+    out[(int64_t)G * p.I32 + kk] = cbuf[nl] + cbuf[kTileNeurons + nl];
   }
 }
 
 // Fixed-order reduction of the partial sums (float64 accumulation).
 __global__ __launch_bounds__(256) void finalize_up_kernel(const float* __restrict__ part,
+                                                          const float* __restrict__ add,
                                                           int n_chunks, int G, int I, int I32,
                                                           const float* __restrict__ wd_sq,
                                                           float scale, int accumulate,
@@ -384,17 +372,22 @@ __global__ __launch_bounds__(256) void finalize_up_kernel(const float* __restric
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)rows * I) return;
   const int row = (int)(idx / I), k = (int)(idx - (int64_t)row * I);
-  double s = 0.0;
-  for (int c = 0; c < n_chunks; ++c) s += part[((int64_t)c * (2 * G + 1) + row) * I32 + k];
   float* dst;
-  double v = s * (double)scale;
-  if (row < G) {
-    v *= (double)wd_sq[k];
-    dst = S_fo + (int64_t)row * I + k;
-  } else if (row < 2 * G) {
-    dst = S_add + (int64_t)(row - G) * I + k;
+  double v;
+  if (row < G || row == 2 * G) {
+    const int prow = row < G ? row : G;
+    double s = 0.0;
+    for (int c = 0; c < n_chunks; ++c) s += part[((int64_t)c * (G + 1) + prow) * I32 + k];
+    v = s * (double)scale;
+    if (row < G) {
+      v *= (double)wd_sq[k];
+      dst = S_fo + (int64_t)row * I + k;
+    } else {
+      dst = c_down + k;
+    }
   } else {
-    dst = c_down + k;
+    v = n_chunks > 0 ? (double)add[(int64_t)(row - G) * I32 + k] * (double)scale : 0.0;
+    dst = S_add + (int64_t)(row - G) * I + k;
   }
   *dst = accumulate ? *dst + (float)v : (float)v;
 }
@@ -424,10 +417,13 @@ hipError_t launch_by_steps(const UpParams& p, size_t lds, int grid, hipStream_t 
   }
 }
 
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
 }  // namespace
 
 UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype) {
   UpGeometry g{};
+  const bool bf = dtype == 1;
   g.I32 = round_up(I, 32);
   g.n_tt = (int)((T + kTileTokens - 1) / kTileTokens);
   g.n_kt = (g.I32 + kTileNeurons - 1) / kTileNeurons;
@@ -436,33 +432,50 @@ UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype) {
   g.n_cg = (g.n_chunks + kSuperChunks - 1) / kSuperChunks;
   g.n_st = g.n_ktg * g.n_cg;
   g.grid = round_up(g.n_st, 8) * 32;
-  g.part_floats = (size_t)g.n_chunks * (2 * G + 1) * g.I32;
-  const int cpr = (d / 16) * (dtype == 1 ? 2 : 4);
-  const int slots = pow2_slots(cpr);
-  const bool gulds = dtype == 1 && I % 8 == 0;
-  g.gu_lds = gulds;
-  g.dyn_lds_bytes = (size_t)2 * G * 2 * kTileNeurons * 4;
-  g.lds_bytes = (size_t)2 * kTileTokens * slots * 16 + (gulds ? 2 * kTileTokens * 256 : 16) +
-                (size_t)2 * kTokVec * 4 + (size_t)2 * kTileNeurons * 4 + g.dyn_lds_bytes;
+  g.gu_lds = bf && I % 8 == 0;
+  // Gram kernel: enough (head, token chunk) workgroups to fill the chip
+  if (T > 0) {
+    const int64_t want = (512 + H - 1) / H;
+    int64_t ct = (T + want - 1) / want;
+    ct = (ct + kGramStage - 1) / kGramStage * kGramStage;
+    if (ct < 4 * kGramStage) ct = 4 * kGramStage;
+    g.gram_chunk = ct;
+    g.n_gc = (int)((T + ct - 1) / ct);
+  }
+  g.part_bytes = a256((size_t)g.n_chunks * (G + 1) * g.I32 * sizeof(float));
+  g.gram_part_bytes = a256((size_t)g.n_gc * H * d * d * sizeof(float));
+  g.gram_bytes = a256((size_t)H * d * d * sizeof(float));
+  g.add_bytes = a256((size_t)G * g.I32 * sizeof(float));
+  g.off_gram_part = g.part_bytes;
+  g.off_gram = g.off_gram_part + g.gram_part_bytes;
+  g.off_add = g.off_gram + g.gram_bytes;
+  g.ws_bytes = g.off_add + g.add_bytes;
+  const int esize = bf ? 2 : 4;
+  const int cpr = d * esize / 16;
+  const size_t bufb = (size_t)kTileTokens * pow2_slots(cpr) * 16;
+  const size_t gub = g.gu_lds ? 2 * kTileTokens * 256 : 16;
+  g.dyn_lds_bytes = (size_t)G * 2 * kTileNeurons * sizeof(float);
+  g.lds_bytes = 2 * bufb + gub + (2 * kTokVec + 2 * kTileNeurons) * sizeof(float) + g.dyn_lds_bytes;
   return g;
 }
 
-hipError_t launch_affinity_up(const UpParams& p, int dtype, size_t dyn_lds_bytes, int grid,
+hipError_t launch_affinity_up(const UpParams& p, const UpGeometry& geo, int dtype,
                               hipStream_t st) {
-  if (grid == 0) return hipSuccess;
-  if (dtype == 1)
-    return p.I % 8 == 0 ? launch_by_steps<__bf16, true>(p, dyn_lds_bytes, grid, st)
-                        : launch_by_steps<__bf16, false>(p, dyn_lds_bytes, grid, st);
-  return launch_by_steps<float, false>(p, dyn_lds_bytes, grid, st);
+  if (geo.grid == 0) return hipSuccess;
+  if (dtype == 1) {
+    return geo.gu_lds ? launch_by_steps<__bf16, true>(p, geo.dyn_lds_bytes, geo.grid, st)
+                      : launch_by_steps<__bf16, false>(p, geo.dyn_lds_bytes, geo.grid, st);
+  }
+  return launch_by_steps<float, false>(p, geo.dyn_lds_bytes, geo.grid, st);
 }
 
-hipError_t launch_finalize_up(const float* part, int n_chunks, int G, int I, int I32,
-                              const float* wd_sq, float scale, int accumulate, float* S_fo,
-                              float* S_add, float* c_down, hipStream_t st) {
+hipError_t launch_finalize_up(const float* part, const float* add, int n_chunks, int G, int I,
+                              int I32, const float* wd_sq, float scale, int accumulate,
+                              float* S_fo, float* S_add, float* c_down, hipStream_t st) {
   const int64_t n = (int64_t)(2 * G + (c_down ? 1 : 0)) * I;
   const int blocks = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(finalize_up_kernel, dim3(blocks), dim3(256), 0, st, part, n_chunks, G, I,
-                     I32, wd_sq, scale, accumulate, S_fo, S_add, c_down);
+  hipLaunchKernelGGL(finalize_up_kernel, dim3(blocks), dim3(256), 0, st, part, add, n_chunks, G,
+                     I, I32, wd_sq, scale, accumulate, S_fo, S_add, c_down);
   return hipGetLastError();
 }
 

@@ -1,0 +1,336 @@
+// The ADD up score of "Affinity-Aware Sharding for Delayed Tensor
+// Parallelism", section 3, paragraph "Affinity scores", through per-head Gram
+// matrices.
+//
+// With p_h = gamma * (a_h W_o^(h)T) / r and the folded weights M_h (column
+// m_hk = W_o^(h)T diag(gamma) w^g_k for the gate, likewise for the up
+// projection), p_h . w^g_k = (a_h . m_hk) / r, so
+//   sum_t (p_h . w^g_k)^2 = m_hk^T C_h m_hk,   C_h = sum_t a_th a_th^T / r_t^2.
+// The identity is exact (linearity of the sum), so ADD needs one d x d Gram
+// matrix per head instead of a per-(token, head, neuron) square:
+//   gram_kernel   C_h over a token chunk, on the matrix cores, staged through
+//                 LDS transposed (token index contiguous) so that both MFMA
+//                 operands read 16-byte fragments;
+//   gram_reduce   fixed-order sum over the token chunks;
+//   quad_kernel   Y = C_h M_h(:, block) on the matrix cores, then
+//                 add[g][k] = sum_{h in g} sum_{gate, up} m_hk . Y(:, k).
+// bf16 path: the scaled operand a / r^2 and the fp32 Gram entries are split
+// into two bf16 terms (hi + lo), so products stay exact in fp32 and the split
+// leaves a relative error near 2^-16.  f32 path: fp32 MFMA throughout.
+#include "hna_internal.h"
+
+namespace hna {
+namespace {
+
+constexpr int kGThreads = 256;
+
+template <typename E> struct GramLds;
+template <> struct GramLds<__bf16> {
+  static constexpr int kPitch = kGramStage + 8;   // elements; 144-byte rows
+  static constexpr int kBufs = 3;                 // a, (a / r^2) hi, (a / r^2) lo
+  static constexpr int kQ = 1;
+};
+template <> struct GramLds<float> {
+  static constexpr int kPitch = kGramStage + 4;   // 272-byte rows
+  static constexpr int kBufs = 2;                 // a, a / r^2
+  static constexpr int kQ = 2;
+};
+
+__device__ inline uint16_t bf16_rn(float x) { return (uint16_t)f32_to_bf16_bits(x); }
+
+// grid: n_gc * H workgroups (head fastest); C_part[gc][h] = sum over chunk gc.
+template <typename E>
+__global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
+  using L = GramLds<E>;
+  constexpr int TP = L::kPitch;
+  constexpr int Q = L::kQ;
+  __shared__ __attribute__((aligned(16))) E xs[L::kBufs][128 * TP];
+
+  const int h = blockIdx.x % p.H;
+  const int gc = blockIdx.x / p.H;
+  const int d = p.d;
+  const int d32 = (d + 31) & ~31;
+  const int nt = d32 >> 5;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int64_t t_begin = (int64_t)gc * p.chunk_tokens;
+  const int64_t t_end = min(p.T, t_begin + p.chunk_tokens);
+  const int64_t H = p.H;
+
+  // rows d .. d32-1 stay zero
+  for (int x = tid; x < (d32 - d) * TP; x += kGThreads)
+#pragma unroll
+    for (int b = 0; b < L::kBufs; ++b) xs[b][d * TP + x] = E(0.f);
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+
+  const int items = (kGramStage / 4) * (d / 8);   // (4 tokens) x (8 features)
+  for (int64_t ts = t_begin; ts < t_end; ts += kGramStage) {
+    __syncthreads();   // the previous stage has been read
+    for (int it = tid; it < items; it += kGThreads) {
+      const int tq = it % (kGramStage / 4), fo = it / (kGramStage / 4);
+      float x[4][8];
+      float wt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = ts + 4 * tq + j;
+        if (t < t_end) {
+          const float r = p.r[t];
+          wt[j] = 1.0f / (r * r);
+          const int64_t off = (t * H + h) * d + 8 * fo;
+          if constexpr (sizeof(E) == 2) {
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.a) + off);
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[j][2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
+              x[j][2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
+            }
+          } else {
+            const float* src = static_cast<const float*>(p.a) + off;
+            const float4 v0 = *reinterpret_cast<const float4*>(src);
+            const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+            x[j][0] = v0.x; x[j][1] = v0.y; x[j][2] = v0.z; x[j][3] = v0.w;
+            x[j][4] = v1.x; x[j][5] = v1.y; x[j][6] = v1.z; x[j][7] = v1.w;
+          }
+        } else {
+          wt[j] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[j][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int base = (8 * fo + e) * TP + 4 * tq;
+        if constexpr (sizeof(E) == 2) {
+          uint16_t xv[4], hv[4], lv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float y = x[j][e] * wt[j];
+            xv[j] = bf16_rn(x[j][e]);   // exact: x is a bf16 value
+            hv[j] = bf16_rn(y);
+            lv[j] = bf16_rn(y - bf16_bits_to_f32(hv[j]));
+          }
+          *reinterpret_cast<uint2*>(&xs[0][base]) =
+              make_uint2(xv[0] | ((uint32_t)xv[1] << 16), xv[2] | ((uint32_t)xv[3] << 16));
+          *reinterpret_cast<uint2*>(&xs[1][base]) =
+              make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+          *reinterpret_cast<uint2*>(&xs[2][base]) =
+              make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+        } else {
+          *reinterpret_cast<float4*>(&xs[0][base]) = make_float4(x[0][e], x[1][e], x[2][e], x[3][e]);
+          *reinterpret_cast<float4*>(&xs[1][base]) = make_float4(
+              x[0][e] * wt[0], x[1][e] * wt[1], x[2][e] * wt[2], x[3][e] * wt[3]);
+        }
+      }
+    }
+    __syncthreads();
+    // C[i][j] += sum_t x[i][t] * (x[j][t] / r_t^2): A rows i, B rows j
+#pragma unroll
+    for (int q = 0; q < kGramStage / 16; ++q) {
+      const int col = 16 * q + 8 * (l >> 5);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        const int tile = w + 4 * ti;
+        if (tile < nt * nt) {
+          const int it = tile / nt, jt = tile - it * nt;
+          const E* arow = &xs[0][(it * 32 + (l & 31)) * TP + col];
+          uint4 af[Q], bh[Q];
+#pragma unroll
+          for (int qq = 0; qq < Q; ++qq) {
+            af[qq] = *reinterpret_cast<const uint4*>(arow + qq * (16 / sizeof(E)));
+            bh[qq] = *reinterpret_cast<const uint4*>(&xs[1][(jt * 32 + (l & 31)) * TP + col] +
+                                                     qq * (16 / sizeof(E)));
+          }
+          mma(acc[ti], af, bh);
+          if constexpr (sizeof(E) == 2) {
+            uint4 bl[1];
+            bl[0] = *reinterpret_cast<const uint4*>(&xs[2][(jt * 32 + (l & 31)) * TP + col]);
+            mma(acc[ti], af, bl);
+          }
+        }
+      }
+    }
+  }
+  // write the tiles (C layout: column l & 31, row 8 (v / 4) + 4 (l / 32) + v % 4)
+  float* out = p.part + ((int64_t)gc * p.H + h) * d * d;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    const int tile = w + 4 * ti;
+    if (tile < nt * nt) {
+      const int it = tile / nt, jt = tile - it * nt;
+      const int j = jt * 32 + (l & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = it * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+        if (i < d && j < d) out[(int64_t)i * d + j] = acc[ti][v];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int n_gc,
+                                                          int64_t n, float* __restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < n_gc; ++c) s += part[(int64_t)c * n + i];
+  C[i] = s;
+}
+
+// grid (G, ceil(KB / 4)); wave w handles neuron block blockIdx.y * 4 + w.
+template <typename E, int S>
+__global__ __launch_bounds__(kGThreads) void quad_kernel(const QuadParams p) {
+  constexpr bool BF = sizeof(E) == 2;
+  constexpr int Q = BF ? 1 : 2;
+  constexpr int DD = 16 * S;                          // d
+  constexpr int D32 = (DD + 31) & ~31;
+  constexpr int NT = D32 / 32;
+  constexpr int CP = DD + (BF ? 8 : 4);               // LDS pitch of C (elements)
+  constexpr int kSlabBytes = 64 * 8 * sizeof(E);
+  __shared__ __attribute__((aligned(16))) E chi[D32 * CP];
+  __shared__ __attribute__((aligned(16))) E clo[BF ? D32 * CP : 8];
+  __shared__ __attribute__((aligned(16))) float ybuf[4][D32 * 32];
+
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int kb = blockIdx.y * 4 + w;
+  const bool active = kb < p.KB;
+  const int kbc = active ? kb : p.KB - 1;
+  const char* Mbytes = static_cast<const char*>(p.M);
+  float q = 0.f;
+
+  for (int x = tid; x < (D32 - DD) * CP; x += kGThreads) {
+    chi[DD * CP + x] = E(0.f);
+    if constexpr (BF) clo[DD * CP + x] = E(0.f);
+  }
+  for (int hh = p.group_start[g]; hh < p.group_start[g + 1]; ++hh) {
+    const int h = p.head_order[hh];
+    const float* C = p.C + (int64_t)h * DD * DD;
+    __syncthreads();
+    for (int x = tid; x < DD * DD / 4; x += kGThreads) {
+      const int i = (4 * x) / DD, j = (4 * x) % DD;
+      const float4 v = *reinterpret_cast<const float4*>(C + 4 * x);
+      const float cv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF) {
+          const uint16_t hb = bf16_rn(cv[e]);
+          reinterpret_cast<uint16_t*>(chi)[i * CP + j + e] = hb;
+          reinterpret_cast<uint16_t*>(clo)[i * CP + j + e] = bf16_rn(cv[e] - bf16_bits_to_f32(hb));
+        } else {
+          chi[i * CP + j + e] = cv[e];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int gu = 0; gu < 2; ++gu) {
+      const char* Mb = Mbytes + (((int64_t)h * p.KB + kbc) * 2 + gu) * S * kSlabBytes +
+                       (uint32_t)l * 8u * sizeof(E);
+      uint4 bfr[S][Q];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int qq = 0; qq < Q; ++qq)
+          bfr[s][qq] = *reinterpret_cast<const uint4*>(Mb + s * kSlabBytes + qq * 16);
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int off = (it * 32 + (l & 31)) * CP + 16 * s + 8 * (l >> 5);
+          uint4 ah[Q];
+#pragma unroll
+          for (int qq = 0; qq < Q; ++qq)
+            ah[qq] = *reinterpret_cast<const uint4*>(&chi[off] + qq * (16 / sizeof(E)));
+          mma(acc, ah, bfr[s]);
+          if constexpr (BF) {
+            uint4 al[1];
+            al[0] = *reinterpret_cast<const uint4*>(&clo[off]);
+            mma(acc, al, bfr[s]);
+          }
+        }
+        // Y rows it*32 + m, column l & 31
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+          ybuf[w][(it * 32 + m) * 32 + (l & 31)] = acc[v];
+        }
+      }
+      __syncthreads();
+      // q += sum_j M[j][k] Y[j][k] over this lane's fragment rows j
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        float mv[8];
+        if constexpr (BF) {
+          const uint32_t wv[4] = {bfr[s][0].x, bfr[s][0].y, bfr[s][0].z, bfr[s][0].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            mv[2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
+            mv[2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
+          }
+        } else {
+          mv[0] = __uint_as_float(bfr[s][0].x); mv[1] = __uint_as_float(bfr[s][0].y);
+          mv[2] = __uint_as_float(bfr[s][0].z); mv[3] = __uint_as_float(bfr[s][0].w);
+          mv[4] = __uint_as_float(bfr[s][Q - 1].x); mv[5] = __uint_as_float(bfr[s][Q - 1].y);
+          mv[6] = __uint_as_float(bfr[s][Q - 1].z); mv[7] = __uint_as_float(bfr[s][Q - 1].w);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 16 * s + 8 * (l >> 5) + e;
+          q = fmaf(mv[e], ybuf[w][j * 32 + (l & 31)], q);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  q += __shfl_xor(q, 32);
+  if (active && l < 32) p.add[(int64_t)g * p.KB * 32 + kb * 32 + l] = q;
+}
+
+template <typename E, int S>
+hipError_t launch_quad_t(const QuadParams& p, hipStream_t st) {
+  const dim3 grid(p.G, (p.KB + 3) / 4);
+  hipLaunchKernelGGL((quad_kernel<E, S>), grid, dim3(kGThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_quad_e(const QuadParams& p, hipStream_t st) {
+  switch (p.d / 16) {
+    case 1: return launch_quad_t<E, 1>(p, st);
+    case 2: return launch_quad_t<E, 2>(p, st);
+    case 3: return launch_quad_t<E, 3>(p, st);
+    case 4: return launch_quad_t<E, 4>(p, st);
+    case 5: return launch_quad_t<E, 5>(p, st);
+    case 6: return launch_quad_t<E, 6>(p, st);
+    case 7: return launch_quad_t<E, 7>(p, st);
+    case 8: return launch_quad_t<E, 8>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gram(const GramParams& p, int dtype, hipStream_t st) {
+  if (p.n_gc == 0) return hipSuccess;
+  const dim3 grid(p.n_gc * p.H);
+  if (dtype == 1) hipLaunchKernelGGL(gram_kernel<__bf16>, grid, dim3(kGThreads), 0, st, p);
+  else hipLaunchKernelGGL(gram_kernel<float>, grid, dim3(kGThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, float* C, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     part, n_gc, n, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_quad(const QuadParams& p, int dtype, hipStream_t st) {
+  return dtype == 1 ? launch_quad_e<__bf16>(p, st) : launch_quad_e<float>(p, st);
+}
+
+}  // namespace hna

@@ -2,10 +2,10 @@
 
 The pass follows section 3 ("Affinity scores") of "Affinity-Aware Sharding for
 Delayed Tensor Parallelism": fold the up weights, take ||w^d_k||^2, run the
-hot kernel over the calibration tokens, reduce the partial sums into S_fo and
-S_add (and the down-edge moment), then the down edge's weight norms and
-S_down.  Every step is a libhna call on torch's current stream; this module
-only owns the buffers.
+hot kernel over the calibration tokens (FO and the down-edge moment), the ADD
+score through per-head Gram matrices, reduce the partial sums into S_fo and
+S_add, then the down edge's weight norms and S_down.  Every step is a libhna
+call on torch's current stream; this module only owns the buffers.
 """
 from __future__ import annotations
 
@@ -57,6 +57,9 @@ class AffinityPass:
                       layer.get("r_next") if self.with_down else None, self.M, group_of_head,
                       workspace=self.up_ws)
 
+    def add(self, layer, group_of_head: Sequence[int]):
+        B.affinity_add(self.dims, layer["a"], layer["r"], self.M, group_of_head, self.up_ws)
+
     def finalize(self, scale: float, accumulate: bool = False):
         B.finalize_up(self.dims, self.wd_sq, self.up_ws, scale, accumulate=accumulate,
                       S_fo=self.S_fo, S_add=self.S_add,
@@ -73,6 +76,7 @@ class AffinityPass:
         grp = [int(x) for x in layer["group_of_head"].tolist()]
         self.fold(layer)
         self.hot(layer, grp)
+        self.add(layer, grp)
         self.finalize(1.0 / max(self.T, 1) if scale is None else scale)
         out = {"S_fo": self.S_fo, "S_add": self.S_add}
         if self.with_down:

@@ -120,22 +120,25 @@ int hna_fold_up_weights(const hna_dims* dims, const void* W_o, const float* gamm
 int hna_down_col_sqnorm(const hna_dims* dims, const void* W_down, float* wd_sq,
                         void* stream);
 
-/* Bytes of workspace hna_affinity_up / hna_finalize_up need for `dims`. */
+/*
+ * Bytes of workspace hna_affinity_up, hna_affinity_add and hna_finalize_up
+ * share for `dims`: the FO and down-moment partial sums of each 1024-token
+ * block of neurons, the per-head Gram partials and sums, and the ADD sums.
+ */
 size_t hna_up_workspace_bytes(const hna_dims* dims);
 
 /*
- * The hot pass (equation (5) and the two up scores).  For every token t of
- * this call, head h and neuron k it forms (p_h . w^g_k, p_h . w^u_k) from a
- * and M, the operating-point coefficients silu'(g)u/r and silu(g)/r, the
- * damage Delta_hk, and accumulates sum_t Delta^2, sum_t (p.w^g)^2 + (p.w^u)^2
- * over the query heads of each KV group, plus sum_t (silu(g)u/r_next)^2 when
- * r_next is not NULL.  Token-block partial sums go to `workspace`
- * (>= hna_up_workspace_bytes); nothing of size T x H x I is ever written.
+ * The hot pass (equation (5) and the FO score).  For every token t of this
+ * call, head h and neuron k it forms (p_h . w^g_k, p_h . w^u_k) from a and M,
+ * the operating-point coefficients silu'(g)u/r and silu(g)/r, the damage
+ * Delta_hk, and accumulates sum_t Delta^2 over the query heads of each KV
+ * group, plus sum_t (silu(g)u/r_next)^2 when r_next is not NULL.  Partial
+ * sums go to `workspace` (>= hna_up_workspace_bytes); nothing of size
+ * T x H x I is ever written.
  *   a [T,H,d], g, u [T,I] (dtype of dims); r [T], r_next [T] or NULL (fp32);
  *   M from hna_fold_up_weights with the same dims;
  *   group_of_head: host int32 [H], values in [0, G).
- * The partial sums are consumed by hna_finalize_up with the same dims and
- * workspace; T = 0 is allowed and yields zero partial sums.
+ * T = 0 is allowed and yields zero sums.
  */
 int hna_affinity_up(const hna_dims* dims, const void* a, const void* g, const void* u,
                     const float* r, const float* r_next, const void* M,
@@ -143,7 +146,22 @@ int hna_affinity_up(const hna_dims* dims, const void* a, const void* g, const vo
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Fixed-order reduction of the partial sums left by hna_affinity_up:
+ * The ADD score of the same section ("ignores the operating point"):
+ *   sum_t sum_{h in g} (p_h.w^g_k)^2 + (p_h.w^u_k)^2
+ *     = sum_{h in g} m^g_hk . C_h m^g_hk + m^u_hk . C_h m^u_hk,
+ *   C_h = sum_t a_th a_th^T / r_t^2  (d x d),
+ * where m^g_hk, m^u_hk are columns of the folded weights M_h (exact by
+ * linearity of the sum over tokens).  Reads a, r and M; writes the Gram
+ * matrices and the ADD sums into `workspace`, the same workspace as
+ * hna_affinity_up, for hna_finalize_up.  Arguments as for hna_affinity_up.
+ */
+int hna_affinity_add(const hna_dims* dims, const void* a, const float* r, const void* M,
+                     const int32_t* group_of_head,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fixed-order reduction of the sums left by hna_affinity_up and
+ * hna_affinity_add (both must have run on this workspace):
  *   S_fo[g*I+k]  (+)= scale * wd_sq[k] * sum_t sum_{h in g} Delta^2
  *   S_add[g*I+k] (+)= scale * sum_t sum_{h in g} ((p.w^g)^2 + (p.w^u)^2)
  *   c_down[k]    (+)= scale * sum_t (silu(g_k) u_k / r_next)^2   (if not NULL)

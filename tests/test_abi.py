@@ -127,14 +127,18 @@ def test_workspace_too_small():
 
 def test_workspace_sizes_follow_geometry():
     hna = _lib()
+    a256 = lambda x: (x + 255) // 256 * 256
     # Qwen3-0.6B-shaped layer: 512 token tiles of 128 -> 64 chunks of 8 tiles;
-    # partial sums [64][2G+1][I] fp32.
+    # FO partial sums [64][G+1][I] fp32, then the Gram partials over 32 token
+    # chunks [32][H][d][d], the reduced Gram matrices [H][d][d] and ADD [G][I].
     dm = hna.make_dims(65536, 1024, 16, 8, 128, 3072, 1)
-    assert hna.up_workspace_bytes(dm) == 64 * 17 * 3072 * 4
+    assert hna.up_workspace_bytes(dm) == (64 * 9 * 3072 * 4 + 32 * 16 * 128 * 128 * 4
+                                          + 16 * 128 * 128 * 4 + 8 * 3072 * 4)
     assert hna.folded_bytes(dm) == 16 * 128 * 2 * 3072 * 2
-    # ragged neuron count pads to 32; T = 1 is one chunk
-    dm = hna.make_dims(1, 64, 4, 2, 16, 100, 0)
-    assert hna.up_workspace_bytes(dm) == ((5 * 128 * 4 + 255) // 256) * 256
+    # ragged neuron count pads to 32; T = 1 is one chunk and one Gram chunk
+    dm = hna.make_dims(1, 64, 4, 2, 16, 101, 0)
+    assert hna.up_workspace_bytes(dm) == (a256(1 * 3 * 128 * 4) + a256(4 * 16 * 16 * 4)
+                                          + a256(4 * 16 * 16 * 4) + a256(2 * 128 * 4))
     assert hna.folded_bytes(dm) == 4 * 16 * 2 * 128 * 4
     dd = hna.hna_down_dims(1024, 3072, 16, 8, 128, 1)
     assert hna.down_workspace_bytes(dd) == 3072 * 1024 * 2 + 32 * 3072 * 4
@@ -146,6 +150,26 @@ def test_lds_limit_reported_unsupported():
     dm = hna.make_dims(256, 4096, 32, 32, 128, 128, 0)
     rc = call_up(hna, dm, grp=tuple(range(32)))
     assert rc == -2 and "LDS" in hna.last_error()
+
+
+def test_affinity_add_validates():
+    hna = _lib()
+    L = hna.lib()
+    vp = ctypes.c_void_p
+    dm = dims(hna)
+    grp = (ctypes.c_int32 * 4)(0, 0, 1, 1)
+    need = hna.up_workspace_bytes(dm)
+    assert L.hna_affinity_add(None, vp(FAKE), vp(FAKE), vp(FAKE), grp, vp(FAKE), need, None) == -1
+    bad = (ctypes.c_int32 * 4)(0, 0, 1, 3)
+    assert L.hna_affinity_add(ctypes.byref(dm), vp(FAKE), vp(FAKE), vp(FAKE), bad, vp(FAKE), need,
+                              None) == -1
+    assert "group_of_head[3]" in hna.last_error()
+    assert L.hna_affinity_add(ctypes.byref(dm), None, vp(FAKE), vp(FAKE), grp, vp(FAKE), need,
+                              None) == -1
+    assert L.hna_affinity_add(ctypes.byref(dm), vp(FAKE), vp(MIS), vp(FAKE), grp, vp(FAKE), need,
+                              None) == -3
+    assert L.hna_affinity_add(ctypes.byref(dm), vp(FAKE), vp(FAKE), vp(FAKE), grp, vp(FAKE),
+                              need - 1, None) == -4
 
 
 def test_finalize_and_other_calls_validate():

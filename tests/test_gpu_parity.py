@@ -219,6 +219,7 @@ def test_chunked_tokens_accumulate(hna):
                              ap.dims.dtype)
         ws = hna.affinity_up(dims, part["a"], part["g"], part["u"], part["r"], part["r_next"],
                              ap.M, grp)
+        hna.affinity_add(dims, part["a"], part["r"], ap.M, grp, ws)
         hna.finalize_up(dims, ap.wd_sq, ws, 1.0 / 1500, accumulate=(i > 0), S_fo=ap.S_fo,
                         S_add=ap.S_add, c_down=ap.c_down)
     torch.cuda.synchronize()
@@ -233,6 +234,7 @@ def test_zero_tokens(hna):
     dims = hna.make_dims(0, ap.dims.hidden, ap.dims.H, ap.dims.G, ap.dims.d, ap.dims.I, ap.dims.dtype)
     ws = hna.affinity_up(dims, L["a"], L["g"], L["u"], L["r"], L["r_next"], ap.M,
                          L["group_of_head"].tolist())
+    hna.affinity_add(dims, L["a"], L["r"], ap.M, L["group_of_head"].tolist(), ws)
     S_fo, S_add, c = hna.finalize_up(dims, ap.wd_sq, ws, 1.0)
     torch.cuda.synchronize()
     assert torch.count_nonzero(S_fo) == 0 and torch.count_nonzero(S_add) == 0
