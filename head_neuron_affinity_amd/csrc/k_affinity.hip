@@ -1,32 +1,38 @@
 // The hot pass: first-order damage (eq. 5) and the FO up score of
 // "Affinity-Aware Sharding for Delayed Tensor Parallelism", section 3,
 // paragraph "Affinity scores", plus the token moment of the down edge.
-// (The ADD score is linear in per-head Gram matrices and is formed from them
-// in k_gram.hip; this kernel does not touch it.)
+// (The ADD score is linear in the per-head Gram matrices and is formed from
+// them in k_gram.hip.)
 //
-// Work decomposition (gfx950, wave64, 8 waves = 2 per SIMD):
-//   * a workgroup owns 128 neurons and a chunk of up to 8 consecutive token
-//     tiles of 128 tokens; wave w covers 64 tokens (w >> 2) x 32 neurons
-//     (w & 3);
-//   * per token tile each lane computes, once, the operating-point
-//     coefficients A = silu'(g) u / r and B = silu(g) / r for the 32 (t, k)
-//     pairs it holds in the MFMA C layout, and the down-edge moment;
-//   * then for every head h (in KV-group order) the wave runs a 64 x 32 x d
-//     contraction a_h . M_h on the matrix cores for gate and up columns,
-//     giving r * (p_h.w^g_k, p_h.w^u_k) in registers;
-//   * the epilogue forms Delta = A Pg + B Pu and accumulates Delta^2 into
-//     per-lane running sums (three VALU operations per pair); when the KV
-//     group changes the sums are added to a per-(group, lane) LDS slot.  The
-//     two waves of a SIMD overlap one's epilogue with the other's MFMAs;
-//   * nothing of size T x H x I leaves registers: each workgroup writes one
-//     [G+1, 128] block of fp32 partial sums, reduced later in fixed order.
-// The head's a tile is double-buffered in LDS by asynchronous LDS DMA
-// (XOR-swizzled 16-byte chunks, conflict-free fragment reads); the g/u tile
-// of the next token tile is copied the same way; the folded weights stream
-// straight from global memory into a register ring in fragment order.
+// Work decomposition (gfx950, wave64, one wave per SIMD, 512 registers):
+//   * a workgroup of 4 waves owns 128 neurons and a chunk of up to 8
+//     consecutive token tiles of 128 tokens; wave w owns neurons 32w..32w+31
+//     of the tile and all 128 tokens (4 blocks of 32 in the MFMA C layout);
+//   * once per token tile each lane computes the operating-point
+//     coefficients A = silu'(g) u / r and B = silu(g) / r of its 64 (t, k)
+//     pairs (registers) and the down-edge moment (alpha / r_next)^2;
+//   * per head h (in KV-group order) the wave runs four contraction chains,
+//     one per 32-token block: 2 x d/16 MFMAs 32x32x16 into gate and up
+//     accumulators, giving r * (p_h.w^g_k, p_h.w^u_k);
+//   * the epilogue of each chain, Delta = A Pg + B Pu and fo += Delta^2, is
+//     spread over the MFMAs of the next chain (the last block's over the next
+//     head's first chain), so the VALU and the matrix cores overlap within
+//     the wave; the folded-weight fragments of a head stay in registers for
+//     all four chains and are refilled with the next head's during the last;
+//   * at the end of a KV group the per-lane sums go to an LDS slot of that
+//     group; nothing of size T x H x I leaves the chip: each workgroup writes
+//     one [G+1, 128] block of fp32 partial sums, reduced later in fixed order.
+// Data movement: the a tile of each (token tile, head) step arrives in LDS by
+// asynchronous 16-byte buffer -> LDS DMA one step ahead (double buffered,
+// XOR-swizzled rows: conflict-free fragment reads); the g/u tile of the next
+// token tile is copied the same way a whole tile ahead; buffer range checks
+// zero-fill past the tile edges.  Each wave reads the folded weights of its
+// 32 neurons once per head (no duplicate reads within the workgroup).
 // Workgroups are mapped to XCDs so that the 32 concurrent workgroups of one
 // XCD cover 4 neuron tiles x 8 token chunks and share a and M in that XCD's L2.
 #include "hna_internal.h"
+
+#include <type_traits>
 
 namespace hna {
 namespace {
@@ -43,15 +49,7 @@ template <> struct Traits<float> {
   static constexpr int kQuads = 2;          // 32 bytes per lane per fragment
 };
 
-__device__ inline float load_elem(const __bf16* p, int64_t i) {
-  return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-}
-__device__ inline float load_elem(const float* p, int64_t i) { return p[i]; }
-
 constexpr int pow2_slots(int cpr) { return cpr <= 8 ? 8 : (cpr <= 16 ? 16 : 32); }
-
-// LDS per-token vectors of one tile: 1/r, 1/r_next.
-constexpr int kTokVec = 2 * kTileTokens;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (LGKM and export counters untouched).
@@ -68,99 +66,111 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;   // offset past any resource: reads zeros
 
 // Asynchronous 16-byte buffer -> LDS copy: lane l copies the 16 bytes at
-// voff + soff and writes them at dst + 16 l.  Only voff is range checked.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                             unsigned char* dst_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst_wave_base, 16, voff, soff, 0, 0);
+// voff and writes them at dst + 16 l (voff is what the range check covers).
+// Issued as inline assembly on purpose: the compiler then does not track the
+// LDS write, so it adds no vmcnt wait before reads of the other buffer (the
+// kernel orders every copy itself with explicit vmcnt waits and barriers).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                             const unsigned char* dst_wave_base) {
+  const uint32_t lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)dst_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
-constexpr int kWaves = 8;             // 2 per SIMD
+constexpr int kWaves = 4;              // one per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTB = 2;                // 32-token blocks per wave (64 tokens)
+constexpr int kTB = 4;                 // 32-token blocks per wave (the whole tile)
+constexpr int kPairs = kTB * 16;       // (t, k) pairs per lane
+
+template <int V> using IC = std::integral_constant<int, V>;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 template <typename E, int S, bool GULDS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void affinity_up_kernel(const UpParams p) {
-  using T = E;
   using Tr = Traits<E>;
+  constexpr int EB = Tr::kBytes;
   constexpr int Q = Tr::kQuads;
   constexpr int CPS = Tr::kChunksPerStep;
-  constexpr int EPC = 16 / Tr::kBytes;      // elements per 16-byte chunk
   constexpr int CPR = S * CPS;              // 16-byte chunks per row of a_h
   constexpr int SLOTS = pow2_slots(CPR);
   constexpr int ROWB = SLOTS * 16;
   constexpr int BUFB = kTileTokens * ROWB;
-  constexpr int DMA_A = kTileTokens * SLOTS / kThreads;   // a-tile copies per thread per step
+  constexpr int DMA_A = kTileTokens * SLOTS / kThreads;           // per thread per step
   constexpr int DMA_GU = GULDS ? 2 * kTileTokens * 16 / kThreads : 0;
   constexpr int GU_BYTES = GULDS ? 2 * kTileTokens * 256 : 16;
+  constexpr int NMS = 2 * S * Q;            // folded-weight loads per step
+  constexpr int kSlabBytes = 64 * 8 * EB;   // one (h, kb, gu, s) fragment slab
 
-  // Distinct static LDS objects: the compiler can tell a pending copy into one
-  // a-tile buffer (or the g/u tile) from reads of the other buffer.
+
   __shared__ __attribute__((aligned(16))) unsigned char abuf0[BUFB];
   __shared__ __attribute__((aligned(16))) unsigned char abuf1[BUFB];
   __shared__ __attribute__((aligned(16))) unsigned char gubuf[GU_BYTES];
-  __shared__ __attribute__((aligned(16))) float tokvec[2 * kTokVec];
-  __shared__ __attribute__((aligned(16))) float cbuf[2 * kTileNeurons];
-  extern __shared__ __attribute__((aligned(16))) float accl[];   // [G][2][128] FO sums
+  __shared__ __attribute__((aligned(16))) float tokinv[2 * kTileTokens];   // 1/r, 1/r_next
+  __shared__ __attribute__((aligned(16))) float rraw[4 * kTileTokens];     // r, pad, r_next, pad
+  extern __shared__ __attribute__((aligned(16))) float accl[];             // [G][128] FO sums
+  __shared__ int8_t s_order[kMaxHeads], s_group[kMaxHeads];               // head tables
 
   // workgroup -> (neuron tile, token chunk); consecutive ids alternate XCDs
   const int id = blockIdx.x;
   const int xcd = id & 7, wi = id >> 3;
   const int st = xcd + 8 * (wi >> 5), mem = wi & 31;
   if (st >= p.n_st) return;
-  const int kt = (st % p.n_ktg) * kSuperKt + (mem & 3);
-  const int chunk = (st / p.n_ktg) * kSuperChunks + (mem >> 2);
+  const int kt = (st % p.n_ktg) * kSuperKt + (mem % kSuperKt);
+  const int chunk = (st / p.n_ktg) * kSuperChunks + (mem / kSuperKt);
   if (kt >= p.n_kt || chunk >= p.n_chunks) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int wn = w & 3, wt = w >> 2;         // neuron block, token half
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int H = p.H, G = p.G, I = p.I, d = p.d;
   const int64_t NT = p.T;
   const int KB = p.I32 >> 5;
-  const int nb = kt * 4 + wn;                // this wave's block of 32 neurons
+  const int nb = kt * 4 + w;                 // this wave's block of 32 neurons
   const int nbc = nb < KB ? nb : KB - 1;     // clamped so that M reads stay in bounds
+  const int nl = w * 32 + (l & 31);          // this lane's neuron within the tile
   const int k = nb * 32 + (l & 31);
   const int kc = k < I ? k : I - 1;          // clamped neuron for direct g/u reads
-  const T* a = static_cast<const T*>(p.a);
-  const T* gp = static_cast<const T*>(p.g);
-  const T* up = static_cast<const T*>(p.u);
-  const T* M = static_cast<const T*>(p.M);
-  const bool want_c = p.want_c != 0;
+  const E* gp = static_cast<const E*>(p.g);
+  const E* up = static_cast<const E*>(p.u);
 
-  for (int x = tid; x < G * 2 * kTileNeurons; x += kThreads) accl[x] = 0.f;
+  for (int x = tid; x < G * kTileNeurons; x += kThreads) accl[x] = 0.f;
+  if (tid < kMaxHeads) {
+    s_order[tid] = p.head_order[tid];
+    s_group[tid] = p.head_group[tid];
+  }
+  __syncthreads();
 
   const int tt0 = chunk * kTilesPerChunk;
   const int ntile = min(kTilesPerChunk, p.n_tt - tt0);
   const int nsteps = ntile * H;
 
-  // ---- asynchronous copies into LDS --------------------------------------
-  // a tile of a (token tile, head) step: slot q of the buffer holds row
-  // q / SLOTS, chunk (q % SLOTS) ^ (row % SLOTS).  A wave copies 64
-  // consecutive slots (64 / SLOTS whole rows); rows past T and unused slots
-  // read zeros through the buffer range check.
-  auto dma_a = [&](int step, unsigned char* buf) {
+  // ---- asynchronous copies ---------------------------------------------------
+  // a tile of step `step`: slot q of the buffer holds row q / SLOTS, chunk
+  // (q % SLOTS) ^ (row % SLOTS).  A wave copies 64 consecutive slots (64 /
+  // SLOTS whole rows); rows past T and unused slots read zeros.
+  auto dma_a = [&](int step, const unsigned char* buf) __attribute__((always_inline)) {
     const int ti = step / H;
-    const int h = p.head_order[step - ti * H];
+    const int h = s_order[step - ti * H];
     const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
     const int rows = (int)min((int64_t)kTileTokens, NT - t0);
-    const uint32_t row_bytes = (uint32_t)(H * d * Tr::kBytes);
-    const auto rs = buffer_rsrc(a + (t0 * H + h) * d,
-                                (uint32_t)(rows - 1) * row_bytes + (uint32_t)(d * Tr::kBytes));
+    const uint32_t row_bytes = (uint32_t)(H * d * EB);
+    const auto rs = buffer_rsrc(static_cast<const char*>(p.a) + (t0 * H + h) * (int64_t)d * EB,
+                                (uint32_t)(rows - 1) * row_bytes + (uint32_t)(d * EB));
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
       const int slot0 = (i * kWaves + w) * 64;
-      const int row0 = slot0 / SLOTS;                       // wave-uniform
-      const int row = row0 + l / SLOTS, sl = l % SLOTS;
+      const int row = slot0 / SLOTS + l / SLOTS, sl = l % SLOTS;
       const int c = sl ^ (row & (SLOTS - 1));
-      // the whole offset goes in voff: the range check does not cover soff
       const uint32_t voff = c < CPR ? (uint32_t)row * row_bytes + (uint32_t)(c * 16) : kOutOfRange;
-      dma16(rs, voff, 0u, buf + slot0 * 16);
+      dma16(rs, voff, buf + slot0 * 16);
     }
   };
-  // g and u tiles (bf16, 128 tokens x 128 neurons each; row = 16 chunks of 8
-  // neurons, chunk c of row r in slot c ^ (r & 4): conflict-free reads).  A
-  // wave copies 4 whole rows per instruction; rows past T read zeros.
-  auto dma_gu = [&](int ti) {
+  // g and u tiles of token tile ti (bf16, 128 tokens x 128 neurons each; a row
+  // is 16 chunks of 8 neurons, chunk c of row r in slot c ^ (r & 4)).  A wave
+  // copies 4 whole rows per instruction; rows past T read zeros.
+  auto dma_gu = [&](int ti) __attribute__((always_inline)) {
     if constexpr (GULDS) {
       const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
       const int rows = (int)min((int64_t)kTileTokens, NT - t0);
@@ -171,192 +181,223 @@ void affinity_up_kernel(const UpParams p) {
       const auto ru = buffer_rsrc(up + t0 * I + n0, bytes);
 #pragma unroll
       for (int i = 0; i < DMA_GU; ++i) {
-        const int slot0 = (i * kWaves + w) * 64;   // slot index over [g tile | u tile]
-        const int which = slot0 >= kTileTokens * 16;
-        const int row0 = (slot0 - which * kTileTokens * 16) >> 4;
-        const int row = row0 + (l >> 4);
+        const int slot0 = (i * kWaves + w) * 64;
+        const int which = slot0 >= kTileTokens * 16;       // wave-uniform: g or u
+        const int row = ((slot0 - which * kTileTokens * 16) >> 4) + (l >> 4);
         const int c = (l & 15) ^ (row & 4);
-        const uint32_t voff = (uint32_t)row * row_bytes + (uint32_t)(c * 16);
-        dma16(which ? ru : rg, voff, 0u, gubuf + slot0 * 16);
+        dma16(which ? ru : rg, (uint32_t)row * row_bytes + (uint32_t)(c * 16), gubuf + slot0 * 16);
       }
     }
   };
-  auto stage_tokvec = [&](int ti, int tb) {
-    if (tid < kTileTokens) {
-      const int64_t t = (int64_t)(tt0 + ti) * kTileTokens + tid;
-      float ri = 0.f, rn = 0.f;
-      if (t < NT) {
-        ri = __builtin_amdgcn_rcpf(p.r[t]);
-        if (want_c) rn = __builtin_amdgcn_rcpf(p.r_next[t]);
-      }
-      float* tv = tokvec + tb * kTokVec;
-      tv[tid] = ri;
-      tv[kTileTokens + tid] = rn;
+  // r and r_next of token tile ti (wave 0; 32 lanes x 16 bytes each, the
+  // other 32 lanes read zeros into padding); tokens past T read zeros
+  auto dma_tok = [&](int ti) __attribute__((always_inline)) {
+    if (w == 0) {
+      const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
+      const uint32_t bytes = (uint32_t)min((int64_t)kTileTokens, NT - t0) * 4u;
+      const uint32_t voff = l < 32 ? (uint32_t)l * 16u : kOutOfRange;
+      dma16(buffer_rsrc(p.r + t0, bytes), voff, reinterpret_cast<unsigned char*>(rraw));
+      dma16(buffer_rsrc(p.r_next + t0, bytes), voff,
+            reinterpret_cast<unsigned char*>(rraw + 2 * kTileTokens));
     }
   };
 
-  // ---- registers ------------------------------------------------------------
+  // ---- registers ---------------------------------------------------------------
   f32x16 accG[kTB], accU[kTB];
-  float coefA[kTB][16], coefB[kTB][16];
+  // (A, B) of each pair: a packed fp16 pair on the bf16 path (one register,
+  // rounded to nearest; the epilogue widens it inside v_fma_mix), fp32 on the
+  // fp32 path
+  using Coef = std::conditional_t<sizeof(E) == 2, half2_t, float2_t>;
+  Coef cAB[kTB][16];
   float fo_run[kTB];
 #pragma unroll
   for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
   float c_acc = 0.f;
-  constexpr int kSlabBytes = 64 * 8 * Tr::kBytes;      // one (h, kb, gu, s) fragment slab
-  const char* Mbytes = reinterpret_cast<const char*>(M);
-  const uint32_t mlane = (uint32_t)l * 8u * Tr::kBytes;
-  // M fragments stream through a ring of D register slots: K-step s of a
-  // step uses slot s % D, and right after its MFMAs the slot is refilled with
-  // the K-step D positions later (in this step or the next one).
-  constexpr int D = (S % 2 == 0) ? S / 2 : S;
-  constexpr int NM = 2 * D * Q;   // M loads that may be outstanding at a step boundary
-  uint4 mreg[D][2][Q];
-  auto load_m = [&](int slot, int s, int h) {
+  const char* Mbytes = static_cast<const char*>(p.M);
+  const uint32_t mlane = (uint32_t)l * 8u * EB;
+  uint4 mreg[S][2][Q];        // the head's folded-weight fragments, all d-steps
+  auto load_m = [&](int s, int h) __attribute__((always_inline)) {
     // wave-uniform base of (h, this wave's neuron block), per-lane 32-bit offset
     const char* Mh = Mbytes + ((int64_t)h * KB + nbc) * 2 * S * kSlabBytes;
 #pragma unroll
     for (int qq = 0; qq < Q; ++qq) {
-      mreg[slot][0][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + s * kSlabBytes + qq * 16);
-      mreg[slot][1][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + (S + s) * kSlabBytes + qq * 16);
+      mreg[s][0][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + s * kSlabBytes + qq * 16);
+      mreg[s][1][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + (S + s) * kSlabBytes + qq * 16);
     }
   };
-  const int row0 = wt * 64;                            // first token row of this wave
 
-  // operating-point coefficients of tile ti (shared by all heads)
-  auto coefficients = [&](int ti) {
-    const float* tv = tokvec + (ti & 1) * kTokVec;
+  // operating-point coefficients of token tile ti (shared by all heads)
+  auto burst = [&](int ti) __attribute__((always_inline)) {
+    // this tile's g/u copies completed before the step-start wait; the
+    // barrier makes every wave's copies visible
+    __syncthreads();
+    {
+      const int64_t t = (int64_t)(tt0 + ti) * kTileTokens + (tid & (kTileTokens - 1));
+      const bool ok = t < NT && (tid < kTileTokens || p.want_c);
+      const float rv = rraw[(tid < kTileTokens ? 0 : 2 * kTileTokens) + (tid & (kTileTokens - 1))];
+      tokinv[tid] = ok ? __builtin_amdgcn_rcpf(rv) : 0.f;
+    }
+    __syncthreads();
     const int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
-    const int nl = wn * 32 + (l & 31);                  // neuron within the tile
+    const int last = (int)min((int64_t)kTileTokens, NT - tbase) - 1;
+    // Every row this lane reads has (row & 4) == 4 (l >> 5), so the swizzled
+    // g/u address is a per-lane base plus a compile-time row offset (nothing
+    // per (row, lane) to keep live across the step loop).
+    const int half = l >> 5;
+    const unsigned char* gu_lane =
+        gubuf + half * 4 * 256 + ((((nl >> 3) ^ (half * 4)) << 4) | ((nl & 7) * 2));
+    const float* tok_lane = tokinv + 4 * half;
 #pragma unroll
     for (int tb = 0; tb < kTB; ++tb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row0 + tb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        float gv, uv;
-        if constexpr (GULDS) {
-          const int off = row * 256 + (((nl >> 3) ^ (row & 4)) << 4) + (nl & 7) * 2;
-          gv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(gubuf + off));
-          uv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(gubuf + kTileTokens * 256 + off));
-        } else {
-          const int last = (int)min((int64_t)kTileTokens, NT - tbase) - 1;
-          const int rr = row < last ? row : last;
-          const uint32_t off = (uint32_t)rr * (uint32_t)I + (uint32_t)kc;
-          gv = load_elem(gp + tbase * I, off);
-          uv = load_elem(up + tbase * I, off);
+      for (int vq = 0; vq < 4; ++vq) {
+        const int rowb = tb * 32 + 8 * vq;                 // + 4 (l >> 5)
+        const float4 ri4 = *reinterpret_cast<const float4*>(tok_lane + rowb);
+        const float4 rn4 = *reinterpret_cast<const float4*>(tok_lane + kTileTokens + rowb);
+        const float ri[4] = {ri4.x, ri4.y, ri4.z, ri4.w};
+        const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rowb + 4 * half + i, v = vq * 4 + i;
+          float gv, uv;
+          if constexpr (GULDS) {
+            const int roff = (rowb + i) * 256;
+            gv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(gu_lane + roff));
+            uv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(gu_lane + kTileTokens * 256 + roff));
+          } else {
+            const int rr = row < last ? row : last;
+            const int64_t off = (tbase + rr) * I + kc;
+            if constexpr (sizeof(E) == 2) {
+              gv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(gp)[off]);
+              uv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(up)[off]);
+            } else {
+              gv = gp[off];
+              uv = up[off];
+            }
+          }
+          const float ex = __builtin_amdgcn_exp2f(-1.4426950408889634f * gv);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + ex);     // logistic sigma(g)
+          const float silu = gv * sg;
+          const float dsilu = fmaf(silu, 1.0f - sg, sg);         // sigma (1 + g (1 - sigma))
+          using CT = std::conditional_t<sizeof(E) == 2, _Float16, float>;
+          cAB[tb][v] = Coef{(CT)(dsilu * uv * ri[i]), (CT)(silu * ri[i])};
+          const float al = silu * uv * rn[i];
+          c_acc = fmaf(al, al, c_acc);
         }
-        const float ri = tv[row];
-        const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * gv);
-        const float sg = __builtin_amdgcn_rcpf(1.0f + e);     // logistic sigma(g)
-        const float silu = gv * sg;
-        const float dsilu = fmaf(silu, 1.0f - sg, sg);         // sigma (1 + g (1 - sigma))
-        coefA[tb][v] = dsilu * uv * ri;
-        coefB[tb][v] = silu * ri;
-        const float al = silu * uv * tv[kTileTokens + row];
-        c_acc = fmaf(al, al, c_acc);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __syncthreads();                            // g/u tile and 1/r read by every wave
+    if (ti + 1 < ntile) {
+      dma_tok(ti + 1);
+      dma_gu(ti + 1);
+    }
   };
 
-  // one (token tile, head) step reading a-tile buffer `ab`
-  auto step_body = [&](int step, const unsigned char* ab, unsigned char* ab_next) {
-    const int ti = step / H, hi = step - ti * H;
-    const int grp = p.head_group[hi];
-    const int h = p.head_order[hi];
-    const bool has_next = step + 1 < nsteps;
-    // head of the next step (the last step refills with its own head: the
-    // loads stay in bounds and are simply not used)
-    const int hn = has_next ? p.head_order[(hi + 1) % H] : h;
-    if (has_next) dma_a(step + 1, ab_next);
-    const bool gu_now = GULDS && hi == 0 && ti + 1 < ntile;
-    if (gu_now) dma_gu(ti + 1);
-    if (hi == 0 && ti + 1 < ntile) stage_tokvec(ti + 1, (ti + 1) & 1);
+  // epilogue of pair v of token block tb
+  auto epi_pair = [&](int tb, int v) __attribute__((always_inline)) {
+    const float pg = accG[tb][v], pu = accU[tb][v];
+    const Coef c = cAB[tb][v];
+    const float dl = fmaf((float)c.x, pg, fmaf((float)c.y, pu, 0.0f));
+    fo_run[tb] = fmaf(dl, dl, fo_run[tb]);
+  };
+  // KV group grp ends: fold the lane sums into its LDS slot (lanes l and l+32
+  // hold the same neuron)
+  auto flush = [&](int grp) __attribute__((always_inline)) {
+    float fo = (fo_run[0] + fo_run[1]) + (fo_run[2] + fo_run[3]);
+    fo += __shfl_xor(fo, 32);
+    if (l < 32) accl[grp * kTileNeurons + nl] += fo;
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
+  };
 
+  // ---- one (token tile, head) step ------------------------------------------------
+  auto step = [&](int s) __attribute__((always_inline)) {
+    const int ti = s / H, hi = s - ti * H;
+    const bool has_next = s + 1 < nsteps;
+    const int hn = has_next ? s_order[hi + 1 == H ? 0 : hi + 1] : s_order[hi];
+    // Everything this wave issued before this point has landed: the a tile of
+    // this step (copied one step earlier), this head's folded-weight
+    // fragments (refilled during the previous step's last chain) and, after a
+    // tile's first step, the next tile's g/u copies.  The copy of the next a
+    // tile is issued only after this wait, so it overlaps the whole step.
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __syncthreads();
+    const bool odd = (s & 1) != 0;
+    const unsigned char* ab = odd ? abuf1 : abuf0;
+    if (has_next) dma_a(s + 1, odd ? abuf0 : abuf1);
+
+    // a fragments go through a 3-slot register ring, read two contraction
+    // steps ahead so that LDS latency hides behind the MFMAs
+    constexpr int NQ = kTB * S;
+    uint4 afr[3][Q];
+    auto read_af = [&](int q, uint4 (&dst)[Q]) __attribute__((always_inline)) {
+      const int row = (q / S) * 32 + (l & 31), ks = q % S;
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
-      accG[tb] = f32x16{};
-      accU[tb] = f32x16{};
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-#pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) {
-        const int row = row0 + tb * 32 + (l & 31);
-        uint4 af[Q];
-#pragma unroll
-        for (int qq = 0; qq < Q; ++qq) {
-          const int col = s * CPS + (l >> 5) * Q + qq;
-          af[qq] = *reinterpret_cast<const uint4*>(ab + row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4));
-        }
-        mma(accG[tb], af, mreg[s % D][0]);
-        mma(accU[tb], af, mreg[s % D][1]);
+      for (int qq = 0; qq < Q; ++qq) {
+        const int col = ks * CPS + (l >> 5) * Q + qq;
+        dst[qq] = *reinterpret_cast<const uint4*>(ab + row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4));
       }
-      if (s + D < S) load_m(s % D, s + D, h);
-      else load_m(s % D, s + D - S, hn);
+    };
+    read_af(0, afr[0]);
+    if (NQ > 1) read_af(1, afr[1]);
+    auto body = [&](int q) __attribute__((always_inline)) {
+      const int tb = q / S, ks = q % S;
+      // the chain before this one: token block tb - 1 of this head, or the
+      // previous head's last block
+      const int ptb = tb == 0 ? kTB - 1 : tb - 1;
+      if (q + 2 < NQ) read_af(q + 2, afr[(q + 2) % 3]);
+      if (ks == 0) {
+        accG[tb] = f32x16{};
+        accU[tb] = f32x16{};
+      }
+      // a slice of the previous chain's epilogue (other accumulators)
+      if (tb > 0 || s > 0) {
+#pragma unroll
+        for (int v = ks * 16 / S; v < (ks + 1) * 16 / S; ++v) epi_pair(ptb, v);
+      }
+      mma(accG[tb], afr[q % 3], mreg[ks][0]);
+      mma(accU[tb], afr[q % 3], mreg[ks][1]);
+      // after the last chain's use, refill with the next head's fragments
+      if (tb == kTB - 1) load_m(ks, hn);
       __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // fused epilogue: eq. (5) and its square
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    // chain 0, which also finishes the previous head's epilogue
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pg = accG[tb][v], pu = accU[tb][v];
-        const float dl = fmaf(coefA[tb][v], pg, coefB[tb][v] * pu);
-        fo_run[tb] = fmaf(dl, dl, fo_run[tb]);
-      }
+    for (int q = 0; q < S; ++q) body(q);
+    if (s > 0) {
+      // the previous head is complete: flush if it ends its KV group
+      const int hp = hi == 0 ? H - 1 : hi - 1;
+      const int grp = s_group[hp];
+      if (hp == H - 1 || s_group[hp + 1] != grp) flush(grp);
     }
-    if (hi == H - 1 || p.head_group[hi + 1] != grp) {
-      // lanes l and l + 32 hold the same neuron (other token rows)
-      float fo = fo_run[0];
+    if (hi == 0) burst(ti);   // coefficients of this tile, used from chain 1 on
+    // chains 1 .. 3
 #pragma unroll
-      for (int tb = 1; tb < kTB; ++tb) fo += fo_run[tb];
-      fo += __shfl_xor(fo, 32);
-      if (l < 32) accl[(grp * 2 + wt) * kTileNeurons + wn * 32 + l] += fo;
-#pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
-    }
-    // publish the next a tile (unless the next step opens a new token tile,
-    // whose coefficient phase waits and synchronises instead)
-    if (has_next && hi + 1 < H) {
-      if (gu_now) __builtin_amdgcn_s_waitcnt(vm_wait(NM + DMA_GU));
-      else __builtin_amdgcn_s_waitcnt(vm_wait(NM));
-      __syncthreads();
-    }
+    for (int q = S; q < NQ; ++q) body(q);
   };
 
-  // ---- prologue ------------------------------------------------------------
-  dma_a(0, abuf0);
+  // ---- prologue and step loop ----------------------------------------------------
   dma_gu(0);
-  stage_tokvec(0, 0);
+  dma_tok(0);
+  dma_a(0, abuf0);
 #pragma unroll
-  for (int s = 0; s < D; ++s) load_m(s, s, p.head_order[0]);
+  for (int ks = 0; ks < S; ++ks) load_m(ks, s_order[0]);
 
-  for (int step = 0; step < nsteps; ++step) {
-    if (step % H == 0) {
-      // new token tile: its a tile, g/u tile and token vectors must be in LDS
-      __builtin_amdgcn_s_waitcnt(vm_wait(NM));
-      __syncthreads();
-      coefficients(step / H);
-      __syncthreads();   // g/u tile fully read before it is refilled
-    }
-    if ((step & 1) == 0) step_body(step, abuf0, abuf1);
-    else step_body(step, abuf1, abuf0);
-  }
+  for (int s = 0; s < nsteps; ++s) step(s);
 
-  // write this workgroup's partial sums (token halves added in fixed order)
-  __builtin_amdgcn_s_waitcnt(vm_wait(0));   // drain the last (unused) M refills
+  // epilogue of the last chain (its head ends the last KV group)
+#pragma unroll
+  for (int v = 0; v < 16; ++v) epi_pair(kTB - 1, v);
+  flush(s_group[H - 1]);
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));   // drain the last (unused) weight refills
+
+  // ---- write this workgroup's partial sums ----------------------------------------
   c_acc += __shfl_xor(c_acc, 32);
-  if (l < 32) cbuf[wt * kTileNeurons + wn * 32 + l] = c_acc;
-  __syncthreads();
-  if (wt == 0 && l < 32 && nb < KB) {
-    const int kk = nb * 32 + l, nl = wn * 32 + l;
-    float* out = p.part + (int64_t)chunk * (G + 1) * p.I32;
-    for (int gg = 0; gg < G; ++gg)
-      out[(int64_t)gg * p.I32 + kk] =
-          accl[(gg * 2 + 0) * kTileNeurons + nl] + accl[(gg * 2 + 1) * kTileNeurons + nl];
-    out[(int64_t)G * p.I32 + kk] = cbuf[nl] + cbuf[kTileNeurons + nl];
+  if (l < 32 && nb < KB) {
+    float* out = p.part + (int64_t)chunk * (G + 1) * p.I32 + nb * 32 + l;
+    for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * p.I32] = accl[gg * kTileNeurons + nl];
+    out[(int64_t)G * p.I32] = c_acc;
   }
 }
 
@@ -454,8 +495,9 @@ UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype) {
   const int cpr = d * esize / 16;
   const size_t bufb = (size_t)kTileTokens * pow2_slots(cpr) * 16;
   const size_t gub = g.gu_lds ? 2 * kTileTokens * 256 : 16;
-  g.dyn_lds_bytes = (size_t)G * 2 * kTileNeurons * sizeof(float);
-  g.lds_bytes = 2 * bufb + gub + (2 * kTokVec + 2 * kTileNeurons) * sizeof(float) + g.dyn_lds_bytes;
+  g.dyn_lds_bytes = (size_t)G * kTileNeurons * sizeof(float);
+  // a double buffer, g/u tile, 1/r and 1/r_next, raw r and r_next, head tables
+  g.lds_bytes = 2 * bufb + gub + 6 * kTileTokens * sizeof(float) + 2 * kMaxHeads + g.dyn_lds_bytes;
   return g;
 }
 

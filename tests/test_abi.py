@@ -146,9 +146,9 @@ def test_workspace_sizes_follow_geometry():
 
 def test_lds_limit_reported_unsupported():
     hna = _lib()
-    # fp32, d = 128 and 32 KV groups need more than 160 KiB of LDS
-    dm = hna.make_dims(256, 4096, 32, 32, 128, 128, 0)
-    rc = call_up(hna, dm, grp=tuple(range(32)))
+    # fp32, d = 128 and 64 KV groups need more than 160 KiB of LDS
+    dm = hna.make_dims(256, 4096, 64, 64, 128, 128, 0)
+    rc = call_up(hna, dm, grp=tuple(range(64)))
     assert rc == -2 and "LDS" in hna.last_error()
 
 
