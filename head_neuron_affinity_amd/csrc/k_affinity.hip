@@ -11,14 +11,15 @@
 //   * once per token tile each lane computes the operating-point
 //     coefficients A = silu'(g) u / r and B = silu(g) / r of its 64 (t, k)
 //     pairs (registers) and the down-edge moment (alpha / r_next)^2;
-//   * per head h (in KV-group order) the wave runs four contraction chains,
-//     one per 32-token block: 2 x d/16 MFMAs 32x32x16 into gate and up
-//     accumulators, giving r * (p_h.w^g_k, p_h.w^u_k);
-//   * the epilogue of each chain, Delta = A Pg + B Pu and fo += Delta^2, is
-//     spread over the MFMAs of the next chain (the last block's over the next
-//     head's first chain), so the VALU and the matrix cores overlap within
-//     the wave; the folded-weight fragments of a head stay in registers for
-//     all four chains and are refilled with the next head's during the last;
+//   * per head h (in KV-group order) the wave runs the contraction a_h . M_h
+//     on the matrix cores as two chain pairs (token blocks 0-1, then 2-3),
+//     2 x 2 x d/16 MFMAs 32x32x16 each into gate and up accumulators, giving
+//     r * (p_h.w^g_k, p_h.w^u_k); four independent accumulators are in flight;
+//   * the epilogue of each chain pair, Delta = A Pg + B Pu and fo += Delta^2,
+//     is spread over the MFMAs of the next pair (the second pair's over the
+//     next head's first), so the VALU and the matrix cores overlap within the
+//     wave; the folded-weight fragments of a head stay in registers for both
+//     pairs and are refilled with the next head's during the second;
 //   * at the end of a KV group the per-lane sums go to an LDS slot of that
 //     group; nothing of size T x H x I leaves the chip: each workgroup writes
 //     one [G+1, 128] block of fp32 partial sums, reduced later in fixed order.
@@ -327,42 +328,55 @@ void affinity_up_kernel(const UpParams p) {
     const unsigned char* ab = odd ? abuf1 : abuf0;
     if (has_next) dma_a(s + 1, odd ? abuf0 : abuf1);
 
-    // a fragments go through a 3-slot register ring, read two contraction
-    // steps ahead so that LDS latency hides behind the MFMAs
-    constexpr int NQ = kTB * S;
-    uint4 afr[3][Q];
-    auto read_af = [&](int q, uint4 (&dst)[Q]) __attribute__((always_inline)) {
-      const int row = (q / S) * 32 + (l & 31), ks = q % S;
+    // Two token blocks' chains run together (four independent accumulators,
+    // enough to keep the matrix pipeline full); the a fragments go through a
+    // 3-slot register ring, read two contraction steps ahead so that LDS
+    // latency hides behind the MFMAs.
+    constexpr int NQ = 2 * S;   // (chain pair, d-step)
+    uint4 afr[3][2][Q];
+    auto read_af = [&](int q, uint4 (&dst)[2][Q]) __attribute__((always_inline)) {
+      const int ks = q % S;
 #pragma unroll
-      for (int qq = 0; qq < Q; ++qq) {
-        const int col = ks * CPS + (l >> 5) * Q + qq;
-        dst[qq] = *reinterpret_cast<const uint4*>(ab + row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4));
+      for (int j = 0; j < 2; ++j) {
+        const int row = (2 * (q / S) + j) * 32 + (l & 31);
+#pragma unroll
+        for (int qq = 0; qq < Q; ++qq) {
+          const int col = ks * CPS + (l >> 5) * Q + qq;
+          dst[j][qq] =
+              *reinterpret_cast<const uint4*>(ab + row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4));
+        }
       }
     };
     read_af(0, afr[0]);
     if (NQ > 1) read_af(1, afr[1]);
     auto body = [&](int q) __attribute__((always_inline)) {
-      const int tb = q / S, ks = q % S;
-      // the chain before this one: token block tb - 1 of this head, or the
-      // previous head's last block
-      const int ptb = tb == 0 ? kTB - 1 : tb - 1;
+      const int pr = q / S, ks = q % S;
+      // the chain pair before this one: pair 0 of this head, or the previous
+      // head's pair 1 (token blocks 2 and 3)
+      const int ppr = pr == 0 ? 1 : 0;
       if (q + 2 < NQ) read_af(q + 2, afr[(q + 2) % 3]);
       if (ks == 0) {
-        accG[tb] = f32x16{};
-        accU[tb] = f32x16{};
-      }
-      // a slice of the previous chain's epilogue (other accumulators)
-      if (tb > 0 || s > 0) {
 #pragma unroll
-        for (int v = ks * 16 / S; v < (ks + 1) * 16 / S; ++v) epi_pair(ptb, v);
+        for (int j = 0; j < 2; ++j) {
+          accG[2 * pr + j] = f32x16{};
+          accU[2 * pr + j] = f32x16{};
+        }
       }
-      mma(accG[tb], afr[q % 3], mreg[ks][0]);
-      mma(accU[tb], afr[q % 3], mreg[ks][1]);
-      // after the last chain's use, refill with the next head's fragments
-      if (tb == kTB - 1) load_m(ks, hn);
+      // a slice of the previous pair's epilogue (other accumulators)
+      if (pr > 0 || s > 0) {
+#pragma unroll
+        for (int x = ks * 32 / S; x < (ks + 1) * 32 / S; ++x) epi_pair(2 * ppr + (x >> 4), x & 15);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        mma(accG[2 * pr + j], afr[q % 3][j], mreg[ks][0]);
+        mma(accU[2 * pr + j], afr[q % 3][j], mreg[ks][1]);
+      }
+      // after the last pair's use, refill with the next head's fragments
+      if (pr == 1) load_m(ks, hn);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // chain 0, which also finishes the previous head's epilogue
+    // pair 0 (token blocks 0, 1), which also finishes the previous head
 #pragma unroll
     for (int q = 0; q < S; ++q) body(q);
     if (s > 0) {
@@ -371,8 +385,8 @@ void affinity_up_kernel(const UpParams p) {
       const int grp = s_group[hp];
       if (hp == H - 1 || s_group[hp + 1] != grp) flush(grp);
     }
-    if (hi == 0) burst(ti);   // coefficients of this tile, used from chain 1 on
-    // chains 1 .. 3
+    if (hi == 0) burst(ti);   // coefficients of this tile, used from pair 1 on
+    // pair 1 (token blocks 2, 3)
 #pragma unroll
     for (int q = S; q < NQ; ++q) body(q);
   };
@@ -386,9 +400,12 @@ void affinity_up_kernel(const UpParams p) {
 
   for (int s = 0; s < nsteps; ++s) step(s);
 
-  // epilogue of the last chain (its head ends the last KV group)
+  // epilogue of the last pair (its head ends the last KV group)
 #pragma unroll
-  for (int v = 0; v < 16; ++v) epi_pair(kTB - 1, v);
+  for (int v = 0; v < 16; ++v) {
+    epi_pair(kTB - 2, v);
+    epi_pair(kTB - 1, v);
+  }
   flush(s_group[H - 1]);
   __builtin_amdgcn_s_waitcnt(vm_wait(0));   // drain the last (unused) weight refills
 
