@@ -434,8 +434,19 @@ __global__ __launch_bounds__(256) void finalize_up_kernel(const float* __restric
   double v;
   if (row < G || row == 2 * G) {
     const int prow = row < G ? row : G;
+    // chunks in order; eight loads in flight before they are added
+    const float* src = part + (int64_t)prow * I32 + k;
+    const int64_t stride = (int64_t)(G + 1) * I32;
     double s = 0.0;
-    for (int c = 0; c < n_chunks; ++c) s += part[((int64_t)c * (G + 1) + prow) * I32 + k];
+    int c = 0;
+    for (; c + 8 <= n_chunks; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = src[(c + j) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += (double)v[j];
+    }
+    for (; c < n_chunks; ++c) s += (double)src[c * stride];
     v = s * (double)scale;
     if (row < G) {
       v *= (double)wd_sq[k];

@@ -65,39 +65,52 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
-  const int items = (kGramStage / 4) * (d / 8);   // (4 tokens) x (8 features)
+  // One (4 tokens) x (8 features) item per thread (d <= 128); the next
+  // stage's item is loaded into registers while the current stage's MFMAs run.
+  const int items = (kGramStage / 4) * (d / 8);
+  const bool has_item = tid < items;
+  const int tq = tid % (kGramStage / 4), fo = tid / (kGramStage / 4);
+  constexpr int NV = sizeof(E) == 2 ? 1 : 2;   // 16-byte loads per token
+  uint4 raw[4][NV];
+  float rr[4];
+  auto load_item = [&](int64_t ts) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = ts + 4 * tq + j;
+      if (has_item && t < t_end) {
+        rr[j] = p.r[t];
+        const char* src = static_cast<const char*>(p.a) + ((t * H + h) * d + 8 * fo) * sizeof(E);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) raw[j][v] = reinterpret_cast<const uint4*>(src)[v];
+      } else {
+        rr[j] = 0.f;   // marks a token outside the chunk: weight 0, values 0
+#pragma unroll
+        for (int v = 0; v < NV; ++v) raw[j][v] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_item(t_begin);
   for (int64_t ts = t_begin; ts < t_end; ts += kGramStage) {
     __syncthreads();   // the previous stage has been read
-    for (int it = tid; it < items; it += kGThreads) {
-      const int tq = it % (kGramStage / 4), fo = it / (kGramStage / 4);
+    if (has_item) {
       float x[4][8];
       float wt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t t = ts + 4 * tq + j;
-        if (t < t_end) {
-          const float r = p.r[t];
-          wt[j] = 1.0f / (r * r);
-          const int64_t off = (t * H + h) * d + 8 * fo;
-          if constexpr (sizeof(E) == 2) {
-            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.a) + off);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        wt[j] = rr[j] != 0.f ? 1.0f / (rr[j] * rr[j]) : 0.f;
+        if constexpr (sizeof(E) == 2) {
+          const uint32_t wv[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[j][2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
-              x[j][2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
-            }
-          } else {
-            const float* src = static_cast<const float*>(p.a) + off;
-            const float4 v0 = *reinterpret_cast<const float4*>(src);
-            const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-            x[j][0] = v0.x; x[j][1] = v0.y; x[j][2] = v0.z; x[j][3] = v0.w;
-            x[j][4] = v1.x; x[j][5] = v1.y; x[j][6] = v1.z; x[j][7] = v1.w;
+          for (int e = 0; e < 4; ++e) {
+            x[j][2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
+            x[j][2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
           }
         } else {
-          wt[j] = 0.f;
+          const uint32_t wv[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
+                                  raw[j][NV - 1].x, raw[j][NV - 1].y, raw[j][NV - 1].z,
+                                  raw[j][NV - 1].w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[j][e] = 0.f;
+          for (int e = 0; e < 8; ++e) x[j][e] = __uint_as_float(wv[e]);
         }
       }
 #pragma unroll
@@ -126,6 +139,7 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
       }
     }
     __syncthreads();
+    if (ts + kGramStage < t_end) load_item(ts + kGramStage);
     // C[i][j] += sum_t x[i][t] * (x[j][t] / r_t^2): A rows i, B rows j
 #pragma unroll
     for (int q = 0; q < kGramStage / 16; ++q) {

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in
 }
 
 // out[k] = sum_r W[r][k]^2 for a row-major [rows, cols] matrix.
-// 64 columns per block, 4 row lanes; the 4 lane sums are added in fixed order.
+// Scalar form (any column count): 64 columns per block, 4 row lanes; the 4
+// lane sums are added in fixed order.
 template <int BF16>
 __global__ __launch_bounds__(256) void col_sqnorm_kernel(const void* __restrict__ Wv, int rows,
                                                          int cols, float* __restrict__ out) {
@@ -52,6 +53,55 @@ __global__ __launch_bounds__(256) void col_sqnorm_kernel(const void* __restrict_
   part[ry][cx] = s;
   __syncthreads();
   if (ry == 0 && c < cols) out[c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
+}
+
+// Vector form (16-byte aligned rows): a block covers 4 groups of EPC columns
+// (one 16-byte load each) x 64 row lanes, several rows in flight per thread;
+// the 64 lane sums of a column are added in a fixed tree order.
+template <int BF16>
+__global__ __launch_bounds__(256) void col_sqnorm16_kernel(const void* __restrict__ Wv, int rows,
+                                                           int cols, float* __restrict__ out) {
+  constexpr int EPC = BF16 ? 8 : 4;
+  __shared__ float part[64][4 * EPC + 1];
+  const int cg = threadIdx.x & 3, rl = threadIdx.x >> 2;
+  const int c0 = (blockIdx.x * 4 + cg) * EPC;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  if (c0 < cols) {
+    const char* base = static_cast<const char*>(Wv) + (int64_t)c0 * (BF16 ? 2 : 4);
+    const int64_t pitch = (int64_t)cols * (BF16 ? 2 : 4);
+#pragma unroll 4
+    for (int r = rl; r < rows; r += 64) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + r * pitch);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) {
+          const float lo = bf16_bits_to_f32(w[q] & 0xffffu), hi = bf16_bits_to_f32(w[q] >> 16);
+          acc[2 * q] = fmaf(lo, lo, acc[2 * q]);
+          acc[2 * q + 1] = fmaf(hi, hi, acc[2 * q + 1]);
+        } else {
+          const float f = __uint_as_float(w[q]);
+          acc[q] = fmaf(f, f, acc[q]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[rl][cg * EPC + e] = acc[e];
+  __syncthreads();
+  for (int half = 32; half >= 1; half >>= 1) {
+    for (int x = threadIdx.x; x < half * 4 * EPC; x += 256) {
+      const int r = x / (4 * EPC), c = x - r * (4 * EPC);
+      part[r][c] += part[r + half][c];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < 4 * EPC) {
+    const int c = blockIdx.x * 4 * EPC + threadIdx.x;
+    if (c < cols) out[c] = part[0][threadIdx.x];
+  }
 }
 
 struct SegList {
@@ -98,7 +148,14 @@ hipError_t launch_transpose(const void* in, void* out, int rows, int cols, int e
 hipError_t launch_col_sqnorm(const void* W, int rows, int cols, int dtype, float* out,
                              hipStream_t st) {
   if (cols == 0) return hipSuccess;
-  dim3 grid((cols + 63) / 64);
+  const int epc = dtype == 1 ? 8 : 4;
+  if (cols % epc == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
+    const dim3 grid((cols + 4 * epc - 1) / (4 * epc));
+    if (dtype == 1) hipLaunchKernelGGL(col_sqnorm16_kernel<1>, grid, dim3(256), 0, st, W, rows, cols, out);
+    else hipLaunchKernelGGL(col_sqnorm16_kernel<0>, grid, dim3(256), 0, st, W, rows, cols, out);
+    return hipGetLastError();
+  }
+  const dim3 grid((cols + 63) / 64);
   if (dtype == 1) hipLaunchKernelGGL(col_sqnorm_kernel<1>, grid, dim3(256), 0, st, W, rows, cols, out);
   else hipLaunchKernelGGL(col_sqnorm_kernel<0>, grid, dim3(256), 0, st, W, rows, cols, out);
   return hipGetLastError();
