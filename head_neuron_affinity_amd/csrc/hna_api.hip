@@ -102,8 +102,12 @@ int check_map(const char* fn, const int32_t* map, int H, int G) {
   return HNA_OK;
 }
 
+// The GEMMs' left operand is written once, scaled and transposed; bf16 keeps it
+// as a high part plus a remainder (two planes).
+size_t xs_planes(int dtype) { return dtype == HNA_BF16 ? 2 : 1; }
+
 size_t fold_ws_bytes(const hna_dims* dm) {
-  return align256((size_t)dm->H * dm->d * dm->hidden * esize_of(dm->dtype));
+  return align256((size_t)dm->H * dm->d * dm->hidden * esize_of(dm->dtype) * xs_planes(dm->dtype));
 }
 
 size_t up_ws_bytes(const hna_dims* dm) {
@@ -111,7 +115,7 @@ size_t up_ws_bytes(const hna_dims* dm) {
 }
 
 size_t down_ws_transposed(const hna_down_dims* dm) {
-  return align256((size_t)dm->I * dm->hidden * esize_of(dm->dtype));
+  return align256((size_t)dm->I * dm->hidden * esize_of(dm->dtype) * xs_planes(dm->dtype));
 }
 size_t down_ws_bytes(const hna_down_dims* dm) {
   return down_ws_transposed(dm) + align256((size_t)(dm->H + 2 * dm->G) * dm->I * sizeof(float));
@@ -167,13 +171,12 @@ int hna_fold_up_weights(const hna_dims* dm, const void* W_o, const float* gamma,
     return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need_ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int Hd = dm->H * dm->d;
-  hipError_t e = launch_transpose(W_o, workspace, dm->hidden, Hd, esize_of(dm->dtype), st);
+  hipError_t e = launch_scale_transpose(W_o, gamma, workspace, dm->hidden, Hd, dm->dtype, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   GemmParams p{};
   p.X = workspace;
   p.Y[0] = W_gate;
   p.Y[1] = W_up;
-  p.s = gamma;
   p.ldx = dm->hidden;
   p.ldy = dm->hidden;
   p.Mrows = Hd;
@@ -380,8 +383,7 @@ int hna_down_weight_norms(const hna_down_dims* dm, const void* W_q, const void* 
   if (workspace_bytes < need)
     return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int es = esize_of(dm->dtype);
-  hipError_t e = launch_transpose(W_down, workspace, dm->hidden, dm->I, es, st);
+  hipError_t e = launch_scale_transpose(W_down, gamma_next, workspace, dm->hidden, dm->I, dm->dtype, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   float* seg_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + down_ws_transposed(dm));
   GemmParams p{};
@@ -389,7 +391,6 @@ int hna_down_weight_norms(const hna_down_dims* dm, const void* W_q, const void* 
   p.Y[0] = W_q;
   p.Y[1] = W_k;
   p.Y[2] = W_v;
-  p.s = gamma_next;
   p.ldx = dm->hidden;
   p.ldy = dm->hidden;
   p.Mrows = dm->I;

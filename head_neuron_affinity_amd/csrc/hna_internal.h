@@ -124,8 +124,6 @@ hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, float* C, 
 hipError_t launch_quad(const QuadParams& p, int dtype, hipStream_t st);
 
 // --------------------------------------------------------------- small kernels
-hipError_t launch_transpose(const void* in, void* out, int rows, int cols, int esize,
-                            hipStream_t st);
 hipError_t launch_col_sqnorm(const void* W, int rows, int cols, int dtype, float* out,
                              hipStream_t st);
 hipError_t launch_down_group_sum(const float* seg_part, const int16_t* seg_list,
@@ -135,15 +133,16 @@ hipError_t launch_down_combine(const float* c, const float* n, int I, int G_next
                                float* S_down, hipStream_t st);
 
 // ------------------------------------------------------ scaled NT GEMM (MFMA)
-// C[m, n] = sum_c X[m, c] * s[c] * Y[n, c]; X [Mrows, K] and Y [N, K] row-major
-// with c contiguous.  Epilogues: write the folded layout, or sum C^2 over the
-// n of a segment.
+// C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] (for bf16: a high plane and
+// a remainder plane, Mrows*K elements apart) and Y [N, K] row-major with c
+// contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a
+// row-major X [K, Mrows].  Epilogues: write the folded layout, or sum C^2 over
+// the n of a segment.
 enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1 };
 
 struct GemmParams {
-  const void* X;       // [Mrows, K]
+  const void* X;       // Xs [Mrows, K] (bf16: two planes)
   const void* Y[3];    // fold: Y[0] = W_gate, Y[1] = W_up; segsq: W_q, W_k, W_v
-  const float* s;      // [K]
   int64_t ldx, ldy;
   int Mrows, N, K;     // fold: N = I32 (rows of Y beyond Nvalid are zero)
   int Nvalid;
@@ -154,6 +153,8 @@ struct GemmParams {
   float* seg_part;     // [n_seg][Mrows]
   int H_next, G_next, d_next;
 };
+hipError_t launch_scale_transpose(const void* X, const float* s, void* Xs, int K, int Mrows,
+                                  int dtype, hipStream_t st);
 hipError_t launch_gemm(const GemmParams& p, int dtype, int epilogue, dim3 grid,
                        hipStream_t st);
 

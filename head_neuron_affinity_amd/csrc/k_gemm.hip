@@ -1,16 +1,18 @@
-// Scaled "NT" GEMM on the matrix cores, C[m, n] = sum_c X[m, c] s[c] Y[n, c],
-// with X [Mrows, K] and Y [N, K] row-major (c contiguous).  Two uses, both
-// from section 3 ("Affinity scores") of the affinity-aware sharding paper:
-//   * weight fold: X = W_o^T (rows h*d+j), Y = W_gate or W_up, s = gamma;
+// Scaled "NT" GEMM on the matrix cores, C[m, n] = sum_c s[c] X[c, m] Y[n, c],
+// where X is given as [K, Mrows] (so it is transposed once) and Y is [N, K]
+// row-major.  Two uses, both from section 3 ("Affinity scores") of the
+// affinity-aware sharding paper:
+//   * weight fold: X = W_o (columns h*d+j), Y = W_gate or W_up, s = gamma;
 //     C = M_h[j, k], written in the fragment order the affinity kernel reads;
-//   * down edge: X = W_down^T (rows k), Y = one d'-row segment of W_q, W_k or
+//   * down edge: X = W_down (columns k), Y = one d'-row segment of W_q, W_k or
 //     W_v, s = gamma'; the epilogue squares C and sums over the segment's
 //     rows, so b_gk itself is never stored.
-// bf16 inputs: X is exact in bf16; s*Y is formed in fp32 and split into a
-// bf16 high part and a bf16 remainder, and both are multiplied (2 MFMAs), so
-// the product is accurate to fp32 accumulation.  fp32 inputs use fp32 MFMA.
-// Tile 128 x 128 x 32, 4 waves (2 x 2, 64 x 64 each), LDS double buffer with
-// XOR-swizzled 16-byte chunks.
+// A prep kernel writes Xs[m, c] = s[c] X[c, m] once, transposed; for bf16 it
+// writes Xs as a bf16 high part and a bf16 remainder, both multiplied against
+// the exact bf16 Y (2 MFMAs), so the product is accurate to fp32 accumulation
+// and the GEMM's main loop does no arithmetic besides the MFMAs.  fp32 inputs
+// use fp32 MFMA.  Tile 128 x 128 x 32, 4 waves (2 x 2, 64 x 64 each), LDS
+// double buffer with XOR-swizzled 16-byte chunks.
 #include "hna_internal.h"
 
 namespace hna {
@@ -41,9 +43,99 @@ __device__ inline void mma(f32x16& c, const uint4 (&a)[2], const uint4 (&b)[2]) 
   for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], c, 0, 0, 0);
 }
 
+// Chunk position of (row, 16-byte column) in a tile of CR chunks per row.  The
+// XOR spreads the chunks that one fragment read touches (16 consecutive rows,
+// one column) over 16 distinct 16-byte bank slots, and any 8 consecutive rows
+// over 8 distinct slots of a 128-byte line.
 template <int CR>
 __device__ inline int swz(int row, int col) {
-  return row * CR + (col ^ ((row / (8 / CR)) % CR));
+  return row * CR + (col ^ (((row / (8 / CR)) ^ (row >> 3)) % CR));
+}
+
+// Xs[c, r] = s[r] * in[r, c] for in [rows, cols] row-major; bf16 output goes
+// to two planes (high part at out, remainder at out + cols*rows).  64 x 64
+// tiles through LDS; VEC reads the input rows in 16-byte pieces (needs
+// cols % (16 / sizeof(E)) == 0).  rows is a multiple of 8.
+constexpr int PT = 64;
+template <typename E, bool VEC>
+__global__ __launch_bounds__(256) void scale_transpose_kernel(const E* __restrict__ in,
+                                                              const float* __restrict__ s,
+                                                              E* __restrict__ out, int rows, int cols) {
+  constexpr int EPC = 16 / sizeof(E);
+  constexpr bool kBf = sizeof(E) == 2;
+  __shared__ float tile[PT][PT + 1];
+  const int r0 = blockIdx.y * PT, c0 = blockIdx.x * PT, tid = threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int it = 0; it < PT * PT / EPC / 256; ++it) {
+      const int q = tid + 256 * it;
+      const int cc = q % (PT / EPC), rl = q / (PT / EPC);
+      const int r = r0 + rl, c = c0 + cc * EPC;
+      float f[EPC];
+      if (r < rows && c < cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(in + (int64_t)r * cols + c);
+        const float sv = s[r];
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (kBf) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu) * sv;
+            f[2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16) * sv;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(wv[e]) * sv;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) f[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) tile[rl][cc * EPC + e] = f[e];
+    }
+  } else {
+    const int tx = tid & 63, ty = tid >> 6;
+    for (int i = ty; i < PT; i += 4) {
+      const int r = r0 + i, c = c0 + tx;
+      float v = 0.f;
+      if (r < rows && c < cols) {
+        if constexpr (kBf)
+          v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(in)[(int64_t)r * cols + c]);
+        else
+          v = in[(int64_t)r * cols + c];
+        v *= s[r];
+      }
+      tile[i][tx] = v;
+    }
+  }
+  __syncthreads();
+  const int64_t plane = (int64_t)rows * cols;
+#pragma unroll
+  for (int it = 0; it < PT * PT / EPC / 256; ++it) {
+    const int q = tid + 256 * it;
+    const int kq = q % (PT / EPC), cl = q / (PT / EPC);
+    const int c = c0 + cl, r = r0 + kq * EPC;
+    if (c >= cols || r >= rows) continue;
+    float f[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) f[e] = tile[kq * EPC + e][cl];
+    E* o = out + (int64_t)c * rows + r;
+    if constexpr (kBf) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = f32_to_bf16_bits(f[2 * e]), h1 = f32_to_bf16_bits(f[2 * e + 1]);
+        const uint32_t l0 = f32_to_bf16_bits(f[2 * e] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(f[2 * e + 1] - bf16_bits_to_f32(h1));
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<uint4*>(o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(o + plane) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    } else {
+      *reinterpret_cast<float4*>(o) = make_float4(f[0], f[1], f[2], f[3]);
+    }
+  }
 }
 
 template <typename T, int EPI>
@@ -56,8 +148,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   constexpr int Q = Tr::kQ;
   constexpr int TILE_CHUNKS = BM * CR;
 
-  __shared__ uint4 xs[2][TILE_CHUNKS];
-  __shared__ uint4 ys[2][NSPLIT][TILE_CHUNKS];
+  __shared__ uint4 xs[2][NSPLIT][TILE_CHUNKS];
+  __shared__ uint4 ys[2][TILE_CHUNKS];
   __shared__ float red[2][BM];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -83,62 +175,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     Nrows = p.d_next;
   }
   const T* X = static_cast<const T*>(p.X);
+  const int64_t xplane = (int64_t)p.Mrows * p.ldx;
   const int K = p.K;
 
-  uint4 xr[CPT], yr[CPT][NSPLIT];
+  uint4 xr[CPT][NSPLIT], yr[CPT];
   auto load = [&](int k0) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int q = tid + 256 * c;
       const int row = q / CR, col = q % CR;
       const int kc = k0 + col * EPC;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + row < p.Mrows && kc < K)
-        v = *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + row) * p.ldx + kc);
-      xr[c] = v;
-      float f[8];
-      const bool ok = n0 + row < Nrows && kc < K;
-      if constexpr (NSPLIT == 2) {
-        uint4 yv = make_uint4(0, 0, 0, 0);
-        if (ok) yv = *reinterpret_cast<const uint4*>(Y + (int64_t)(n0 + row) * p.ldy + kc);
-        const uint32_t wv[4] = {yv.x, yv.y, yv.z, yv.w};
+      const bool okx = m0 + row < p.Mrows && kc < K;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
-          f[2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float sv = ok ? f[e] * p.s[kc + e] : 0.f;
-          const uint32_t hb = f32_to_bf16_bits(sv);
-          const uint32_t lb = f32_to_bf16_bits(sv - bf16_bits_to_f32(hb));
-          if (e & 1) { hi[e >> 1] |= hb << 16; lo[e >> 1] |= lb << 16; }
-          else { hi[e >> 1] = hb; lo[e >> 1] = lb; }
-        }
-        yr[c][0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        yr[c][1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      } else {
-        float4 yv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ok) {
-          yv = *reinterpret_cast<const float4*>(Y + (int64_t)(n0 + row) * p.ldy + kc);
-          yv.x *= p.s[kc]; yv.y *= p.s[kc + 1]; yv.z *= p.s[kc + 2]; yv.w *= p.s[kc + 3];
-        }
-        yr[c][0] = make_uint4(__float_as_uint(yv.x), __float_as_uint(yv.y),
-                              __float_as_uint(yv.z), __float_as_uint(yv.w));
-        (void)f;
-      }
+      for (int sp = 0; sp < NSPLIT; ++sp)
+        xr[c][sp] = okx ? *reinterpret_cast<const uint4*>(X + sp * xplane + (int64_t)(m0 + row) * p.ldx + kc)
+                        : make_uint4(0, 0, 0, 0);
+      const bool oky = n0 + row < Nrows && kc < K;
+      yr[c] = oky ? *reinterpret_cast<const uint4*>(Y + (int64_t)(n0 + row) * p.ldy + kc)
+                  : make_uint4(0, 0, 0, 0);
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int q = tid + 256 * c;
-      const int row = q / CR, col = q % CR;
-      const int o = swz<CR>(row, col);
-      xs[buf][o] = xr[c];
+      const int o = swz<CR>(q / CR, q % CR);
 #pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp) ys[buf][sp][o] = yr[c][sp];
+      for (int sp = 0; sp < NSPLIT; ++sp) xs[buf][sp][o] = xr[c][sp];
+      ys[buf][o] = yr[c];
     }
   };
 
@@ -157,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     if (kt + 1 < nk) load((kt + 1) * BK);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      uint4 af[2][Q], bf[2][NSPLIT][Q];
+      uint4 af[2][NSPLIT][Q], bf[2][Q];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int ra = wm * 64 + i * 32 + (l & 31);
@@ -165,41 +229,71 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int qq = 0; qq < Q; ++qq) {
           const int col = s * Tr::kCPS + (l >> 5) * Q + qq;
-          af[i][qq] = xs[buf][swz<CR>(ra, col)];
 #pragma unroll
-          for (int sp = 0; sp < NSPLIT; ++sp) bf[i][sp][qq] = ys[buf][sp][swz<CR>(rb, col)];
+          for (int sp = 0; sp < NSPLIT; ++sp) af[i][sp][qq] = xs[buf][sp][swz<CR>(ra, col)];
+          bf[i][qq] = ys[buf][swz<CR>(rb, col)];
         }
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int sp = 0; sp < NSPLIT; ++sp)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int sp = 0; sp < NSPLIT; ++sp) mma(acc[i][j], af[i], bf[j][sp]);
+          for (int j = 0; j < 2; ++j) mma(acc[i][j], af[i][sp], bf[j]);
     }
     if (kt + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
 
   if (EPI == kEpiFold) {
-    T* Mout = static_cast<T*>(p.M);
+    // Lane l holds rows 8a + 4(l/32) + {0..3} (a = 0..3) of column l%32.  Lanes
+    // l and l^32 swap halves so each lane owns two whole 8-row groups (even a
+    // for l < 32, odd a otherwise); a group of 8 consecutive j of one neuron is
+    // one contiguous 16-byte (bf16) or 32-byte (f32) piece of the fold layout.
+    constexpr int WPR = Tr::kBytes == 2 ? 2 : 4;  // 32-bit words per 4 rows
+    const int up = l >> 5;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        uint32_t mine[4][WPR];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-          const int n = n0 + wn * 64 + j * 32 + (l & 31);
+        for (int a = 0; a < 4; ++a) {
+          if constexpr (Tr::kBytes == 2) {
+            mine[a][0] = f32_to_bf16_bits(acc[i][j][4 * a]) | (f32_to_bf16_bits(acc[i][j][4 * a + 1]) << 16);
+            mine[a][1] = f32_to_bf16_bits(acc[i][j][4 * a + 2]) | (f32_to_bf16_bits(acc[i][j][4 * a + 3]) << 16);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mine[a][v] = __float_as_uint(acc[i][j][4 * a + v]);
+          }
+        }
+        const int n = n0 + wn * 64 + j * 32 + (l & 31);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int ka = 2 * b + up;  // the group this lane keeps
+          uint32_t lo_w[WPR], hi_w[WPR];
+#pragma unroll
+          for (int v = 0; v < WPR; ++v) {
+            const uint32_t send = up ? mine[2 * b][v] : mine[2 * b + 1][v];
+            const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+            const uint32_t keep = up ? mine[2 * b + 1][v] : mine[2 * b][v];
+            lo_w[v] = up ? recv : keep;
+            hi_w[v] = up ? keep : recv;
+          }
+          const int m = m0 + wm * 64 + i * 32 + 8 * ka;
           if (m < p.Mrows && n < p.N) {
             const int h = m / p.d, jj = m - h * p.d;
             const int64_t o = folded_index(h, jj, n, gu, p.KB, p.S);
-            if constexpr (Tr::kBytes == 2)
-              reinterpret_cast<uint16_t*>(Mout)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][v]);
-            else
-              reinterpret_cast<float*>(Mout)[o] = acc[i][j][v];
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<T*>(p.M) + o);
+            if constexpr (Tr::kBytes == 2) {
+              dst[0] = make_uint4(lo_w[0], lo_w[1], hi_w[0], hi_w[1]);
+            } else {
+              dst[0] = make_uint4(lo_w[0], lo_w[1], lo_w[2], lo_w[3]);
+              dst[1] = make_uint4(hi_w[0], hi_w[1], hi_w[2], hi_w[3]);
+            }
           }
         }
+      }
   } else {
     // sum of squares over this segment's rows n (columns of C)
     float sq[2][16];
@@ -228,6 +322,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 }
 
 }  // namespace
+
+hipError_t launch_scale_transpose(const void* in, const float* s, void* out, int rows, int cols,
+                                  int dtype, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid((cols + PT - 1) / PT, (rows + PT - 1) / PT);
+  if (dtype == 1) {
+    const auto* i = static_cast<const __bf16*>(in);
+    auto* o = static_cast<__bf16*>(out);
+    if (cols % 8 == 0) hipLaunchKernelGGL((scale_transpose_kernel<__bf16, true>), grid, dim3(256), 0, st, i, s, o, rows, cols);
+    else hipLaunchKernelGGL((scale_transpose_kernel<__bf16, false>), grid, dim3(256), 0, st, i, s, o, rows, cols);
+  } else {
+    const auto* i = static_cast<const float*>(in);
+    auto* o = static_cast<float*>(out);
+    if (cols % 4 == 0) hipLaunchKernelGGL((scale_transpose_kernel<float, true>), grid, dim3(256), 0, st, i, s, o, rows, cols);
+    else hipLaunchKernelGGL((scale_transpose_kernel<float, false>), grid, dim3(256), 0, st, i, s, o, rows, cols);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmParams& p, int dtype, int epilogue, dim3 grid, hipStream_t st) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;

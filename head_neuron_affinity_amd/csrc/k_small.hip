@@ -1,6 +1,4 @@
 // Small bandwidth-bound kernels around the two matrix-core passes:
-//   * transpose (W_o -> W_o^T and W_down -> W_down^T, so the GEMM reads both
-//     operands along the contracted dimension);
 //   * ||w^d_k||^2, the squared norms of W_down's columns (section 3,
 //     "Affinity scores": the FO score's write-size factor);
 //   * the down edge's group sum n[g', k] over the q/k/v row segments of each
@@ -9,26 +7,6 @@
 
 namespace hna {
 namespace {
-
-constexpr int TD = 64;
-
-// out[c][r] = in[r][c]; 64 x 64 tiles through LDS, 256 threads.
-template <typename E>
-__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in, E* __restrict__ out,
-                                                        int rows, int cols) {
-  __shared__ E tile[TD][TD + 1];
-  const int r0 = blockIdx.y * TD, c0 = blockIdx.x * TD;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < TD; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = in[(int64_t)r * cols + c];
-  }
-  __syncthreads();
-  for (int i = ty; i < TD; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) out[(int64_t)c * rows + r] = tile[tx][i];
-  }
-}
 
 // out[k] = sum_r W[r][k]^2 for a row-major [rows, cols] matrix.
 // Scalar form (any column count): 64 columns per block, 4 row lanes; the 4
@@ -131,19 +109,6 @@ __global__ __launch_bounds__(256) void down_combine_kernel(const float* __restri
 }
 
 }  // namespace
-
-hipError_t launch_transpose(const void* in, void* out, int rows, int cols, int esize,
-                            hipStream_t st) {
-  if (rows == 0 || cols == 0) return hipSuccess;
-  dim3 grid((cols + TD - 1) / TD, (rows + TD - 1) / TD);
-  if (esize == 2)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), rows, cols);
-  else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st,
-                       static_cast<const float*>(in), static_cast<float*>(out), rows, cols);
-  return hipGetLastError();
-}
 
 hipError_t launch_col_sqnorm(const void* W, int rows, int cols, int dtype, float* out,
                              hipStream_t st) {
