@@ -57,6 +57,36 @@ constexpr int pow2_slots(int cpr) { return cpr <= 8 ? 8 : (cpr <= 16 ? 16 : 32);
 constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Untracked 16-byte buffer load into four accumulation registers (MFMA
+// operands may come from them): dst = the 16 bytes at voff of resource rs.
+// The compiler does not count it; the caller waits for it with an explicit
+// vmcnt that names dst as an operand (so dst is neither read nor reused
+// before the data has landed).
+__device__ inline void bload16(u32x4& dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(dst) : "v"(voff), "s"(rs));
+}
+
+// s_waitcnt vmcnt(N) that also names the registers it guards as operands, so
+// the compiler cannot move their uses (or reuse them) ahead of the wait.
+template <int N>
+__device__ inline void vm_wait_tied(u32x4& x, u32x4& y) {
+  asm volatile("s_waitcnt vmcnt(%2)" : "+a"(x), "+a"(y) : "n"(N));
+}
+template <int N>
+__device__ inline void vm_wait_tied(u32x4& x, u32x4& y, u32x4& z, u32x4& w) {
+  asm volatile("s_waitcnt vmcnt(%4)" : "+a"(x), "+a"(y), "+a"(z), "+a"(w) : "n"(N));
+}
+
+// Calls f(IC<B>), f(IC<B+1>), ..., f(IC<E-1>) (a loop with a compile-time index).
+template <int B, int E, typename F>
+__device__ inline __attribute__((always_inline)) void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zeros (hardware range check), so tile edges need no clamping.
@@ -151,7 +181,7 @@ void affinity_up_kernel(const UpParams p) {
   // a tile of step `step`: slot q of the buffer holds row q / SLOTS, chunk
   // (q % SLOTS) ^ (row % SLOTS).  A wave copies 64 consecutive slots (64 /
   // SLOTS whole rows); rows past T and unused slots read zeros.
-  auto dma_a = [&](int step, const unsigned char* buf) __attribute__((always_inline)) {
+  auto dma_a = [&](int step, const unsigned char* buf, bool real) __attribute__((always_inline)) {
     const int ti = step / H;
     const int h = s_order[step - ti * H];
     const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
@@ -164,7 +194,8 @@ void affinity_up_kernel(const UpParams p) {
       const int slot0 = (i * kWaves + w) * 64;
       const int row = slot0 / SLOTS + l / SLOTS, sl = l % SLOTS;
       const int c = sl ^ (row & (SLOTS - 1));
-      const uint32_t voff = c < CPR ? (uint32_t)row * row_bytes + (uint32_t)(c * 16) : kOutOfRange;
+      const uint32_t voff =
+          c < CPR && real ? (uint32_t)row * row_bytes + (uint32_t)(c * 16) : kOutOfRange;
       dma16(rs, voff, buf + slot0 * 16);
     }
   };
@@ -216,15 +247,28 @@ void affinity_up_kernel(const UpParams p) {
   float c_acc = 0.f;
   const char* Mbytes = static_cast<const char*>(p.M);
   const uint32_t mlane = (uint32_t)l * 8u * EB;
-  uint4 mreg[S][2][Q];        // the head's folded-weight fragments, all d-steps
+  // The head's folded-weight fragments, all d-steps.  They are loaded with
+  // untracked loads (gload16) and waited for with exact counts (wait_m), so
+  // the a-tile copies issued between a refill and its use are not waited for.
+  u32x4 mreg[S][2][Q];
   auto load_m = [&](int s, int h) __attribute__((always_inline)) {
-    // wave-uniform base of (h, this wave's neuron block), per-lane 32-bit offset
-    const char* Mh = Mbytes + ((int64_t)h * KB + nbc) * 2 * S * kSlabBytes;
+    // the 2 S slabs of (h, this wave's neuron block); per-lane offsets
+    const int hu = __builtin_amdgcn_readfirstlane(h);
+    const auto rs = buffer_rsrc(Mbytes + ((int64_t)hu * KB + nbc) * 2 * S * kSlabBytes,
+                                2 * S * kSlabBytes);
 #pragma unroll
     for (int qq = 0; qq < Q; ++qq) {
-      mreg[s][0][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + s * kSlabBytes + qq * 16);
-      mreg[s][1][qq] = *reinterpret_cast<const uint4*>(Mh + mlane + (S + s) * kSlabBytes + qq * 16);
+      bload16(mreg[s][0][qq], rs, mlane + s * kSlabBytes + qq * 16);
+      bload16(mreg[s][1][qq], rs, mlane + (S + s) * kSlabBytes + qq * 16);
     }
+  };
+  // Wait until d-step s's fragments have landed, given that `newer` untracked
+  // loads were issued after them (the fragments pass through the wait, so no
+  // use can be scheduled before it).
+  auto wait_m = [&](int s, auto newer) __attribute__((always_inline)) {
+    constexpr int N = decltype(newer)::value;
+    if constexpr (Q == 1) vm_wait_tied<N>(mreg[s][0][0], mreg[s][1][0]);
+    else vm_wait_tied<N>(mreg[s][0][0], mreg[s][0][1], mreg[s][1][0], mreg[s][1][1]);
   };
 
   // operating-point coefficients of token tile ti (shared by all heads)
@@ -317,16 +361,22 @@ void affinity_up_kernel(const UpParams p) {
     const int ti = s / H, hi = s - ti * H;
     const bool has_next = s + 1 < nsteps;
     const int hn = has_next ? s_order[hi + 1 == H ? 0 : hi + 1] : s_order[hi];
-    // Everything this wave issued before this point has landed: the a tile of
-    // this step (copied one step earlier), this head's folded-weight
-    // fragments (refilled during the previous step's last chain) and, after a
-    // tile's first step, the next tile's g/u copies.  The copy of the next a
-    // tile is issued only after this wait, so it overlaps the whole step.
-    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    // Vector-memory loads complete in issue order.  The last NMS loads this
+    // wave issued are this head's folded-weight fragments (refilled during
+    // the previous step's last chain); everything before them has landed
+    // once at most NMS are outstanding: the a tile of this step (copied one
+    // step earlier) and the g/u, r and r_next copies of the next tile.  The
+    // compiler waits for each weight fragment itself just before its first
+    // MFMA, so the refills issued last keep most of a chain of lead time.
+    // The copy of the next a tile is issued after this wait and overlaps the
+    // whole step.
+    __builtin_amdgcn_s_waitcnt(vm_wait(NMS));
     __syncthreads();
     const bool odd = (s & 1) != 0;
     const unsigned char* ab = odd ? abuf1 : abuf0;
-    if (has_next) dma_a(s + 1, odd ? abuf0 : abuf1);
+    // (after the last step: a copy that reads nothing and fills the idle
+    // buffer with zeros, so every step issues the same number of loads)
+    dma_a(has_next ? s + 1 : s, odd ? abuf0 : abuf1, has_next);
 
     // Two token blocks' chains run together (four independent accumulators,
     // enough to keep the matrix pipeline full); the a fragments go through a
@@ -349,11 +399,12 @@ void affinity_up_kernel(const UpParams p) {
     };
     read_af(0, afr[0]);
     if (NQ > 1) read_af(1, afr[1]);
-    auto body = [&](int q) __attribute__((always_inline)) {
-      const int pr = q / S, ks = q % S;
+    auto body = [&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int pr = q / S, ks = q % S;
       // the chain pair before this one: pair 0 of this head, or the previous
       // head's pair 1 (token blocks 2 and 3)
-      const int ppr = pr == 0 ? 1 : 0;
+      constexpr int ppr = pr == 0 ? 1 : 0;
       if (q + 2 < NQ) read_af(q + 2, afr[(q + 2) % 3]);
       if (ks == 0) {
 #pragma unroll
@@ -362,23 +413,43 @@ void affinity_up_kernel(const UpParams p) {
           accU[2 * pr + j] = f32x16{};
         }
       }
-      // a slice of the previous pair's epilogue (other accumulators)
-      if (pr > 0 || s > 0) {
+      // a slice of the previous pair's epilogue (other accumulators; before the
+      // first head they and the coefficients are zero, adding nothing).  The
+      // slice's pairs go through each stage together, so no result is read
+      // by the very next instruction.
+      {
+        constexpr int x0 = ks * 32 / S, x1 = (ks + 1) * 32 / S, nx = x1 - x0;
+        float t[nx > 0 ? nx : 1];
 #pragma unroll
-        for (int x = ks * 32 / S; x < (ks + 1) * 32 / S; ++x) epi_pair(2 * ppr + (x >> 4), x & 15);
+        for (int x = x0; x < x1; ++x)
+          t[x - x0] = fmaf((float)cAB[2 * ppr + (x >> 4)][x & 15].y, accU[2 * ppr + (x >> 4)][x & 15], 0.0f);
+#pragma unroll
+        for (int x = x0; x < x1; ++x)
+          t[x - x0] = fmaf((float)cAB[2 * ppr + (x >> 4)][x & 15].x, accG[2 * ppr + (x >> 4)][x & 15], t[x - x0]);
+#pragma unroll
+        for (int x = x0; x < x1; ++x)
+          fo_run[2 * ppr + (x >> 4)] = fmaf(t[x - x0], t[x - x0], fo_run[2 * ppr + (x >> 4)]);
+      }
+      // first use of d-step ks's fragments: issued after them are the later
+      // d-steps' refills and this step's copy of the next a tile
+      if constexpr (pr == 0) wait_m(ks, IC<2 * Q * (S - 1 - ks) + DMA_A>{});
+      uint4 mg[Q], mu[Q];
+#pragma unroll
+      for (int qq = 0; qq < Q; ++qq) {
+        mg[qq] = __builtin_bit_cast(uint4, mreg[ks][0][qq]);
+        mu[qq] = __builtin_bit_cast(uint4, mreg[ks][1][qq]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        mma(accG[2 * pr + j], afr[q % 3][j], mreg[ks][0]);
-        mma(accU[2 * pr + j], afr[q % 3][j], mreg[ks][1]);
+        mma(accG[2 * pr + j], afr[q % 3][j], mg);
+        mma(accU[2 * pr + j], afr[q % 3][j], mu);
       }
       // after the last pair's use, refill with the next head's fragments
-      if (pr == 1) load_m(ks, hn);
+      if (pr == 1 && has_next) load_m(ks, hn);
       __builtin_amdgcn_sched_barrier(0);
     };
     // pair 0 (token blocks 0, 1), which also finishes the previous head
-#pragma unroll
-    for (int q = 0; q < S; ++q) body(q);
+    static_for<0, S>(body);
     if (s > 0) {
       // the previous head is complete: flush if it ends its KV group
       const int hp = hi == 0 ? H - 1 : hi - 1;
@@ -387,14 +458,22 @@ void affinity_up_kernel(const UpParams p) {
     }
     if (hi == 0) burst(ti);   // coefficients of this tile, used from pair 1 on
     // pair 1 (token blocks 2, 3)
-#pragma unroll
-    for (int q = S; q < NQ; ++q) body(q);
+    static_for<S, NQ>(body);
   };
 
   // ---- prologue and step loop ----------------------------------------------------
+  // The first step's pair 0 runs the epilogue of a "previous" pair that does
+  // not exist: zero accumulators and coefficients make it add nothing.
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) {
+    accG[tb] = f32x16{};
+    accU[tb] = f32x16{};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cAB[tb][v] = Coef{0, 0};
+  }
   dma_gu(0);
   dma_tok(0);
-  dma_a(0, abuf0);
+  dma_a(0, abuf0, true);
 #pragma unroll
   for (int ks = 0; ks < S; ++ks) load_m(ks, s_order[0]);
 
