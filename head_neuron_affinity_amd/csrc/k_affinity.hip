@@ -97,16 +97,19 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;   // offset past any resource: reads zeros
 
 // Asynchronous 16-byte buffer -> LDS copy: lane l copies the 16 bytes at
-// voff and writes them at dst + 16 l (voff is what the range check covers).
-// Issued as inline assembly on purpose: the compiler then does not track the
-// LDS write, so it adds no vmcnt wait before reads of the other buffer (the
-// kernel orders every copy itself with explicit vmcnt waits and barriers).
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                             const unsigned char* dst_wave_base) {
-  const uint32_t lds =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)dst_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
+// voff of resource rs (voff is what the range check covers) and writes them
+// at LDS address lds_base + OFF + 16 l (lds_base wave-uniform).  Issued as
+// inline assembly on purpose: the compiler then does not track the LDS write,
+// so it adds no vmcnt wait before reads of the other buffer (the kernel orders
+// every copy itself with explicit vmcnt waits and barriers).
+template <int OFF>
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               :: "s"(lds_base), "n"(OFF), "v"(voff), "s"(rs) : "memory", "scc");
+}
+// LDS address of a workgroup-shared object
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr)const_cast<void*>(p);
 }
 
 constexpr int kWaves = 4;              // one per SIMD
@@ -178,47 +181,69 @@ void affinity_up_kernel(const UpParams p) {
   const int nsteps = ntile * H;
 
   // ---- asynchronous copies ---------------------------------------------------
-  // a tile of step `step`: slot q of the buffer holds row q / SLOTS, chunk
-  // (q % SLOTS) ^ (row % SLOTS).  A wave copies 64 consecutive slots (64 /
-  // SLOTS whole rows); rows past T and unused slots read zeros.
-  auto dma_a = [&](int step, const unsigned char* buf, bool real) __attribute__((always_inline)) {
-    const int ti = step / H;
-    const int h = s_order[step - ti * H];
-    const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
-    const int rows = (int)min((int64_t)kTileTokens, NT - t0);
-    const uint32_t row_bytes = (uint32_t)(H * d * EB);
-    const auto rs = buffer_rsrc(static_cast<const char*>(p.a) + (t0 * H + h) * (int64_t)d * EB,
-                                (uint32_t)(rows - 1) * row_bytes + (uint32_t)(d * EB));
+  // Per-wave LDS destinations: instruction i of wave w fills 64 slots of 16
+  // bytes at byte offset (4 i + w) * 1024 of its buffer.
+  const uint32_t lw = (uint32_t)w * 1024u;
+  const uint32_t lds_a0 = lds_addr(abuf0) + lw, lds_a1 = lds_addr(abuf1) + lw;
+  const uint32_t lds_gu = lds_addr(gubuf) + lw;
+  const uint32_t lds_r = lds_addr(rraw);
+  // a tile of one (token tile, head): slot q of the buffer holds row q / SLOTS,
+  // chunk (q % SLOTS) ^ (row % SLOTS).  A wave copies 64 consecutive slots (64
+  // / SLOTS whole rows) per instruction.  The per-lane offsets are the same
+  // for every step; the resource selects the rows (rows past T, and every row
+  // of the copy after the last step, read zeros).
+  const uint32_t row_bytes_a = (uint32_t)(H * d * EB);
+  auto voff_of = [&](int i) __attribute__((always_inline)) {
+    const int slot0 = (i * kWaves + w) * 64;
+    const int row = slot0 / SLOTS + l / SLOTS, sl = l % SLOTS;
+    const int c = sl ^ (row & (SLOTS - 1));
+    return c < CPR ? (uint32_t)row * row_bytes_a + (uint32_t)(c * 16) : kOutOfRange;
+  };
+  // kept in registers when there are few of them (bf16), else recomputed
+  constexpr bool kKeepVoff = DMA_A <= 8;
+  uint32_t voff_a[kKeepVoff ? DMA_A : 1];
+  if constexpr (kKeepVoff) {
 #pragma unroll
-    for (int i = 0; i < DMA_A; ++i) {
-      const int slot0 = (i * kWaves + w) * 64;
-      const int row = slot0 / SLOTS + l / SLOTS, sl = l % SLOTS;
-      const int c = sl ^ (row & (SLOTS - 1));
-      const uint32_t voff =
-          c < CPR && real ? (uint32_t)row * row_bytes + (uint32_t)(c * 16) : kOutOfRange;
-      dma16(rs, voff, buf + slot0 * 16);
-    }
+    for (int i = 0; i < DMA_A; ++i) voff_a[i] = voff_of(i);
+  }
+  const char* const abytes = static_cast<const char*>(p.a);
+  // first byte and byte range of token tile ti's a rows (range 0 past the chunk)
+  auto a_tile = [&](int ti, const char*& base, uint32_t& nrec) __attribute__((always_inline)) {
+    const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
+    base = abytes + t0 * row_bytes_a;
+    nrec = ti < ntile ? (uint32_t)(min((int64_t)kTileTokens, NT - t0) - 1) * row_bytes_a + (uint32_t)(d * EB)
+                      : 0u;
+  };
+  auto dma_a = [&](__amdgpu_buffer_rsrc_t rs, uint32_t lds) __attribute__((always_inline)) {
+    static_for<0, DMA_A>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (kKeepVoff) dma16<i * kWaves * 1024>(rs, voff_a[i], lds);
+      else dma16<i * kWaves * 1024>(rs, voff_of(i), lds);
+    });
   };
   // g and u tiles of token tile ti (bf16, 128 tokens x 128 neurons each; a row
   // is 16 chunks of 8 neurons, chunk c of row r in slot c ^ (r & 4)).  A wave
-  // copies 4 whole rows per instruction; rows past T read zeros.
+  // copies 4 whole rows per instruction; rows past T read zeros.  Instruction
+  // i covers rows 16 (i % 8) + 4 w + l / 16 of g (i < 8) or of u.
+  const uint32_t row_bytes_gu = (uint32_t)I * 2u;
+  uint32_t voff_gu = 0;
+  if constexpr (GULDS) {
+    const int row = 4 * w + (l >> 4);
+    voff_gu = (uint32_t)row * row_bytes_gu + (uint32_t)(((l & 15) ^ (row & 4)) * 16);
+  }
   auto dma_gu = [&](int ti) __attribute__((always_inline)) {
     if constexpr (GULDS) {
       const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
       const int rows = (int)min((int64_t)kTileTokens, NT - t0);
       const int n0 = kt * kTileNeurons;
-      const uint32_t row_bytes = (uint32_t)I * 2u;
-      const uint32_t bytes = (uint32_t)rows * row_bytes - (uint32_t)n0 * 2u;
+      const uint32_t bytes = (uint32_t)rows * row_bytes_gu - (uint32_t)n0 * 2u;
       const auto rg = buffer_rsrc(gp + t0 * I + n0, bytes);
       const auto ru = buffer_rsrc(up + t0 * I + n0, bytes);
-#pragma unroll
-      for (int i = 0; i < DMA_GU; ++i) {
-        const int slot0 = (i * kWaves + w) * 64;
-        const int which = slot0 >= kTileTokens * 16;       // wave-uniform: g or u
-        const int row = ((slot0 - which * kTileTokens * 16) >> 4) + (l >> 4);
-        const int c = (l & 15) ^ (row & 4);
-        dma16(which ? ru : rg, (uint32_t)row * row_bytes + (uint32_t)(c * 16), gubuf + slot0 * 16);
-      }
+      static_for<0, DMA_GU>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        const uint32_t voff = voff_gu + (uint32_t)(16 * (i % 8)) * row_bytes_gu;
+        dma16<i * kWaves * 1024>(i < DMA_GU / 2 ? rg : ru, voff, lds_gu);
+      });
     }
   };
   // r and r_next of token tile ti (wave 0; 32 lanes x 16 bytes each, the
@@ -228,9 +253,8 @@ void affinity_up_kernel(const UpParams p) {
       const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
       const uint32_t bytes = (uint32_t)min((int64_t)kTileTokens, NT - t0) * 4u;
       const uint32_t voff = l < 32 ? (uint32_t)l * 16u : kOutOfRange;
-      dma16(buffer_rsrc(p.r + t0, bytes), voff, reinterpret_cast<unsigned char*>(rraw));
-      dma16(buffer_rsrc(p.r_next + t0, bytes), voff,
-            reinterpret_cast<unsigned char*>(rraw + 2 * kTileTokens));
+      dma16<0>(buffer_rsrc(p.r + t0, bytes), voff, lds_r);
+      dma16<2 * kTileTokens * 4>(buffer_rsrc(p.r_next + t0, bytes), voff, lds_r);
     }
   };
 
@@ -251,10 +275,12 @@ void affinity_up_kernel(const UpParams p) {
   // untracked loads (gload16) and waited for with exact counts (wait_m), so
   // the a-tile copies issued between a refill and its use are not waited for.
   u32x4 mreg[S][2][Q];
+  // this wave's neuron block of head 0, and the distance between heads
+  const char* const Mw = Mbytes + (int64_t)nbc * 2 * S * kSlabBytes;
+  const int64_t m_head = (int64_t)KB * 2 * S * kSlabBytes;
   auto load_m = [&](int s, int h) __attribute__((always_inline)) {
     // the 2 S slabs of (h, this wave's neuron block); per-lane offsets
-    const int hu = __builtin_amdgcn_readfirstlane(h);
-    const auto rs = buffer_rsrc(Mbytes + ((int64_t)hu * KB + nbc) * 2 * S * kSlabBytes,
+    const auto rs = buffer_rsrc(Mw + (int64_t)__builtin_amdgcn_readfirstlane(h) * m_head,
                                 2 * S * kSlabBytes);
 #pragma unroll
     for (int qq = 0; qq < Q; ++qq) {
@@ -283,7 +309,11 @@ void affinity_up_kernel(const UpParams p) {
       tokinv[tid] = ok ? __builtin_amdgcn_rcpf(rv) : 0.f;
     }
     __syncthreads();
-    const int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
+    int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
+    // opaque to the optimizer: the direct g/u addresses below are formed here,
+    // once per tile, rather than hoisted out of the head loop (which would
+    // keep all 64 of them live through every step)
+    asm volatile("" : "+s"(tbase));
     const int last = (int)min((int64_t)kTileTokens, NT - tbase) - 1;
     // Every row this lane reads has (row & 4) == 4 (l >> 5), so the swizzled
     // g/u address is a per-lane base plus a compile-time row offset (nothing
@@ -357,10 +387,13 @@ void affinity_up_kernel(const UpParams p) {
   };
 
   // ---- one (token tile, head) step ------------------------------------------------
-  auto step = [&](int s) __attribute__((always_inline)) {
-    const int ti = s / H, hi = s - ti * H;
+  // s = ti * H + hi; a_cur / r_cur and a_nxt / r_nxt: the a rows of token
+  // tiles ti and ti + 1 (see a_tile)
+  auto step = [&](int s, int ti, int hi, const char* a_cur, uint32_t r_cur, const char* a_nxt,
+                  uint32_t r_nxt) __attribute__((always_inline)) {
+    const bool last_h = hi + 1 == H;
     const bool has_next = s + 1 < nsteps;
-    const int hn = has_next ? s_order[hi + 1 == H ? 0 : hi + 1] : s_order[hi];
+    const int hn = __builtin_amdgcn_readfirstlane(s_order[last_h ? 0 : hi + 1]);   // next head
     // Vector-memory loads complete in issue order.  The last NMS loads this
     // wave issued are this head's folded-weight fragments (refilled during
     // the previous step's last chain); everything before them has landed
@@ -374,9 +407,11 @@ void affinity_up_kernel(const UpParams p) {
     __syncthreads();
     const bool odd = (s & 1) != 0;
     const unsigned char* ab = odd ? abuf1 : abuf0;
-    // (after the last step: a copy that reads nothing and fills the idle
-    // buffer with zeros, so every step issues the same number of loads)
-    dma_a(has_next ? s + 1 : s, odd ? abuf0 : abuf1, has_next);
+    // the next step's a tile (after the last step the range is empty: the
+    // copy reads nothing and fills the idle buffer with zeros, so every step
+    // issues the same number of loads)
+    dma_a(buffer_rsrc((last_h ? a_nxt : a_cur) + (int64_t)hn * d * EB, last_h ? r_nxt : r_cur),
+          odd ? lds_a0 : lds_a1);
 
     // Two token blocks' chains run together (four independent accumulators,
     // enough to keep the matrix pipeline full); the a fragments go through a
@@ -471,13 +506,24 @@ void affinity_up_kernel(const UpParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) cAB[tb][v] = Coef{0, 0};
   }
+  const char* a_cur;
+  uint32_t r_cur;
+  a_tile(0, a_cur, r_cur);
+  const int h0 = __builtin_amdgcn_readfirstlane(s_order[0]);
   dma_gu(0);
   dma_tok(0);
-  dma_a(0, abuf0, true);
+  dma_a(buffer_rsrc(a_cur + (int64_t)h0 * d * EB, r_cur), lds_a0);
 #pragma unroll
-  for (int ks = 0; ks < S; ++ks) load_m(ks, s_order[0]);
+  for (int ks = 0; ks < S; ++ks) load_m(ks, h0);
 
-  for (int s = 0; s < nsteps; ++s) step(s);
+  for (int ti = 0, s = 0; ti < ntile; ++ti) {
+    const char* a_nxt;
+    uint32_t r_nxt;
+    a_tile(ti + 1, a_nxt, r_nxt);
+    for (int hi = 0; hi < H; ++hi, ++s) step(s, ti, hi, a_cur, r_cur, a_nxt, r_nxt);
+    a_cur = a_nxt;
+    r_cur = r_nxt;
+  }
 
   // epilogue of the last pair (its head ends the last KV group)
 #pragma unroll
