@@ -19,6 +19,11 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
+# Per-source additions.  The affinity kernel's epilogue reads the MFMA results
+# with ordinary vector instructions; the VGPR form of MFMA keeps accumulators
+# in VGPRs, so no accumulation-register reads are needed (its weight
+# fragments still go to accumulation registers, as MFMA operands).
+EXTRA = {"k_affinity.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -38,7 +43,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
         for msg in ex.map(_run, jobs):
             if verbose and msg.strip():
