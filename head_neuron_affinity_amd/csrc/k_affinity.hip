@@ -214,6 +214,13 @@ void affinity_up_kernel(const UpParams p) {
     nrec = ti < ntile ? (uint32_t)(min((int64_t)kTileTokens, NT - t0) - 1) * row_bytes_a + (uint32_t)(d * EB)
                       : 0u;
   };
+  auto dma_a_part = [&](__amdgpu_buffer_rsrc_t rs, uint32_t lds, auto lo, auto hi) __attribute__((always_inline)) {
+    static_for<decltype(lo)::value, decltype(hi)::value>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (kKeepVoff) dma16<i * kWaves * 1024>(rs, voff_a[i], lds);
+      else dma16<i * kWaves * 1024>(rs, voff_of(i), lds);
+    });
+  };
   auto dma_a = [&](__amdgpu_buffer_rsrc_t rs, uint32_t lds) __attribute__((always_inline)) {
     static_for<0, DMA_A>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
@@ -410,8 +417,9 @@ void affinity_up_kernel(const UpParams p) {
     // the next step's a tile (after the last step the range is empty: the
     // copy reads nothing and fills the idle buffer with zeros, so every step
     // issues the same number of loads)
-    dma_a(buffer_rsrc((last_h ? a_nxt : a_cur) + (int64_t)hn * d * EB, last_h ? r_nxt : r_cur),
-          odd ? lds_a0 : lds_a1);
+    const auto rs_next =
+        buffer_rsrc((last_h ? a_nxt : a_cur) + (int64_t)hn * d * EB, last_h ? r_nxt : r_cur);
+    const uint32_t lds_next = odd ? lds_a0 : lds_a1;
 
     // Two token blocks' chains run together (four independent accumulators,
     // enough to keep the matrix pipeline full); the a fragments go through a
@@ -467,7 +475,10 @@ void affinity_up_kernel(const UpParams p) {
       }
       // first use of d-step ks's fragments: issued after them are the later
       // d-steps' refills and this step's copy of the next a tile
-      if constexpr (pr == 0) wait_m(ks, IC<2 * Q * (S - 1 - ks) + DMA_A>{});
+      // the copies of the next a tile are spread over pair 0, after each
+      // d-step's MFMAs (DMA_A / S per d-step, the rest with the last one)
+      constexpr int dma_lo = ks * (DMA_A / S), dma_hi = ks + 1 == S ? DMA_A : (ks + 1) * (DMA_A / S);
+      if constexpr (pr == 0) wait_m(ks, IC<2 * Q * (S - 1 - ks) + dma_lo>{});
       uint4 mg[Q], mu[Q];
 #pragma unroll
       for (int qq = 0; qq < Q; ++qq) {
@@ -479,6 +490,7 @@ void affinity_up_kernel(const UpParams p) {
         mma(accG[2 * pr + j], afr[q % 3][j], mg);
         mma(accU[2 * pr + j], afr[q % 3][j], mu);
       }
+      if constexpr (pr == 0) dma_a_part(rs_next, lds_next, IC<dma_lo>{}, IC<dma_hi>{});
       // after the last pair's use, refill with the next head's fragments
       if (pr == 1 && has_next) load_m(ks, hn);
       __builtin_amdgcn_sched_barrier(0);
