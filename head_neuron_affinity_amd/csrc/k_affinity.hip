@@ -67,6 +67,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline void bload16(u32x4& dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(dst) : "v"(voff), "s"(rs));
 }
+// The same at voff + OFF, OFF a compile-time byte offset: the multiple of 4096
+// goes in the scalar offset, the rest in the instruction's offset field.  (The
+// range check covers voff only: for reads that are in range by construction.)
+template <int OFF>
+__device__ inline void bload16_at(u32x4& dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+  constexpr uint32_t hi = OFF & ~4095u, lo = OFF & 4095u;
+  if constexpr (hi == 0)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3"
+                 : "=a"(dst) : "v"(voff), "s"(rs), "n"(lo));
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4"
+                 : "=a"(dst) : "v"(voff), "s"(rs), "s"(hi), "n"(lo));
+}
 
 // s_waitcnt vmcnt(N) that also names the registers it guards as operands, so
 // the compiler cannot move their uses (or reuse them) ahead of the wait.
@@ -78,6 +91,11 @@ template <int N>
 __device__ inline void vm_wait_tied(u32x4& x, u32x4& y, u32x4& z, u32x4& w) {
   asm volatile("s_waitcnt vmcnt(%4)" : "+a"(x), "+a"(y), "+a"(z), "+a"(w) : "n"(N));
 }
+
+// Empty statement that names x as read and written: uses of x placed after it
+// cannot move above an earlier volatile statement (such as a wait), and x is
+// not reused before it.
+__device__ inline void tie(u32x4& x) { asm volatile("" : "+a"(x)); }
 
 // Calls f(IC<B>), f(IC<B+1>), ..., f(IC<E-1>) (a loop with a compile-time index).
 template <int B, int E, typename F>
@@ -285,15 +303,17 @@ void affinity_up_kernel(const UpParams p) {
   // this wave's neuron block of head 0, and the distance between heads
   const char* const Mw = Mbytes + (int64_t)nbc * 2 * S * kSlabBytes;
   const int64_t m_head = (int64_t)KB * 2 * S * kSlabBytes;
-  auto load_m = [&](int s, int h) __attribute__((always_inline)) {
-    // the 2 S slabs of (h, this wave's neuron block); per-lane offsets
-    const auto rs = buffer_rsrc(Mw + (int64_t)__builtin_amdgcn_readfirstlane(h) * m_head,
-                                2 * S * kSlabBytes);
-#pragma unroll
-    for (int qq = 0; qq < Q; ++qq) {
-      bload16(mreg[s][0][qq], rs, mlane + s * kSlabBytes + qq * 16);
-      bload16(mreg[s][1][qq], rs, mlane + (S + s) * kSlabBytes + qq * 16);
-    }
+  // resource over the 2 S slabs of (head h, this wave's neuron block)
+  auto m_rsrc = [&](int h) __attribute__((always_inline)) {
+    return buffer_rsrc(Mw + (int64_t)h * m_head, 2 * S * kSlabBytes);
+  };
+  auto load_m = [&](auto sc, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value;
+    static_for<0, Q>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int qq = decltype(qc)::value;
+      bload16_at<s * kSlabBytes + qq * 16>(mreg[s][0][qq], rs, mlane);
+      bload16_at<(S + s) * kSlabBytes + qq * 16>(mreg[s][1][qq], rs, mlane);
+    });
   };
   // Wait until d-step s's fragments have landed, given that `newer` untracked
   // loads were issued after them (the fragments pass through the wait, so no
@@ -399,7 +419,6 @@ void affinity_up_kernel(const UpParams p) {
   auto step = [&](int s, int ti, int hi, const char* a_cur, uint32_t r_cur, const char* a_nxt,
                   uint32_t r_nxt) __attribute__((always_inline)) {
     const bool last_h = hi + 1 == H;
-    const bool has_next = s + 1 < nsteps;
     const int hn = __builtin_amdgcn_readfirstlane(s_order[last_h ? 0 : hi + 1]);   // next head
     // Vector-memory loads complete in issue order.  The last NMS loads this
     // wave issued are this head's folded-weight fragments (refilled during
@@ -420,6 +439,7 @@ void affinity_up_kernel(const UpParams p) {
     const auto rs_next =
         buffer_rsrc((last_h ? a_nxt : a_cur) + (int64_t)hn * d * EB, last_h ? r_nxt : r_cur);
     const uint32_t lds_next = odd ? lds_a0 : lds_a1;
+    const auto rs_m = m_rsrc(hn);   // the next head's weights (refilled during pair 1)
 
     // Two token blocks' chains run together (four independent accumulators,
     // enough to keep the matrix pipeline full); the a fragments go through a
@@ -492,7 +512,9 @@ void affinity_up_kernel(const UpParams p) {
       }
       if constexpr (pr == 0) dma_a_part(rs_next, lds_next, IC<dma_lo>{}, IC<dma_hi>{});
       // after the last pair's use, refill with the next head's fragments
-      if (pr == 1 && has_next) load_m(ks, hn);
+      // (after the last step too, into registers that are drained after the
+      // loop: every step issues the same loads)
+      if constexpr (pr == 1) load_m(IC<ks>{}, rs_m);
       __builtin_amdgcn_sched_barrier(0);
     };
     // pair 0 (token blocks 0, 1), which also finishes the previous head
@@ -525,8 +547,10 @@ void affinity_up_kernel(const UpParams p) {
   dma_gu(0);
   dma_tok(0);
   dma_a(buffer_rsrc(a_cur + (int64_t)h0 * d * EB, r_cur), lds_a0);
-#pragma unroll
-  for (int ks = 0; ks < S; ++ks) load_m(ks, h0);
+  {
+    const auto rs0 = m_rsrc(h0);
+    static_for<0, S>([&](auto kc) __attribute__((always_inline)) { load_m(kc, rs0); });
+  }
 
   for (int ti = 0, s = 0; ti < ntile; ++ti) {
     const char* a_nxt;
@@ -537,6 +561,16 @@ void affinity_up_kernel(const UpParams p) {
     r_cur = r_nxt;
   }
 
+  // the refills issued by the last step land before their registers can be
+  // reused (they pass through the wait)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int ks = 0; ks < S; ++ks)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int qq = 0; qq < Q; ++qq) tie(mreg[ks][g][qq]);
+
   // epilogue of the last pair (its head ends the last KV group)
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -544,7 +578,6 @@ void affinity_up_kernel(const UpParams p) {
     epi_pair(kTB - 1, v);
   }
   flush(s_group[H - 1]);
-  __builtin_amdgcn_s_waitcnt(vm_wait(0));   // drain the last (unused) weight refills
 
   // ---- write this workgroup's partial sums ----------------------------------------
   c_acc += __shfl_xor(c_acc, 32);
