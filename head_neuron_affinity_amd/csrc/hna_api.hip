@@ -102,12 +102,8 @@ int check_map(const char* fn, const int32_t* map, int H, int G) {
   return HNA_OK;
 }
 
-// The GEMMs' left operand is written once, scaled and transposed; bf16 keeps it
-// as a high part plus a remainder (two planes).
-size_t xs_planes(int dtype) { return dtype == HNA_BF16 ? 2 : 1; }
-
 size_t fold_ws_bytes(const hna_dims* dm) {
-  return align256((size_t)dm->H * dm->d * dm->hidden * esize_of(dm->dtype) * xs_planes(dm->dtype));
+  return align256((size_t)dm->H * dm->d * dm->hidden * esize_of(dm->dtype));
 }
 
 size_t up_ws_bytes(const hna_dims* dm) {
@@ -115,7 +111,7 @@ size_t up_ws_bytes(const hna_dims* dm) {
 }
 
 size_t down_ws_transposed(const hna_down_dims* dm) {
-  return align256((size_t)dm->I * dm->hidden * esize_of(dm->dtype) * xs_planes(dm->dtype));
+  return align256((size_t)dm->I * dm->hidden * esize_of(dm->dtype));
 }
 size_t down_ws_bytes(const hna_down_dims* dm) {
   return down_ws_transposed(dm) + align256((size_t)(dm->H + 2 * dm->G) * dm->I * sizeof(float));

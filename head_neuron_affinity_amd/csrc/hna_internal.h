@@ -133,15 +133,14 @@ hipError_t launch_down_combine(const float* c, const float* n, int I, int G_next
                                float* S_down, hipStream_t st);
 
 // ------------------------------------------------------ scaled NT GEMM (MFMA)
-// C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] (for bf16: a high plane and
-// a remainder plane, Mrows*K elements apart) and Y [N, K] row-major with c
-// contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a
+// C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] and Y [N, K] row-major with
+// c contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a
 // row-major X [K, Mrows].  Epilogues: write the folded layout, or sum C^2 over
 // the n of a segment.
 enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1 };
 
 struct GemmParams {
-  const void* X;       // Xs [Mrows, K] (bf16: two planes)
+  const void* X;       // Xs [Mrows, K]
   const void* Y[3];    // fold: Y[0] = W_gate, Y[1] = W_up; segsq: W_q, W_k, W_v
   int64_t ldx, ldy;
   int Mrows, N, K;     // fold: N = I32 (rows of Y beyond Nvalid are zero)

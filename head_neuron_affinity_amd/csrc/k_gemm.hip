@@ -7,12 +7,13 @@
 //   * down edge: X = W_down (columns k), Y = one d'-row segment of W_q, W_k or
 //     W_v, s = gamma'; the epilogue squares C and sums over the segment's
 //     rows, so b_gk itself is never stored.
-// A prep kernel writes Xs[m, c] = s[c] X[c, m] once, transposed; for bf16 it
-// writes Xs as a bf16 high part and a bf16 remainder, both multiplied against
-// the exact bf16 Y (2 MFMAs), so the product is accurate to fp32 accumulation
-// and the GEMM's main loop does no arithmetic besides the MFMAs.  fp32 inputs
-// use fp32 MFMA.  Tile 128 x 128 x 32, 4 waves (2 x 2, 64 x 64 each), LDS
-// double buffer with XOR-swizzled 16-byte chunks.
+// A prep kernel writes Xs[m, c] = s[c] X[c, m] once, transposed, so the GEMM's
+// main loop does loads, LDS stores and MFMAs only.  For bf16 inputs Xs is
+// rounded to bf16 once (relative error <= 2^-9 per element, the same size as
+// the bf16 rounding of the folded weights the fold stores; the sums run in
+// fp32), so each product is one MFMA; fp32 inputs use fp32 MFMA.  Tile
+// 128 x 128 x 32, 4 waves (2 x 2, 64 x 64 each), LDS double buffer with
+// XOR-swizzled 16-byte chunks.  The fragment reads from LDS bound the loop.
 #include "hna_internal.h"
 
 namespace hna {
@@ -22,10 +23,10 @@ constexpr int BM = 128, BN = 128, BK = 32;
 
 template <typename T> struct GT;
 template <> struct GT<__bf16> {
-  static constexpr int kBytes = 2, kCR = 4, kCPS = 2, kQ = 1, kSplit = 2;
+  static constexpr int kBytes = 2, kCR = 4, kCPS = 2, kQ = 1;
 };
 template <> struct GT<float> {
-  static constexpr int kBytes = 4, kCR = 8, kCPS = 4, kQ = 2, kSplit = 1;
+  static constexpr int kBytes = 4, kCR = 8, kCPS = 4, kQ = 2;
 };
 
 __device__ inline void mma(f32x16& c, const uint4 (&a)[1], const uint4 (&b)[1]) {
@@ -52,8 +53,8 @@ __device__ inline int swz(int row, int col) {
   return row * CR + (col ^ (((row / (8 / CR)) ^ (row >> 3)) % CR));
 }
 
-// Xs[c, r] = s[r] * in[r, c] for in [rows, cols] row-major; bf16 output goes
-// to two planes (high part at out, remainder at out + cols*rows).  64 x 64
+// Xs[c, r] = s[r] * in[r, c] for in [rows, cols] row-major (bf16 output
+// rounded to nearest even).  64 x 64
 // tiles through LDS; VEC reads the input rows in 16-byte pieces (needs
 // cols % (16 / sizeof(E)) == 0).  rows is a multiple of 8.
 constexpr int PT = 64;
@@ -109,7 +110,6 @@ __global__ __launch_bounds__(256) void scale_transpose_kernel(const E* __restric
     }
   }
   __syncthreads();
-  const int64_t plane = (int64_t)rows * cols;
 #pragma unroll
   for (int it = 0; it < PT * PT / EPC / 256; ++it) {
     const int q = tid + 256 * it;
@@ -121,17 +121,11 @@ __global__ __launch_bounds__(256) void scale_transpose_kernel(const E* __restric
     for (int e = 0; e < EPC; ++e) f[e] = tile[kq * EPC + e][cl];
     E* o = out + (int64_t)c * rows + r;
     if constexpr (kBf) {
-      uint32_t hi[4], lo[4];
+      uint32_t v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t h0 = f32_to_bf16_bits(f[2 * e]), h1 = f32_to_bf16_bits(f[2 * e + 1]);
-        const uint32_t l0 = f32_to_bf16_bits(f[2 * e] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_bits(f[2 * e + 1] - bf16_bits_to_f32(h1));
-        hi[e] = h0 | (h1 << 16);
-        lo[e] = l0 | (l1 << 16);
-      }
-      *reinterpret_cast<uint4*>(o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(o + plane) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      for (int e = 0; e < 4; ++e)
+        v[e] = f32_to_bf16_bits(f[2 * e]) | (f32_to_bf16_bits(f[2 * e + 1]) << 16);
+      *reinterpret_cast<uint4*>(o) = make_uint4(v[0], v[1], v[2], v[3]);
     } else {
       *reinterpret_cast<float4*>(o) = make_float4(f[0], f[1], f[2], f[3]);
     }
@@ -144,11 +138,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   constexpr int CR = Tr::kCR;            // 16-byte chunks per BK row
   constexpr int CPT = BM * CR / 256;     // chunks per thread per operand tile
   constexpr int EPC = 16 / Tr::kBytes;   // elements per chunk
-  constexpr int NSPLIT = Tr::kSplit;
   constexpr int Q = Tr::kQ;
   constexpr int TILE_CHUNKS = BM * CR;
 
-  __shared__ uint4 xs[2][NSPLIT][TILE_CHUNKS];
+  __shared__ uint4 xs[2][TILE_CHUNKS];
   __shared__ uint4 ys[2][TILE_CHUNKS];
   __shared__ float red[2][BM];
 
@@ -175,10 +168,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     Nrows = p.d_next;
   }
   const T* X = static_cast<const T*>(p.X);
-  const int64_t xplane = (int64_t)p.Mrows * p.ldx;
   const int K = p.K;
 
-  uint4 xr[CPT][NSPLIT], yr[CPT];
+  uint4 xr[CPT], yr[CPT];
   auto load = [&](int k0) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -186,10 +178,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
       const int row = q / CR, col = q % CR;
       const int kc = k0 + col * EPC;
       const bool okx = m0 + row < p.Mrows && kc < K;
-#pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp)
-        xr[c][sp] = okx ? *reinterpret_cast<const uint4*>(X + sp * xplane + (int64_t)(m0 + row) * p.ldx + kc)
-                        : make_uint4(0, 0, 0, 0);
+      xr[c] = okx ? *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + row) * p.ldx + kc)
+                  : make_uint4(0, 0, 0, 0);
       const bool oky = n0 + row < Nrows && kc < K;
       yr[c] = oky ? *reinterpret_cast<const uint4*>(Y + (int64_t)(n0 + row) * p.ldy + kc)
                   : make_uint4(0, 0, 0, 0);
@@ -200,8 +190,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     for (int c = 0; c < CPT; ++c) {
       const int q = tid + 256 * c;
       const int o = swz<CR>(q / CR, q % CR);
-#pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp) xs[buf][sp][o] = xr[c][sp];
+      xs[buf][o] = xr[c];
       ys[buf][o] = yr[c];
     }
   };
@@ -221,7 +210,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     if (kt + 1 < nk) load((kt + 1) * BK);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      uint4 af[2][NSPLIT][Q], bf[2][Q];
+      uint4 af[2][Q], bf[2][Q];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int ra = wm * 64 + i * 32 + (l & 31);
@@ -229,17 +218,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int qq = 0; qq < Q; ++qq) {
           const int col = s * Tr::kCPS + (l >> 5) * Q + qq;
-#pragma unroll
-          for (int sp = 0; sp < NSPLIT; ++sp) af[i][sp][qq] = xs[buf][sp][swz<CR>(ra, col)];
+          af[i][qq] = xs[buf][swz<CR>(ra, col)];
           bf[i][qq] = ys[buf][swz<CR>(rb, col)];
         }
       }
 #pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) mma(acc[i][j], af[i][sp], bf[j]);
+        for (int j = 0; j < 2; ++j) mma(acc[i][j], af[i], bf[j]);
     }
     if (kt + 1 < nk) store(buf ^ 1);
     __syncthreads();

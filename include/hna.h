@@ -98,9 +98,8 @@ const char* hna_last_error(void);
 
 /* Bytes of the folded weight M for `dims` (see hna_fold_up_weights). */
 size_t hna_folded_bytes(const hna_dims* dims);
-/* Bytes of workspace hna_fold_up_weights needs: gamma * W_o transposed,
- * held as a bf16 high part plus remainder for HNA_BF16 (two copies), once
- * for HNA_F32. */
+/* Bytes of workspace hna_fold_up_weights needs: gamma * W_o transposed, in
+ * the input dtype. */
 size_t hna_fold_workspace_bytes(const hna_dims* dims);
 
 /*

@@ -140,13 +140,13 @@ def test_workspace_sizes_follow_geometry():
     assert hna.up_workspace_bytes(dm) == (a256(1 * 3 * 128 * 4) + a256(4 * 16 * 16 * 4)
                                           + a256(4 * 16 * 16 * 4) + a256(2 * 128 * 4))
     assert hna.folded_bytes(dm) == 4 * 16 * 2 * 128 * 4
-    # gamma'-scaled W_down^T as bf16 high part + remainder, then the segment
-    # partials [H' + 2G'][I]
+    # gamma'-scaled W_down^T in the input dtype, then the segment partials
+    # [H' + 2G'][I]
     dd = hna.hna_down_dims(1024, 3072, 16, 8, 128, 1)
-    assert hna.down_workspace_bytes(dd) == 2 * 3072 * 1024 * 2 + 32 * 3072 * 4
-    # fold: gamma-scaled W_o^T, two bf16 planes, or one fp32 copy
+    assert hna.down_workspace_bytes(dd) == 3072 * 1024 * 2 + 32 * 3072 * 4
+    # fold: gamma-scaled W_o^T in the input dtype
     dm = hna.make_dims(65536, 1024, 16, 8, 128, 3072, 1)
-    assert hna.lib().hna_fold_workspace_bytes(ctypes.byref(dm)) == 2 * 2048 * 1024 * 2
+    assert hna.lib().hna_fold_workspace_bytes(ctypes.byref(dm)) == 2048 * 1024 * 2
     dm = hna.make_dims(1, 64, 4, 2, 16, 101, 0)
     assert hna.lib().hna_fold_workspace_bytes(ctypes.byref(dm)) == a256(64 * 64 * 4)
 
