@@ -38,6 +38,14 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two floats to packed bf16 (low half = a), round to nearest even, one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // MFMA helpers shared by the kernels that consume folded-layout fragments.
 // bf16: one 32x32x16 MFMA per 16-wide step of the contraction.
 __device__ inline void mma(f32x16& c, const uint4 (&a)[1], const uint4 (&b)[1]) {

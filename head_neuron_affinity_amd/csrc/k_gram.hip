@@ -117,20 +117,28 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
       for (int e = 0; e < 8; ++e) {
         const int base = (8 * fo + e) * TP + 4 * tq;
         if constexpr (sizeof(E) == 2) {
-          uint16_t xv[4], hv[4], lv[4];
+          // feature e of tokens 0..3: the raw bf16 halves, repacked (exact)
+          const uint32_t w0 = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+          uint32_t r[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float y = x[j][e] * wt[j];
-            xv[j] = bf16_rn(x[j][e]);   // exact: x is a bf16 value
-            hv[j] = bf16_rn(y);
-            lv[j] = bf16_rn(y - bf16_bits_to_f32(hv[j]));
+            const uint32_t wv[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
+            r[j] = wv[e >> 1];
           }
-          *reinterpret_cast<uint2*>(&xs[0][base]) =
-              make_uint2(xv[0] | ((uint32_t)xv[1] << 16), xv[2] | ((uint32_t)xv[3] << 16));
-          *reinterpret_cast<uint2*>(&xs[1][base]) =
-              make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+          const uint32_t x01 = __builtin_amdgcn_perm(r[1], r[0], w0);
+          const uint32_t x23 = __builtin_amdgcn_perm(r[3], r[2], w0);
+          float y[4], yl[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = x[j][e] * wt[j];
+          const uint32_t h01 = pack_bf16x2(y[0], y[1]), h23 = pack_bf16x2(y[2], y[3]);
+          yl[0] = y[0] - bf16_bits_to_f32(h01 & 0xffffu);
+          yl[1] = y[1] - __uint_as_float(h01 & 0xffff0000u);
+          yl[2] = y[2] - bf16_bits_to_f32(h23 & 0xffffu);
+          yl[3] = y[3] - __uint_as_float(h23 & 0xffff0000u);
+          *reinterpret_cast<uint2*>(&xs[0][base]) = make_uint2(x01, x23);
+          *reinterpret_cast<uint2*>(&xs[1][base]) = make_uint2(h01, h23);
           *reinterpret_cast<uint2*>(&xs[2][base]) =
-              make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+              make_uint2(pack_bf16x2(yl[0], yl[1]), pack_bf16x2(yl[2], yl[3]));
         } else {
           *reinterpret_cast<float4*>(&xs[0][base]) = make_float4(x[0][e], x[1][e], x[2][e], x[3][e]);
           *reinterpret_cast<float4*>(&xs[1][base]) = make_float4(
