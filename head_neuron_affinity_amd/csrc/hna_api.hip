@@ -306,13 +306,14 @@ int hna_affinity_add(const hna_dims* dm, const void* a, const float* r, const vo
   gp.chunk_tokens = geo.gram_chunk;
   hipError_t e = launch_gram(gp, dm->dtype, st);
   if (e != hipSuccess) return hip_fail(e, fn);
-  float* C = reinterpret_cast<float*>(ws + geo.off_gram);
-  e = launch_gram_reduce(gp.part, geo.n_gc, (int64_t)dm->H * dm->d * dm->d, C, st);
+  void* C = ws + geo.off_gram;   // H d d fp32, or two bf16 planes of H d d
+  e = launch_gram_reduce(gp.part, geo.n_gc, (int64_t)dm->H * dm->d * dm->d, C, dm->dtype, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   // ADD[g][k] = sum_{h in g} (m^g_hk . C_h m^g_hk + m^u_hk . C_h m^u_hk)
   qp.C = C;
   qp.M = M;
   qp.add = reinterpret_cast<float*>(ws + geo.off_add);
+  qp.add_part = reinterpret_cast<float*>(ws + geo.off_add_part);
   qp.H = dm->H;
   qp.G = dm->G;
   qp.d = dm->d;

@@ -101,11 +101,13 @@ struct GramParams {
   int64_t chunk_tokens;   // multiple of kGramStage
 };
 
-// add[g][k] = sum_{h in g} sum_{gate, up} m_hk^T C_h m_hk, m_hk = column k of M_h.
+// add[g][k] = sum_{h in g} sum_{gate, up} m_hk^T C_h m_hk, m_hk = column k of M_h
+// (per head into add_part, then summed over each group's heads in order).
 struct QuadParams {
-  const float* C;         // [H][d][d]
+  const void* C;          // [H][d][d]: bf16 high plane then remainder plane, or fp32
   const void* M;          // folded weights
   float* add;             // [G][KB * 32]
+  float* add_part;        // [H][KB * 32]: per-head sums before the group sum
   int H, G, d, KB;
   int8_t head_order[kMaxHeads];       // heads sorted by KV group
   int16_t group_start[kMaxHeads + 1]; // group g owns head_order[group_start[g] .. group_start[g+1])
@@ -116,10 +118,10 @@ struct UpGeometry {
   int n_gc;               // token chunks of the Gram kernel
   int64_t gram_chunk;     // tokens per Gram chunk
   bool gu_lds;            // g/u staged in LDS (bf16 with I % 8 == 0)
-  size_t part_bytes, gram_part_bytes, gram_bytes, add_bytes, ws_bytes;
+  size_t part_bytes, gram_part_bytes, gram_bytes, add_bytes, add_part_bytes, ws_bytes;
   size_t lds_bytes, dyn_lds_bytes;
   // byte offsets of the regions inside the workspace
-  size_t off_gram_part, off_gram, off_add;
+  size_t off_gram_part, off_gram, off_add, off_add_part;
 };
 UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype);
 
@@ -128,7 +130,8 @@ hipError_t launch_finalize_up(const float* part, const float* add, int n_chunks,
                               int I32, const float* wd_sq, float scale, int accumulate,
                               float* S_fo, float* S_add, float* c_down, hipStream_t st);
 hipError_t launch_gram(const GramParams& p, int dtype, hipStream_t st);
-hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, float* C, hipStream_t st);
+hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, void* C, int dtype,
+                              hipStream_t st);
 hipError_t launch_quad(const QuadParams& p, int dtype, hipStream_t st);
 
 // --------------------------------------------------------------- small kernels

@@ -687,8 +687,10 @@ UpGeometry up_geometry(int64_t T, int H, int G, int d, int I, int dtype) {
   g.add_bytes = a256((size_t)G * g.I32 * sizeof(float));
   g.off_gram_part = g.part_bytes;
   g.off_gram = g.off_gram_part + g.gram_part_bytes;
+  g.add_part_bytes = a256((size_t)H * g.I32 * sizeof(float));
   g.off_add = g.off_gram + g.gram_bytes;
-  g.ws_bytes = g.off_add + g.add_bytes;
+  g.off_add_part = g.off_add + g.add_bytes;
+  g.ws_bytes = g.off_add_part + g.add_part_bytes;
   const int esize = bf ? 2 : 4;
   const int cpr = d * esize / 16;
   const size_t bufb = (size_t)kTileTokens * pow2_slots(cpr) * 16;

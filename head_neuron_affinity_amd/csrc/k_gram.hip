@@ -14,9 +14,9 @@
 //   gram_reduce   fixed-order sum over the token chunks;
 //   quad_kernel   Y = C_h M_h(:, block) on the matrix cores, then
 //                 add[g][k] = sum_{h in g} sum_{gate, up} m_hk . Y(:, k).
-// bf16 path: the scaled operand a / r^2 and the fp32 Gram entries are split
-// into two bf16 terms (hi + lo), so products stay exact in fp32 and the split
-// leaves a relative error near 2^-16.  f32 path: fp32 MFMA throughout.
+// bf16 path: the scaled operand a / r^2 and the reduced fp32 Gram entries are
+// split into two bf16 terms (hi + lo), so products stay exact in fp32 and the
+// split leaves a relative error near 2^-16.  f32 path: fp32 MFMA throughout.
 #include "hna_internal.h"
 
 namespace hna {
@@ -192,58 +192,82 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
   }
 }
 
+// C = sum over the token chunks in chunk order (4 entries per thread).  bf16
+// path: C is written as two bf16 planes (high part, then remainder), the form
+// the quadratic-form kernel multiplies; fp32 path: fp32.
+template <bool BF>
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int n_gc,
-                                                          int64_t n, float* __restrict__ C) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.f;
-  for (int c = 0; c < n_gc; ++c) s += part[(int64_t)c * n + i];
-  C[i] = s;
+                                                          int64_t n, void* __restrict__ C) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;   // n is a multiple of 16 (d % 16 == 0)
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  int c = 0;
+  for (; c + 4 <= n_gc; c += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float4*>(part + (int64_t)(c + j) * n + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+    }
+  }
+  for (; c < n_gc; ++c) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)c * n + i);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if constexpr (BF) {
+    const uint32_t h01 = pack_bf16x2(s.x, s.y), h23 = pack_bf16x2(s.z, s.w);
+    const uint32_t l01 = pack_bf16x2(s.x - bf16_bits_to_f32(h01 & 0xffffu), s.y - __uint_as_float(h01 & 0xffff0000u));
+    const uint32_t l23 = pack_bf16x2(s.z - bf16_bits_to_f32(h23 & 0xffffu), s.w - __uint_as_float(h23 & 0xffff0000u));
+    uint16_t* c16 = static_cast<uint16_t*>(C);
+    *reinterpret_cast<uint2*>(c16 + i) = make_uint2(h01, h23);
+    *reinterpret_cast<uint2*>(c16 + n + i) = make_uint2(l01, l23);
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(C) + i) = s;
+  }
 }
 
-// grid (G, ceil(KB / 4)); wave w handles neuron block blockIdx.y * 4 + w.
+// grid (H, ceil(KB / 4)), 4 waves: head blockIdx.x; wave w handles neuron block
+// blockIdx.y * 4 + w and writes add_part[h][32 kb + l] (gate and up summed).
+// C_h (bf16 high and remainder planes, or fp32) is copied into LDS; Y = C_h M
+// for the wave's 32 neurons comes out of the MFMAs in the C layout (column
+// l % 32, rows 8 (v / 4) + 4 (l / 32) + v % 4 of a 32-row tile), and each lane
+// takes the dot product of its Y entries with the matching folded-weight
+// entries: rows with (row / 8) % 2 == l / 32 are in its own fragment, the
+// others in the fragment of lane l ^ 32 (one exchange per d-step).
+constexpr int kQWaves = 4;
 template <typename E, int S>
-__global__ __launch_bounds__(kGThreads) void quad_kernel(const QuadParams p) {
+__global__ __launch_bounds__(64 * kQWaves) void quad_kernel(const QuadParams p) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int Q = BF ? 1 : 2;
   constexpr int DD = 16 * S;                          // d
   constexpr int D32 = (DD + 31) & ~31;
   constexpr int NT = D32 / 32;
   constexpr int CP = DD + (BF ? 8 : 4);               // LDS pitch of C (elements)
+  constexpr int EPC = 16 / sizeof(E);                 // elements per 16 bytes
   constexpr int kSlabBytes = 64 * 8 * sizeof(E);
-  __shared__ __attribute__((aligned(16))) E chi[D32 * CP];
-  __shared__ __attribute__((aligned(16))) E clo[BF ? D32 * CP : 8];
-  __shared__ __attribute__((aligned(16))) float ybuf[4][D32 * 32];
+  constexpr int NB = BF ? 2 : 1;                      // C planes
+  constexpr int NTH = 64 * kQWaves;
+  __shared__ __attribute__((aligned(16))) E cs[NB][D32 * CP];
 
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int kb = blockIdx.y * 4 + w;
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, half = l >> 5;
+  const int kb = blockIdx.y * kQWaves + w;
   const bool active = kb < p.KB;
   const int kbc = active ? kb : p.KB - 1;
   const char* Mbytes = static_cast<const char*>(p.M);
   float q = 0.f;
 
-  for (int x = tid; x < (D32 - DD) * CP; x += kGThreads) {
-    chi[DD * CP + x] = E(0.f);
-    if constexpr (BF) clo[DD * CP + x] = E(0.f);
-  }
-  for (int hh = p.group_start[g]; hh < p.group_start[g + 1]; ++hh) {
-    const int h = p.head_order[hh];
-    const float* C = p.C + (int64_t)h * DD * DD;
-    __syncthreads();
-    for (int x = tid; x < DD * DD / 4; x += kGThreads) {
-      const int i = (4 * x) / DD, j = (4 * x) % DD;
-      const float4 v = *reinterpret_cast<const float4*>(C + 4 * x);
-      const float cv[4] = {v.x, v.y, v.z, v.w};
+  for (int x = tid; x < (D32 - DD) * CP; x += NTH)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (BF) {
-          const uint16_t hb = bf16_rn(cv[e]);
-          reinterpret_cast<uint16_t*>(chi)[i * CP + j + e] = hb;
-          reinterpret_cast<uint16_t*>(clo)[i * CP + j + e] = bf16_rn(cv[e] - bf16_bits_to_f32(hb));
-        } else {
-          chi[i * CP + j + e] = cv[e];
-        }
+    for (int b = 0; b < NB; ++b) cs[b][DD * CP + x] = E(0.f);
+  {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const E* C = static_cast<const E*>(p.C) + ((int64_t)b * p.H + h) * DD * DD;
+      for (int x = tid; x < DD * DD / EPC; x += NTH) {
+        const int i = (x * EPC) / DD, jj = (x * EPC) % DD;
+        *reinterpret_cast<uint4*>(&cs[b][i * CP + jj]) = reinterpret_cast<const uint4*>(C)[x];
       }
     }
     __syncthreads();
@@ -257,32 +281,9 @@ __global__ __launch_bounds__(kGThreads) void quad_kernel(const QuadParams p) {
 #pragma unroll
         for (int qq = 0; qq < Q; ++qq)
           bfr[s][qq] = *reinterpret_cast<const uint4*>(Mb + s * kSlabBytes + qq * 16);
-#pragma unroll
-      for (int it = 0; it < NT; ++it) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int off = (it * 32 + (l & 31)) * CP + 16 * s + 8 * (l >> 5);
-          uint4 ah[Q];
-#pragma unroll
-          for (int qq = 0; qq < Q; ++qq)
-            ah[qq] = *reinterpret_cast<const uint4*>(&chi[off] + qq * (16 / sizeof(E)));
-          mma(acc, ah, bfr[s]);
-          if constexpr (BF) {
-            uint4 al[1];
-            al[0] = *reinterpret_cast<const uint4*>(&clo[off]);
-            mma(acc, al, bfr[s]);
-          }
-        }
-        // Y rows it*32 + m, column l & 31
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-          ybuf[w][(it * 32 + m) * 32 + (l & 31)] = acc[v];
-        }
-      }
-      __syncthreads();
-      // q += sum_j M[j][k] Y[j][k] over this lane's fragment rows j
+      // per d-step: this lane's fragment entries 4 half .. 4 half + 3 (own
+      // rows) and the partner's (rows of the other half), as floats
+      float own[S][4], oth[S][4];
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         float mv[8];
@@ -294,28 +295,69 @@ __global__ __launch_bounds__(kGThreads) void quad_kernel(const QuadParams p) {
             mv[2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
           }
         } else {
-          mv[0] = __uint_as_float(bfr[s][0].x); mv[1] = __uint_as_float(bfr[s][0].y);
-          mv[2] = __uint_as_float(bfr[s][0].z); mv[3] = __uint_as_float(bfr[s][0].w);
-          mv[4] = __uint_as_float(bfr[s][Q - 1].x); mv[5] = __uint_as_float(bfr[s][Q - 1].y);
-          mv[6] = __uint_as_float(bfr[s][Q - 1].z); mv[7] = __uint_as_float(bfr[s][Q - 1].w);
+          const uint32_t wv[8] = {bfr[s][0].x, bfr[s][0].y, bfr[s][0].z, bfr[s][0].w,
+                                  bfr[s][Q - 1].x, bfr[s][Q - 1].y, bfr[s][Q - 1].z, bfr[s][Q - 1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mv[e] = __uint_as_float(wv[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 16 * s + 8 * (l >> 5) + e;
-          q = fmaf(mv[e], ybuf[w][j * 32 + (l & 31)], q);
+        for (int r = 0; r < 4; ++r) {
+          own[s][r] = half ? mv[4 + r] : mv[r];
+          const float send = half ? mv[r] : mv[4 + r];   // what the partner needs
+          oth[s][r] = __shfl_xor(send, 32);
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int off = (it * 32 + (l & 31)) * CP + 16 * s + 8 * half;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            uint4 ah[Q];
+#pragma unroll
+            for (int qq = 0; qq < Q; ++qq)
+              ah[qq] = *reinterpret_cast<const uint4*>(&cs[b][off] + qq * EPC);
+            mma(acc, ah, bfr[s]);
+          }
+        }
+        // rows it*32 + 8 a + 4 half + r (v = 4 a + r): d-step 2 it + a / 2,
+        // entry r of own (a % 2 == half) or of the partner's
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int a = v >> 2, r = v & 3, s = 2 * it + (a >> 1);
+          if (s < S) q = fmaf((a & 1) == half ? own[s][r] : oth[s][r], acc[v], q);
+        }
+      }
     }
   }
   q += __shfl_xor(q, 32);
-  if (active && l < 32) p.add[(int64_t)g * p.KB * 32 + kb * 32 + l] = q;
+  if (active && l < 32) p.add_part[(int64_t)h * p.KB * 32 + kb * 32 + l] = q;
+}
+
+// add[g][k] = sum of add_part[h][k] over the heads h of KV group g, in head
+// order (fixed-order sum).
+__global__ __launch_bounds__(256) void quad_group_sum_kernel(const QuadParams p) {
+  const int64_t n = (int64_t)p.KB * 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.G * n) return;
+  const int g = (int)(idx / n);
+  const int64_t k = idx - g * n;
+  float s = 0.f;
+  for (int hh = p.group_start[g]; hh < p.group_start[g + 1]; ++hh)
+    s += p.add_part[(int64_t)p.head_order[hh] * n + k];
+  p.add[idx] = s;
 }
 
 template <typename E, int S>
 hipError_t launch_quad_t(const QuadParams& p, hipStream_t st) {
-  const dim3 grid(p.G, (p.KB + 3) / 4);
-  hipLaunchKernelGGL((quad_kernel<E, S>), grid, dim3(kGThreads), 0, st, p);
+  const dim3 grid(p.H, (p.KB + kQWaves - 1) / kQWaves);
+  hipLaunchKernelGGL((quad_kernel<E, S>), grid, dim3(64 * kQWaves), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)p.G * p.KB * 32;
+  hipLaunchKernelGGL(quad_group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -344,10 +386,12 @@ hipError_t launch_gram(const GramParams& p, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, float* C, hipStream_t st) {
+hipError_t launch_gram_reduce(const float* part, int n_gc, int64_t n, void* C, int dtype,
+                              hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gram_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     part, n_gc, n, C);
+  const dim3 grid((unsigned)((n / 4 + 255) / 256));
+  if (dtype == 1) hipLaunchKernelGGL(gram_reduce_kernel<true>, grid, dim3(256), 0, st, part, n_gc, n, C);
+  else hipLaunchKernelGGL(gram_reduce_kernel<false>, grid, dim3(256), 0, st, part, n_gc, n, C);
   return hipGetLastError();
 }
 

@@ -130,15 +130,17 @@ def test_workspace_sizes_follow_geometry():
     a256 = lambda x: (x + 255) // 256 * 256
     # Qwen3-0.6B-shaped layer: 512 token tiles of 128 -> 64 chunks of 8 tiles;
     # FO partial sums [64][G+1][I] fp32, then the Gram partials over 32 token
-    # chunks [32][H][d][d], the reduced Gram matrices [H][d][d] and ADD [G][I].
+    # chunks [32][H][d][d], the reduced Gram matrices [H][d][d], ADD [G][I] and
+    # the per-head ADD sums [H][I].
     dm = hna.make_dims(65536, 1024, 16, 8, 128, 3072, 1)
     assert hna.up_workspace_bytes(dm) == (64 * 9 * 3072 * 4 + 32 * 16 * 128 * 128 * 4
-                                          + 16 * 128 * 128 * 4 + 8 * 3072 * 4)
+                                          + 16 * 128 * 128 * 4 + 8 * 3072 * 4 + 16 * 3072 * 4)
     assert hna.folded_bytes(dm) == 16 * 128 * 2 * 3072 * 2
     # ragged neuron count pads to 32; T = 1 is one chunk and one Gram chunk
     dm = hna.make_dims(1, 64, 4, 2, 16, 101, 0)
     assert hna.up_workspace_bytes(dm) == (a256(1 * 3 * 128 * 4) + a256(4 * 16 * 16 * 4)
-                                          + a256(4 * 16 * 16 * 4) + a256(2 * 128 * 4))
+                                          + a256(4 * 16 * 16 * 4) + a256(2 * 128 * 4)
+                                          + a256(4 * 128 * 4))
     assert hna.folded_bytes(dm) == 4 * 16 * 2 * 128 * 4
     # gamma'-scaled W_down^T in the input dtype, then the segment partials
     # [H' + 2G'][I]
