@@ -44,6 +44,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = ["LayerShape", "CONFIGS", "layer_shape", "make_layer", "layer_seed",
+           "contiguous_layout", "random_balanced_layout", "make_scores",
            "default_group_map"]
 
 
@@ -209,3 +210,47 @@ def make_config_layer(config: int, layer: int = 0, T: Optional[int] = None,
     if dtype is not None:
         sh = sh.with_dtype(dtype)
     return make_layer(sh, layer_seed(config, layer), device=device, with_next=with_next)
+
+
+# ---------------------------------------------------------------------------
+# Layouts and score matrices for the layout objective
+#
+# A layout of an N-layer stack on L devices is, per layer i, a device for each
+# KV group (heads[i][g]) and for each FFN neuron (neurons[i][k]).  Every layout
+# here is balanced: G/L groups and I/L neurons per device.  "Contiguous" slices
+# groups and neurons in storage order; a random layout is a uniform balanced
+# permutation of the contiguous one, drawn independently per layer.  These are
+# inputs of the objective, as the scores are; nothing here evaluates it.
+
+def contiguous_layout(N: int, G: int, I: int, L: int):
+    """(heads [N, G], neurons [N, I]) int32: device g // (G/L) and k // (I/L)."""
+    if G % L or I % L:
+        raise ValueError(f"G={G} and I={I} must be multiples of L={L}")
+    heads = (torch.arange(G, dtype=torch.int32) // (G // L)).repeat(N, 1)
+    neurons = (torch.arange(I, dtype=torch.int32) // (I // L)).repeat(N, 1)
+    return heads, neurons
+
+
+def random_balanced_layout(N: int, G: int, I: int, L: int, seed: int):
+    """Uniform balanced layout: each layer permutes the contiguous assignment."""
+    gen = torch.Generator().manual_seed(seed)
+    h0, n0 = contiguous_layout(1, G, I, L)
+    heads = torch.stack([h0[0][torch.randperm(G, generator=gen)] for _ in range(N)])
+    neurons = torch.stack([n0[0][torch.randperm(I, generator=gen)] for _ in range(N)])
+    return heads, neurons
+
+
+def make_scores(N: int, G: int, I: int, seed: int, sigma: float = 1.0, zero_frac: float = 0.0):
+    """Non-negative stand-ins for the affinity scores of an N-layer stack:
+    S_up [N, G, I] and S_down [N-1, I, G], float32, log-normal entries with a
+    per-(layer, group) scale (some groups matter more, as on the pages'
+    figures), optionally with a fraction of exact zeros."""
+    gen = torch.Generator().manual_seed(seed)
+    gscale = torch.exp(sigma * torch.randn(N, G, 1, generator=gen, dtype=torch.float64))
+    up = gscale * torch.exp(sigma * torch.randn(N, G, I, generator=gen, dtype=torch.float64))
+    gs2 = torch.exp(sigma * torch.randn(max(N - 1, 0), 1, G, generator=gen, dtype=torch.float64))
+    down = gs2 * torch.exp(sigma * torch.randn(max(N - 1, 0), I, G, generator=gen, dtype=torch.float64))
+    if zero_frac > 0:
+        up[torch.rand(up.shape, generator=gen, dtype=torch.float64) < zero_frac] = 0
+        down[torch.rand(down.shape, generator=gen, dtype=torch.float64) < zero_frac] = 0
+    return up.to(torch.float32), down.to(torch.float32)
