@@ -99,6 +99,40 @@ def copy_probe(mib: int):
     del src, dst
 
 
+def objective_bench(hna, reps: int):
+    """Layout objective J (eq. 6) over a 28-layer stack of score matrices
+    (8 KV groups x 3072 neurons, the Qwen3-0.6B shape) on 4 devices: average
+    duration of one hna_layout_objective call over `reps` calls, HIP events on
+    the launch stream.  Algorithmic bytes: every score read once plus the
+    device maps."""
+    import torch
+    import synth
+    N, G, I, L = 28, 8, 3072, 4
+    S_up, S_down = synth.make_scores(N, G, I, seed=11)
+    heads, neurons = synth.random_balanced_layout(N, G, I, L, seed=11)
+    S_up, S_down, heads, neurons = (t.cuda() for t in (S_up, S_down, heads, neurons))
+    fu = torch.empty(N, dtype=torch.float64, device="cuda")
+    fd = torch.empty(N - 1, dtype=torch.float64, device="cuda")
+    J = torch.empty(1, dtype=torch.float64, device="cuda")
+    for _ in range(3):
+        hna.layout_objective(S_up, S_down, heads, neurons, fu, fd, J)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        hna.layout_objective(S_up, S_down, heads, neurons, fu, fd, J)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = 4 * (N * G * I + (N - 1) * I * G) + 4 * (N * G + N * I)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"score stack N={N} G={G} I={I}, {L} devices", "us_per_call": us,
+            "J": float(J.cpu()[0]),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+
+
 def build_inputs(config: int, T=None):
     import synth
     return synth.make_config_layer(config, T=T, device="cuda")
@@ -191,6 +225,7 @@ def main():
         "mfma_frac_whole_step": flops_hot * n_layers / (ms_step * 1e-3) / 1e12 / peak,
         "hot_stream_gbs": stream_bytes / (hot_ms * 1e-3) / 1e9,
     }
+    rec["objective"] = objective_bench(hna, 200)
     if not args.no_cpu_baseline and n_layers == 1:
         rec["cpu_baseline"] = cpu_baseline(L0)
     print(json.dumps(rec), flush=True)

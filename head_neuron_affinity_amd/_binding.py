@@ -31,7 +31,8 @@ EXPORTED = [
     "hna_abi_version", "hna_status_string", "hna_last_error", "hna_folded_bytes",
     "hna_fold_workspace_bytes", "hna_fold_up_weights", "hna_down_col_sqnorm",
     "hna_up_workspace_bytes", "hna_affinity_up", "hna_affinity_add", "hna_finalize_up",
-    "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine",
+    "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine", "hna_unit_mass",
+    "hna_layout_objective",
 ]
 
 
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         "hna_down_workspace_bytes": (sz, [ddp]),
         "hna_down_weight_norms": (ctypes.c_int, [ddp, vp, vp, vp, vp, vp, ip, vp, vp, sz, vp]),
         "hna_down_combine": (ctypes.c_int, [i32, i32, vp, vp, vp, vp]),
+        "hna_unit_mass": (ctypes.c_int, [vp, i64, i32, vp, vp]),
+        "hna_layout_objective": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -249,3 +252,51 @@ def down_combine(c_down, n, out=None) -> torch.Tensor:
     _check(lib().hna_down_combine(int(I), int(G), _ptr(c_down), _ptr(n), _ptr(out),
                                   _stream(n.device)), "hna_down_combine")
     return out
+
+
+# ------------------------------------------------------- layout objective
+def unit_mass(S: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Each matrix S[m] (fp32, last two dims) divided by its own sum; 0 if the sum is 0."""
+    _need_cuda(S)
+    if S.dtype != torch.float32 or S.dim() < 2:
+        raise ValueError("S must be an fp32 tensor of at least 2 dims")
+    if out is None:
+        out = torch.empty_like(S)
+    count = S.shape[-1] * S.shape[-2]
+    n_mat = S.numel() // count if count else 0
+    _check(lib().hna_unit_mass(_ptr(S), int(count), int(n_mat), _ptr(out), _stream(S.device)),
+           "hna_unit_mass")
+    return out
+
+
+def layout_objective(S_up: torch.Tensor, S_down: Optional[torch.Tensor], head_device: torch.Tensor,
+                     neuron_device: torch.Tensor, frac_up: Optional[torch.Tensor] = None,
+                     frac_down: Optional[torch.Tensor] = None, J: Optional[torch.Tensor] = None):
+    """J of eq. (6) with the per-matrix co-located fractions (fp64 device tensors).
+
+    S_up [N, G, I], S_down [N-1, I, G] fp32; head_device [N, G], neuron_device [N, I] int32.
+    Returns (J [1], frac_up [N], frac_down [N-1]).
+    """
+    _need_cuda(S_up, S_down, head_device, neuron_device)
+    N, G, I = S_up.shape
+    if S_up.dtype != torch.float32 or (S_down is not None and S_down.dtype != torch.float32):
+        raise ValueError("scores must be fp32")
+    if head_device.dtype != torch.int32 or neuron_device.dtype != torch.int32:
+        raise ValueError("device maps must be int32")
+    if tuple(head_device.shape) != (N, G) or tuple(neuron_device.shape) != (N, I):
+        raise ValueError("device maps must be [N, G] and [N, I]")
+    if N > 1 and (S_down is None or tuple(S_down.shape) != (N - 1, I, G)):
+        raise ValueError("S_down must be [N-1, I, G]")
+    dev = S_up.device
+    if frac_up is None:
+        frac_up = torch.empty(N, dtype=torch.float64, device=dev)
+    if frac_down is None:
+        frac_down = torch.empty(max(N - 1, 1), dtype=torch.float64, device=dev)
+    if J is None:
+        J = torch.empty(1, dtype=torch.float64, device=dev)
+    _check(lib().hna_layout_objective(int(N), int(G), int(I), _ptr(S_up),
+                                      _ptr(S_down) if N > 1 else None, _ptr(head_device),
+                                      _ptr(neuron_device), _ptr(frac_up),
+                                      _ptr(frac_down) if N > 1 else None, _ptr(J),
+                                      _stream(dev)), "hna_layout_objective")
+    return J, frac_up, frac_down[:N - 1]

@@ -428,4 +428,45 @@ int hna_down_combine(int32_t I, int32_t G_next, const float* c_down, const float
   return finish(launch_down_combine(c_down, n, I, G_next, S_down, st), st, fn);
 }
 
+int hna_unit_mass(const float* S, int64_t count, int32_t n_matrices, float* out, void* stream) {
+  const char* fn = "hna_unit_mass";
+  if (count < 0 || n_matrices < 0)
+    return fail(HNA_ERR_INVALID_ARG, "%s: count=%lld and n_matrices=%d must be >= 0", fn,
+                (long long)count, n_matrices);
+  if (count == 0 || n_matrices == 0) {
+    g_last_error.clear();
+    return HNA_OK;
+  }
+  REQUIRE_PTR(S);
+  REQUIRE_PTR(out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_unit_mass(S, count, n_matrices, out, st), st, fn);
+}
+
+int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, const float* S_down,
+                         const int32_t* head_device, const int32_t* neuron_device,
+                         double* frac_up, double* frac_down, double* J, void* stream) {
+  const char* fn = "hna_layout_objective";
+  if (N < 1 || G < 1 || I < 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: N=%d, G=%d and I=%d must be positive", fn, N, G, I);
+  if (N > max_objective_layers())
+    return fail(HNA_ERR_UNSUPPORTED, "%s: N=%d exceeds %d layers", fn, N, max_objective_layers());
+  if ((int64_t)G * I > (int64_t)1 << 31)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: G*I=%lld exceeds 2^31 entries per matrix", fn,
+                (long long)G * I);
+  REQUIRE_PTR(S_up);
+  REQUIRE_PTR(head_device);
+  REQUIRE_PTR(neuron_device);
+  REQUIRE_PTR(frac_up);
+  REQUIRE_PTR(J);
+  if (N > 1) {
+    REQUIRE_PTR(S_down);
+    REQUIRE_PTR(frac_down);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_layout_objective(S_up, S_down, head_device, neuron_device, N, G, I,
+                                        frac_up, frac_down, J, st),
+                st, fn);
+}
+
 }  // extern "C"

@@ -143,6 +143,13 @@ hipError_t launch_down_group_sum(const float* seg_part, const int16_t* seg_list,
 hipError_t launch_down_combine(const float* c, const float* n, int I, int G_next,
                                float* S_down, hipStream_t st);
 
+// ----------------------------------------------------------- layout objective
+hipError_t launch_unit_mass(const float* S, int64_t count, int n_mat, float* out, hipStream_t st);
+int max_objective_layers();
+hipError_t launch_layout_objective(const float* S_up, const float* S_down, const int32_t* heads,
+                                   const int32_t* neurons, int N, int G, int I, double* frac_up,
+                                   double* frac_down, double* J, hipStream_t st);
+
 // ------------------------------------------------------ scaled NT GEMM (MFMA)
 // C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] and Y [N, K] row-major with
 // c contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a

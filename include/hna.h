@@ -196,6 +196,43 @@ int hna_down_weight_norms(const hna_down_dims* dims, const void* W_q, const void
 int hna_down_combine(int32_t I, int32_t G_next, const float* c_down, const float* n,
                      float* S_down, void* stream);
 
+/* ------------------------------------------------------- layout objective */
+
+/*
+ * Unit-mass normalisation (section 3, paragraph "Objective"): S holds
+ * n_matrices consecutive fp32 matrices of `count` entries each; every one is
+ * divided by its own sum, taken in fp64 in a fixed order, and the quotient is
+ * rounded to fp32 into out.  A matrix whose sum is 0 becomes all zeros.  out
+ * may equal S (in place).  count == 0 or n_matrices == 0 is a no-op.
+ */
+int hna_unit_mass(const float* S, int64_t count, int32_t n_matrices, float* out, void* stream);
+
+/*
+ * Layout objective J of eq. (6) (section 3, paragraph "Objective") over a
+ * stack of N layers:
+ *   S_up   fp32 [N, G, I]: up-edge scores of layer i (KV group g, neuron k)
+ *   S_down fp32 [N-1, I, G]: down-edge scores from layer i's neuron k to
+ *          layer i+1's KV group g; may be NULL when N == 1
+ *   head_device   int32 [N, G]: device of KV group g of layer i
+ *   neuron_device int32 [N, I]: device of neuron k of layer i
+ * Outputs (fp64, device memory):
+ *   frac_up[i]   = mass of unit-mass S_up[i] on entries (g, k) with
+ *                  head_device[i, g] == neuron_device[i, k]
+ *   frac_down[i] = mass of unit-mass S_down[i] on entries (k, g) with
+ *                  neuron_device[i, k] == head_device[i+1, g]   (N-1 values;
+ *                  may be NULL when N == 1)
+ *   J[0]         = sum of the N + (N-1) fractions, in that order
+ * The scores need not be normalised beforehand: each fraction is the
+ * matrix's co-located sum over its total sum, both accumulated in fp64 in a
+ * fixed order (0 for a matrix whose total is 0), so results are reproducible
+ * bit for bit.  Device ids are only compared for equality, never used as
+ * indices: any int32 values are valid.  Requires G*I <= 2^31 and
+ * N <= 2048 (HNA_ERR_UNSUPPORTED otherwise).
+ */
+int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, const float* S_down,
+                         const int32_t* head_device, const int32_t* neuron_device,
+                         double* frac_up, double* frac_down, double* J, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -201,6 +201,35 @@ def test_finalize_and_other_calls_validate():
     assert L.hna_down_combine(8, 2, vp(MIS), vp(FAKE), vp(FAKE), None) == -3
 
 
+def test_objective_calls_validate():
+    hna = _lib()
+    L = hna.lib()
+    vp = ctypes.c_void_p
+    F = vp(FAKE)
+    # no-op sizes succeed without touching the (NULL) pointers
+    assert L.hna_unit_mass(None, 0, 5, None, None) == 0
+    assert L.hna_unit_mass(None, 16, 0, None, None) == 0
+    assert L.hna_unit_mass(F, -1, 1, F, None) == -1
+    assert L.hna_unit_mass(F, 16, -1, F, None) == -1
+    assert L.hna_unit_mass(None, 16, 2, F, None) == -1
+    assert L.hna_unit_mass(F, 16, 2, vp(MIS), None) == -3
+    assert "out" in hna.last_error()
+    obj = L.hna_layout_objective
+    assert obj(0, 8, 64, F, F, F, F, F, F, F, None) == -1
+    assert obj(2, 0, 64, F, F, F, F, F, F, F, None) == -1
+    assert obj(2, 8, -3, F, F, F, F, F, F, F, None) == -1
+    assert obj(2, 1 << 16, 1 << 16, F, F, F, F, F, F, F, None) == -2   # G*I > 2^31
+    assert obj(2049, 8, 64, F, F, F, F, F, F, F, None) == -2            # N > 2048
+    assert obj(2, 8, 64, F, None, F, F, F, F, F, None) == -1           # S_down needed
+    assert obj(2, 8, 64, F, F, F, F, F, None, F, None) == -1           # frac_down needed
+    assert obj(2, 8, 64, F, F, vp(MIS), F, F, F, F, None) == -3
+    assert "head_device" in hna.last_error()
+    assert obj(2, 8, 64, F, F, F, F, F, F, None, None) == -1           # J
+    # N == 1 needs neither S_down nor frac_down; a NULL S_up still fails first
+    assert obj(1, 8, 64, None, None, F, F, F, None, F, None) == -1
+    assert "S_up" in hna.last_error()
+
+
 def test_error_text_is_thread_local():
     hna = _lib()
     call_up(hna, dims(hna, d=20))
