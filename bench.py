@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (matrix)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_TFLOPS = 78.6     # MI355X fp64 vector
 METRIC = "calibration tokens/s for S↑-fo affinity (Qwen3-0.6B layer); % MFMA peak"
 HOT_SRC = os.path.join(ROOT, "head_neuron_affinity_amd", "csrc", "k_affinity.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hot_kernel_traffic.json")
@@ -133,6 +134,44 @@ def objective_bench(hna, reps: int):
                          "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
 
 
+def neuron_step_bench(hna, reps: int):
+    """Neuron step of the layout search over the same 28-layer stack (unit-mass
+    scores, contiguous head devices on 4 devices): average duration of one
+    hna_neuron_step call (all layers, one workgroup each) over `reps` calls,
+    HIP events on the launch stream."""
+    import torch
+    import synth
+    N, G, I, L = 28, 8, 3072, 4
+    S_up, S_down = synth.make_scores(N, G, I, seed=11)
+    S_up, S_down = S_up.cuda(), S_down.cuda()
+    up, down = hna.unit_mass(S_up), hna.unit_mass(S_down)
+    heads, _ = synth.contiguous_layout(N, G, I, L)
+    heads = heads.cuda()
+    nu = torch.empty((N, I), dtype=torch.int32, device="cuda")
+    st = torch.empty((N, 4), dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        hna.neuron_step(up, down, heads, L, neuron_device=nu, stats=st)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        hna.neuron_step(up, down, heads, L, neuron_device=nu, stats=st)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    iters = hna.DUAL_ITERS
+    # algorithmic fp64 work of the dual ascent: per iteration and neuron, L
+    # subtractions M - lam and L - 1 comparisons
+    flops = (iters + 1) * N * I * (2 * L - 1)
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"workload": f"score stack N={N} G={G} I={I}, {L} devices, {iters} dual iterations",
+            "us_per_call": us, "us_per_dual_iteration": us / (iters + 1),
+            "stats_sum": [int(x) for x in st.sum(0).tolist()],
+            "roofline": {"bound": "alu", "achieved": tflops, "peak": PEAK_FP64_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / PEAK_FP64_TFLOPS, "traffic": None}}
+
+
 def build_inputs(config: int, T=None):
     import synth
     return synth.make_config_layer(config, T=T, device="cuda")
@@ -226,6 +265,7 @@ def main():
         "hot_stream_gbs": stream_bytes / (hot_ms * 1e-3) / 1e9,
     }
     rec["objective"] = objective_bench(hna, 200)
+    rec["neuron_step"] = neuron_step_bench(hna, 20)
     if not args.no_cpu_baseline and n_layers == 1:
         rec["cpu_baseline"] = cpu_baseline(L0)
     print(json.dumps(rec), flush=True)

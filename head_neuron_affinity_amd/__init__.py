@@ -9,7 +9,8 @@ from ._binding import (HnaError, HNA_BF16, HNA_F32, HNA_ACCUMULATE, hna_dims, hn
                        make_dims, lib, LIB_PATH, EXPORTED, fold_up_weights, down_col_sqnorm,
                        affinity_up, affinity_add, finalize_up, down_weight_norms, down_combine,
                        up_workspace_bytes, down_workspace_bytes, folded_bytes, status_string,
-                       last_error, unit_mass, layout_objective)
+                       last_error, unit_mass, layout_objective, neuron_step,
+                       DUAL_ITERS)
 from .pipeline import AffinityPass, pass_for_layer, affinity_layer
 
 __all__ = [
@@ -18,4 +19,5 @@ __all__ = [
     "finalize_up", "down_weight_norms", "down_combine", "up_workspace_bytes",
     "down_workspace_bytes", "folded_bytes", "status_string", "last_error", "AffinityPass",
     "pass_for_layer", "affinity_layer", "unit_mass", "layout_objective",
+    "neuron_step", "DUAL_ITERS",
 ]

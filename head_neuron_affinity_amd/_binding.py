@@ -26,13 +26,18 @@ HNA_ERR_HIP = -5
 HNA_F32 = 0
 HNA_BF16 = 1
 HNA_ACCUMULATE = 1
+HNA_LAYOUT_OK = 0
+HNA_LAYOUT_BAD_HEADS = 1
+HNA_LAYOUT_SWAP_LIMIT = 2
+HNA_LAYOUT_NO_MOVE = 3
+DUAL_ITERS = 300
 
 EXPORTED = [
     "hna_abi_version", "hna_status_string", "hna_last_error", "hna_folded_bytes",
     "hna_fold_workspace_bytes", "hna_fold_up_weights", "hna_down_col_sqnorm",
     "hna_up_workspace_bytes", "hna_affinity_up", "hna_affinity_add", "hna_finalize_up",
     "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine", "hna_unit_mass",
-    "hna_layout_objective",
+    "hna_layout_objective", "hna_neuron_step",
 ]
 
 
@@ -86,6 +91,7 @@ def lib() -> ctypes.CDLL:
         "hna_down_combine": (ctypes.c_int, [i32, i32, vp, vp, vp, vp]),
         "hna_unit_mass": (ctypes.c_int, [vp, i64, i32, vp, vp]),
         "hna_layout_objective": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "hna_neuron_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -300,3 +306,35 @@ def layout_objective(S_up: torch.Tensor, S_down: Optional[torch.Tensor], head_de
                                       _ptr(frac_down) if N > 1 else None, _ptr(J),
                                       _stream(dev)), "hna_layout_objective")
     return J, frac_up, frac_down[:N - 1]
+
+
+def neuron_step(S_up_hat: torch.Tensor, S_down_hat: Optional[torch.Tensor],
+                head_device: torch.Tensor, L: int, iters: int = DUAL_ITERS,
+                max_swaps: Optional[int] = None, neuron_device: Optional[torch.Tensor] = None,
+                stats: Optional[torch.Tensor] = None):
+    """Neuron step of the layout search for every layer (section 3, "Optimiser").
+
+    S_up_hat [N, G, I], S_down_hat [N-1, I, G] fp32 unit-mass scores;
+    head_device [N, G] int32 in [0, L).  Returns (neuron_device [N, I] int32,
+    stats [N, 4] int32: status, excess after the dual ascent, moves, swaps).
+    """
+    _need_cuda(S_up_hat, S_down_hat, head_device)
+    N, G, I = S_up_hat.shape
+    if S_up_hat.dtype != torch.float32 or (S_down_hat is not None and S_down_hat.dtype != torch.float32):
+        raise ValueError("scores must be fp32")
+    if head_device.dtype != torch.int32 or tuple(head_device.shape) != (N, G):
+        raise ValueError("head_device must be int32 [N, G]")
+    if N > 1 and (S_down_hat is None or tuple(S_down_hat.shape) != (N - 1, I, G)):
+        raise ValueError("S_down_hat must be [N-1, I, G]")
+    dev = S_up_hat.device
+    if max_swaps is None:
+        max_swaps = 4 * I
+    if neuron_device is None:
+        neuron_device = torch.empty((N, I), dtype=torch.int32, device=dev)
+    if stats is None:
+        stats = torch.empty((N, 4), dtype=torch.int32, device=dev)
+    _check(lib().hna_neuron_step(int(N), int(G), int(I), int(L), _ptr(S_up_hat),
+                                 _ptr(S_down_hat) if N > 1 else None, _ptr(head_device),
+                                 int(iters), int(max_swaps), _ptr(neuron_device), _ptr(stats),
+                                 _stream(dev)), "hna_neuron_step")
+    return neuron_device, stats

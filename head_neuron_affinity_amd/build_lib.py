@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libhna.so")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 
 SOURCES = ["hna_api.hip", "k_affinity.hip", "k_gram.hip", "k_gemm.hip", "k_small.hip",
-           "k_objective.hip"]
+           "k_objective.hip", "k_layout.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -24,7 +24,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # with ordinary vector instructions; the VGPR form of MFMA keeps accumulators
 # in VGPRs, so no accumulation-register reads are needed (its weight
 # fragments still go to accumulation registers, as MFMA operands).
-EXTRA = {"k_affinity.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"k_affinity.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # the layout search compares fp64 values bit for bit with plain arithmetic
+         "k_layout.hip": ["-ffp-contract=off"]}
 
 
 def _run(cmd):

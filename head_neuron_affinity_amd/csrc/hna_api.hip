@@ -469,4 +469,37 @@ int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, con
                 st, fn);
 }
 
+static_assert(HNA_LAYOUT_OK == kLayoutOk && HNA_LAYOUT_BAD_HEADS == kLayoutBadHeads &&
+                  HNA_LAYOUT_SWAP_LIMIT == kLayoutSwapLimit && HNA_LAYOUT_NO_MOVE == kLayoutNoMove,
+              "layout status codes");
+
+int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
+                    const float* S_down_hat, const int32_t* head_device, int32_t iters,
+                    int32_t max_swaps, int32_t* neuron_device, int32_t* stats, void* stream) {
+  const char* fn = "hna_neuron_step";
+  if (N < 1 || G < 1 || I < 1 || L < 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: N=%d, G=%d, I=%d and L=%d must be positive", fn, N, G,
+                I, L);
+  if (G % L || I % L)
+    return fail(HNA_ERR_INVALID_ARG, "%s: G=%d and I=%d must be multiples of L=%d", fn, G, I, L);
+  if (iters < 0 || max_swaps < 0)
+    return fail(HNA_ERR_INVALID_ARG, "%s: iters=%d and max_swaps=%d must be >= 0", fn, iters,
+                max_swaps);
+  if (L > kLayoutMaxDevices || G > kMaxHeads || I > kLayoutMaxNpt * 1024 ||
+      neuron_step_lds_bytes(I, L) > kLayoutMaxLds)
+    return fail(HNA_ERR_UNSUPPORTED,
+                "%s: L=%d, G=%d, I=%d outside L <= %d, G <= %d, I <= %d, I*L <= %d", fn, L, G, I,
+                kLayoutMaxDevices, kMaxHeads, kLayoutMaxNpt * 1024,
+                (int)(kLayoutMaxLds / sizeof(double)));
+  REQUIRE_PTR(S_up_hat);
+  REQUIRE_PTR(head_device);
+  REQUIRE_PTR(neuron_device);
+  REQUIRE_PTR(stats);
+  if (N > 1) REQUIRE_PTR(S_down_hat);
+  NeuronStepParams p{S_up_hat, S_down_hat, head_device, neuron_device, stats,
+                     N, G, I, L, iters, max_swaps};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_neuron_step(p, st), st, fn);
+}
+
 }  // extern "C"

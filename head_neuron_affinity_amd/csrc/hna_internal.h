@@ -150,6 +150,23 @@ hipError_t launch_layout_objective(const float* S_up, const float* S_down, const
                                    const int32_t* neurons, int N, int G, int I, double* frac_up,
                                    double* frac_down, double* J, hipStream_t st);
 
+// ------------------------------------------------- neuron step of the layout search
+constexpr int kLayoutMaxDevices = 8;
+constexpr int kLayoutMaxNpt = 16;                 // neurons per thread: I <= 16384
+constexpr size_t kLayoutMaxLds = 128 * 1024;      // the fp64 gain M [L][I] in LDS
+enum { kLayoutOk = 0, kLayoutBadHeads = 1, kLayoutSwapLimit = 2, kLayoutNoMove = 3 };
+
+struct NeuronStepParams {
+  const float* S_up;      // [N][G][I]
+  const float* S_down;    // [N-1][I][G]
+  const int32_t* heads;   // [N][G], devices 0..L-1
+  int32_t* neurons;       // [N][I] out
+  int32_t* stats;         // [N][4] out: status, excess after the dual ascent, moves, swaps
+  int N, G, I, L, iters, max_swaps;
+};
+size_t neuron_step_lds_bytes(int I, int L);
+hipError_t launch_neuron_step(const NeuronStepParams& p, hipStream_t st);
+
 // ------------------------------------------------------ scaled NT GEMM (MFMA)
 // C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] and Y [N, K] row-major with
 // c contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a

@@ -233,6 +233,47 @@ int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, con
                          const int32_t* head_device, const int32_t* neuron_device,
                          double* frac_up, double* frac_down, double* J, void* stream);
 
+/* ------------------------------------------- neuron step of the layout search */
+
+/* Per-layer status written by hna_neuron_step into stats[i*4 + 0]. */
+enum hna_layout_status {
+  HNA_LAYOUT_OK = 0,
+  HNA_LAYOUT_BAD_HEADS = 1,   /* a head device of layer i or i+1 is outside [0, L) */
+  HNA_LAYOUT_SWAP_LIMIT = 2,  /* the swap phase stopped at max_swaps swaps */
+  HNA_LAYOUT_NO_MOVE = 3      /* non-finite gains left the fix-up without a move */
+};
+
+/*
+ * Neuron step of the layout search (section 3, paragraph "Optimiser";
+ * iteration count and step decay from appendix A), for every layer of an
+ * N-layer stack at once, given the KV-group devices of all layers:
+ *   M_i[k, l] = sum_{g: h_i(g) = l} S_up_hat_i[g, k]
+ *             + sum_{g: h_{i+1}(g) = l} S_down_hat_i[k, g]     (no down term for i = N-1)
+ *   nu_i = a balanced assignment (I/L neurons per device) maximising
+ *          sum_k M_i[k, nu_i(k)]
+ * solved by dual ascent on the L device offsets (`iters` iterations; the
+ * pages use 300), a fix-up to the capacities and pairwise swaps (at most
+ * max_swaps per layer).  Inputs (device memory):
+ *   S_up_hat   fp32 [N, G, I] unit-mass up-edge scores (see hna_unit_mass)
+ *   S_down_hat fp32 [N-1, I, G] unit-mass down-edge scores; may be NULL if N == 1
+ *   head_device int32 [N, G], values in [0, L)
+ * Outputs (device memory):
+ *   neuron_device int32 [N, I]: nu_i(k) in [0, L); all -1 for a layer whose
+ *                 head devices (of layer i or i+1) fall outside [0, L)
+ *   stats int32 [N, 4]: hna_layout_status, the load in excess of the
+ *                 capacities after the dual ascent, fix-up moves, swaps
+ * Every decision compares fp64 values computed in a fixed order (M sums its
+ * up terms in increasing g, then its down terms; the offsets move by
+ * step*(count-cap)/cap with a first step of (max M - min M)/10 decaying by
+ * 0.98; ties go to the lowest device or neuron), so the result is exactly
+ * reproducible.  Limits: 1 <= L <= 8, G and I multiples of L, G <= 128,
+ * I <= 16384 and I*L <= 16384 (HNA_ERR_UNSUPPORTED otherwise).  Per-layer
+ * failures are reported in stats, not in the return value.
+ */
+int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
+                    const float* S_down_hat, const int32_t* head_device, int32_t iters,
+                    int32_t max_swaps, int32_t* neuron_device, int32_t* stats, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -230,6 +230,33 @@ def test_objective_calls_validate():
     assert "S_up" in hna.last_error()
 
 
+def test_neuron_step_validates():
+    hna = _lib()
+    L = hna.lib()
+    F = ctypes.c_void_p(FAKE)
+    ns = L.hna_neuron_step
+    ok = dict(N=3, G=8, I=3072, L=4)
+
+    def call(N=3, G=8, I=3072, Ld=4, up=F, down=F, heads=F, iters=300, ms=100, out=F, st=F):
+        return ns(N, G, I, Ld, up, down, heads, iters, ms, out, st, None)
+
+    assert call(N=0) == -1
+    assert call(Ld=0) == -1
+    assert call(G=6) == -1                 # G not a multiple of L
+    assert call(I=3070) == -1              # I not a multiple of L
+    assert call(iters=-1) == -1
+    assert call(ms=-1) == -1
+    assert call(Ld=16, G=16, I=1024) == -2  # more than 8 devices
+    assert call(Ld=8, I=4096) == -2         # I*L > 16384: the gains do not fit in LDS
+    assert call(I=20480) == -2
+    assert call(G=256) == -2
+    assert call(up=None) == -1
+    assert call(down=None) == -1
+    assert call(N=1, down=None, heads=ctypes.c_void_p(MIS)) == -3
+    assert call(st=None) == -1 and "stats" in hna.last_error()
+    assert ok
+
+
 def test_error_text_is_thread_local():
     hna = _lib()
     call_up(hna, dims(hna, d=20))
