@@ -172,6 +172,46 @@ def neuron_step_bench(hna, reps: int):
                          "unit": "TFLOP/s", "frac": tflops / PEAK_FP64_TFLOPS, "traffic": None}}
 
 
+def search_bench(hna, reps: int):
+    """Head step and the whole layout search over the same 28-layer stack:
+    average hna_head_step duration (HIP events, `reps` calls, neuron devices
+    from one neuron step), and the wall time of hna_layout_search from the
+    contiguous heads (it synchronises once per sweep)."""
+    import torch
+    import synth
+    N, G, I, L = 28, 8, 3072, 4
+    S_up, S_down = synth.make_scores(N, G, I, seed=11)
+    up, down = hna.unit_mass(S_up.cuda()), hna.unit_mass(S_down.cuda())
+    heads, _ = synth.contiguous_layout(N, G, I, L)
+    heads = heads.cuda()
+    nu, _ = hna.neuron_step(up, down, heads, L)
+    for _ in range(2):
+        hna.head_step(up, down, nu, L)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        hna.head_step(up, down, nu, L)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    head_us = e0.elapsed_time(e1) * 1e3 / reps
+    hna.layout_search(up, down, L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = hna.layout_search(up, down, L)
+    torch.cuda.synchronize()
+    search_ms = (time.perf_counter() - t0) * 1e3
+    # head step bytes: the scores read once plus the neuron devices
+    nbytes = 4 * (N * G * I + (N - 1) * I * G) + 4 * N * I
+    gbs = nbytes / (head_us * 1e-6) / 1e9
+    return {"workload": f"score stack N={N} G={G} I={I}, {L} devices, 2520 partitions per layer",
+            "head_step_us": head_us, "search_ms": search_ms, "sweeps": res["sweeps"],
+            "J_history": res["J_history"],
+            "head_step_roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+
+
 def build_inputs(config: int, T=None):
     import synth
     return synth.make_config_layer(config, T=T, device="cuda")
@@ -266,6 +306,7 @@ def main():
     }
     rec["objective"] = objective_bench(hna, 200)
     rec["neuron_step"] = neuron_step_bench(hna, 20)
+    rec["layout_search"] = search_bench(hna, 50)
     if not args.no_cpu_baseline and n_layers == 1:
         rec["cpu_baseline"] = cpu_baseline(L0)
     print(json.dumps(rec), flush=True)

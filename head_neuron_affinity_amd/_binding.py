@@ -30,6 +30,7 @@ HNA_LAYOUT_OK = 0
 HNA_LAYOUT_BAD_HEADS = 1
 HNA_LAYOUT_SWAP_LIMIT = 2
 HNA_LAYOUT_NO_MOVE = 3
+HNA_LAYOUT_BAD_NEURONS = 4
 DUAL_ITERS = 300
 
 EXPORTED = [
@@ -37,7 +38,8 @@ EXPORTED = [
     "hna_fold_workspace_bytes", "hna_fold_up_weights", "hna_down_col_sqnorm",
     "hna_up_workspace_bytes", "hna_affinity_up", "hna_affinity_add", "hna_finalize_up",
     "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine", "hna_unit_mass",
-    "hna_layout_objective", "hna_neuron_step",
+    "hna_layout_objective", "hna_neuron_step", "hna_head_step",
+    "hna_layout_search_workspace_bytes", "hna_layout_search",
 ]
 
 
@@ -92,6 +94,10 @@ def lib() -> ctypes.CDLL:
         "hna_unit_mass": (ctypes.c_int, [vp, i64, i32, vp, vp]),
         "hna_layout_objective": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "hna_neuron_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp]),
+        "hna_head_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "hna_layout_search_workspace_bytes": (sz, [i32, i32, i32]),
+        "hna_layout_search": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp,
+                                              ctypes.POINTER(ctypes.c_double), ip, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -338,3 +344,62 @@ def neuron_step(S_up_hat: torch.Tensor, S_down_hat: Optional[torch.Tensor],
                                  int(iters), int(max_swaps), _ptr(neuron_device), _ptr(stats),
                                  _stream(dev)), "hna_neuron_step")
     return neuron_device, stats
+
+
+def head_step(S_up_hat: torch.Tensor, S_down_hat: Optional[torch.Tensor],
+              neuron_device: torch.Tensor, L: int):
+    """Head step of the layout search for every layer (section 3, "Optimiser").
+
+    Returns (head_device [N, G] int32, score [N] fp64, status [N] int32)."""
+    _need_cuda(S_up_hat, S_down_hat, neuron_device)
+    N, G, I = S_up_hat.shape
+    if neuron_device.dtype != torch.int32 or tuple(neuron_device.shape) != (N, I):
+        raise ValueError("neuron_device must be int32 [N, I]")
+    if N > 1 and (S_down_hat is None or tuple(S_down_hat.shape) != (N - 1, I, G)):
+        raise ValueError("S_down_hat must be [N-1, I, G]")
+    dev = S_up_hat.device
+    heads = torch.empty((N, G), dtype=torch.int32, device=dev)
+    score = torch.empty(N, dtype=torch.float64, device=dev)
+    status = torch.empty(N, dtype=torch.int32, device=dev)
+    _check(lib().hna_head_step(int(N), int(G), int(I), int(L), _ptr(S_up_hat),
+                               _ptr(S_down_hat) if N > 1 else None, _ptr(neuron_device),
+                               _ptr(heads), _ptr(score), _ptr(status), _stream(dev)),
+           "hna_head_step")
+    return heads, score, status
+
+
+def layout_search(S_up_hat: torch.Tensor, S_down_hat: Optional[torch.Tensor], L: int,
+                  head_device: Optional[torch.Tensor] = None, iters: int = DUAL_ITERS,
+                  max_swaps: Optional[int] = None, max_sweeps: int = 16,
+                  workspace: Optional[torch.Tensor] = None) -> dict:
+    """Coordinate-ascent layout search (section 3, "Optimiser").
+
+    head_device: starting [N, G] int32 map (default contiguous).  Returns a
+    dict with heads [N, G], neurons [N, I], neuron_stats [N, 4] (device
+    tensors), J_history (list of floats, one per sweep run) and sweeps."""
+    _need_cuda(S_up_hat, S_down_hat)
+    N, G, I = S_up_hat.shape
+    dev = S_up_hat.device
+    if head_device is None:
+        head_device = (torch.arange(G, dtype=torch.int32, device=dev) // (G // L)).repeat(N, 1)
+    else:
+        head_device = head_device.clone()
+    _need_cuda(head_device)
+    if max_swaps is None:
+        max_swaps = 4 * I
+    L_ = lib()
+    wsb = L_.hna_layout_search_workspace_bytes(int(N), int(G), int(I))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    neurons = torch.empty((N, I), dtype=torch.int32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.int32, device=dev)
+    hist = (ctypes.c_double * max_sweeps)()
+    n = ctypes.c_int32(0)
+    _check(L_.hna_layout_search(int(N), int(G), int(I), int(L), _ptr(S_up_hat),
+                                _ptr(S_down_hat) if N > 1 else None, int(iters), int(max_swaps),
+                                int(max_sweeps), _ptr(head_device), _ptr(neurons), _ptr(stats),
+                                hist, ctypes.byref(n), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev)),
+           "hna_layout_search")
+    return {"heads": head_device, "neurons": neurons, "neuron_stats": stats,
+            "J_history": [hist[i] for i in range(n.value)], "sweeps": n.value}

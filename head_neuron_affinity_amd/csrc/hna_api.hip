@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/hna.h"
 #include "hna_internal.h"
@@ -470,7 +471,8 @@ int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, con
 }
 
 static_assert(HNA_LAYOUT_OK == kLayoutOk && HNA_LAYOUT_BAD_HEADS == kLayoutBadHeads &&
-                  HNA_LAYOUT_SWAP_LIMIT == kLayoutSwapLimit && HNA_LAYOUT_NO_MOVE == kLayoutNoMove,
+                  HNA_LAYOUT_SWAP_LIMIT == kLayoutSwapLimit &&
+                  HNA_LAYOUT_NO_MOVE == kLayoutNoMove && HNA_LAYOUT_BAD_NEURONS == kLayoutBadNeurons,
               "layout status codes");
 
 int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
@@ -500,6 +502,176 @@ int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_u
                      N, G, I, L, iters, max_swaps};
   hipStream_t st = static_cast<hipStream_t>(stream);
   return finish(launch_neuron_step(p, st), st, fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+// G! / ((G/L)!)^L, or -1 above kHeadMaxParts
+long long partition_count(int G, int L) {
+  // multiply in the multinomial one factor at a time: C(n, per) for each device
+  const int per = G / L;
+  long long total = 1;
+  int n = G;
+  for (int l = 0; l < L; ++l) {
+    long long c = 1;
+    for (int j = 1; j <= per; ++j) c = c * (n - per + j) / j;   // C(n, per), exact at each step
+    total *= c;
+    if (total > kHeadMaxParts) return -1;
+    n -= per;
+  }
+  return total;
+}
+
+int check_layout_dims(const char* fn, int N, int G, int I, int L) {
+  if (N < 1 || G < 1 || I < 1 || L < 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: N=%d, G=%d, I=%d and L=%d must be positive", fn, N, G,
+                I, L);
+  if (G % L || I % L)
+    return fail(HNA_ERR_INVALID_ARG, "%s: G=%d and I=%d must be multiples of L=%d", fn, G, I, L);
+  return HNA_OK;
+}
+
+int check_head_dims(const char* fn, int G, int L) {
+  if (L > kLayoutMaxDevices || G > kHeadMaxGroups || partition_count(G, L) < 0)
+    return fail(HNA_ERR_UNSUPPORTED,
+                "%s: G=%d, L=%d outside L <= %d, G <= %d and at most %d balanced partitions", fn,
+                G, L, kLayoutMaxDevices, kHeadMaxGroups, kHeadMaxParts);
+  return HNA_OK;
+}
+
+struct SearchWorkspace {
+  size_t heads, neurons, stats, hscore, hstatus, frac_up, frac_down, J, total;
+};
+SearchWorkspace search_workspace(int N, int G, int I) {
+  SearchWorkspace w;
+  size_t o = 0;
+  w.heads = o;     o += align256((size_t)N * G * 4);
+  w.neurons = o;   o += align256((size_t)N * I * 4);
+  w.stats = o;     o += align256((size_t)N * 16);
+  w.hscore = o;    o += align256((size_t)N * 8);
+  w.hstatus = o;   o += align256((size_t)N * 4);
+  w.frac_up = o;   o += align256((size_t)N * 8);
+  w.frac_down = o; o += align256((size_t)N * 8);
+  w.J = o;         o += align256(8);
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hna_head_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
+                  const float* S_down_hat, const int32_t* neuron_device, int32_t* head_device,
+                  double* score, int32_t* status, void* stream) {
+  const char* fn = "hna_head_step";
+  int rc = check_layout_dims(fn, N, G, I, L);
+  if (rc != HNA_OK) return rc;
+  rc = check_head_dims(fn, G, L);
+  if (rc != HNA_OK) return rc;
+  REQUIRE_PTR(S_up_hat);
+  REQUIRE_PTR(neuron_device);
+  REQUIRE_PTR(head_device);
+  REQUIRE_PTR(score);
+  REQUIRE_PTR(status);
+  if (N > 1) REQUIRE_PTR(S_down_hat);
+  HeadStepParams p{S_up_hat, S_down_hat, neuron_device, head_device, score, status,
+                   N, G, I, L, (int)partition_count(G, L)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_head_step(p, st), st, fn);
+}
+
+size_t hna_layout_search_workspace_bytes(int32_t N, int32_t G, int32_t I) {
+  if (N < 1 || G < 1 || I < 1) return 0;
+  return search_workspace(N, G, I).total;
+}
+
+int hna_layout_search(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
+                      const float* S_down_hat, int32_t iters, int32_t max_swaps,
+                      int32_t max_sweeps, int32_t* head_device, int32_t* neuron_device,
+                      int32_t* neuron_stats, double* J_history, int32_t* n_sweeps,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "hna_layout_search";
+  int rc = check_layout_dims(fn, N, G, I, L);
+  if (rc != HNA_OK) return rc;
+  rc = check_head_dims(fn, G, L);
+  if (rc != HNA_OK) return rc;
+  if (iters < 0 || max_swaps < 0 || max_sweeps < 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: iters=%d, max_swaps=%d must be >= 0, max_sweeps=%d >= 1",
+                fn, iters, max_swaps, max_sweeps);
+  if (L > kLayoutMaxDevices || I > kLayoutMaxNpt * 1024 ||
+      neuron_step_lds_bytes(I, L) > kLayoutMaxLds)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: I=%d, L=%d outside the neuron step's limits", fn, I, L);
+  if (N > max_objective_layers())
+    return fail(HNA_ERR_UNSUPPORTED, "%s: N=%d exceeds %d layers", fn, N, max_objective_layers());
+  REQUIRE_PTR(S_up_hat);
+  if (N > 1) REQUIRE_PTR(S_down_hat);
+  REQUIRE_PTR(head_device);
+  REQUIRE_PTR(neuron_device);
+  REQUIRE_PTR(neuron_stats);
+  REQUIRE_PTR(workspace);
+  if (!J_history || !n_sweeps)
+    return fail(HNA_ERR_INVALID_ARG, "%s: J_history and n_sweeps are required host pointers", fn);
+  const SearchWorkspace wl = search_workspace(N, G, I);
+  if (workspace_bytes < wl.total)
+    return fail(HNA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, wl.total);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* h_new = reinterpret_cast<int32_t*>(ws + wl.heads);
+  int32_t* nu_new = reinterpret_cast<int32_t*>(ws + wl.neurons);
+  int32_t* st_new = reinterpret_cast<int32_t*>(ws + wl.stats);
+  double* hscore = reinterpret_cast<double*>(ws + wl.hscore);
+  int32_t* hstatus = reinterpret_cast<int32_t*>(ws + wl.hstatus);
+  double* fu = reinterpret_cast<double*>(ws + wl.frac_up);
+  double* fd = reinterpret_cast<double*>(ws + wl.frac_down);
+  double* Jd = reinterpret_cast<double*>(ws + wl.J);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int parts = (int)partition_count(G, L);
+
+  *n_sweeps = 0;
+  double bestJ = 0.0;
+  std::vector<int32_t> hst(N), nst((size_t)N * 4);
+  for (int s = 0; s < max_sweeps; ++s) {
+    // neuron step from the kept heads, head step from the new neurons, then J
+    NeuronStepParams np{S_up_hat, S_down_hat, head_device, nu_new, st_new,
+                        N, G, I, L, iters, max_swaps};
+    hipError_t e = launch_neuron_step(np, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    HeadStepParams hp{S_up_hat, S_down_hat, nu_new, h_new, hscore, hstatus, N, G, I, L, parts};
+    e = launch_head_step(hp, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_layout_objective(S_up_hat, S_down_hat, h_new, nu_new, N, G, I, fu, fd, Jd, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    double J = 0.0;
+    if ((e = hipMemcpyAsync(&J, Jd, sizeof(double), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(nst.data(), st_new, nst.size() * 4, hipMemcpyDeviceToHost, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(hst.data(), hstatus, hst.size() * 4, hipMemcpyDeviceToHost, st)) !=
+            hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess)
+      return hip_fail(e, fn);
+    for (int i = 0; i < N; ++i) {
+      const int ns = nst[(size_t)i * 4];
+      if (ns == HNA_LAYOUT_BAD_HEADS)
+        return fail(HNA_ERR_INVALID_ARG, "%s: head devices of layer %d or %d outside [0, %d)", fn,
+                    i, i + 1 < N ? i + 1 : i, L);
+      if (ns == HNA_LAYOUT_NO_MOVE || hst[i] != HNA_LAYOUT_OK)
+        return fail(HNA_ERR_INVALID_ARG, "%s: layer %d: non-finite scores", fn, i);
+    }
+    J_history[s] = J;
+    *n_sweeps = s + 1;
+    if (s > 0 && !(J > bestJ)) break;
+    bestJ = J;
+    if ((e = hipMemcpyAsync(head_device, h_new, (size_t)N * G * 4, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(neuron_device, nu_new, (size_t)N * I * 4, hipMemcpyDeviceToDevice,
+                            st)) != hipSuccess ||
+        (e = hipMemcpyAsync(neuron_stats, st_new, (size_t)N * 16, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess)
+      return hip_fail(e, fn);
+  }
+  return finish(hipSuccess, st, fn);
 }
 
 }  // extern "C"

@@ -167,6 +167,22 @@ struct NeuronStepParams {
 size_t neuron_step_lds_bytes(int I, int L);
 hipError_t launch_neuron_step(const NeuronStepParams& p, hipStream_t st);
 
+// head step: G <= 16 groups, at most 2^24 balanced partitions
+constexpr int kHeadMaxGroups = 16;
+constexpr int kHeadMaxParts = 1 << 24;
+enum { kLayoutBadNeurons = 4 };
+struct HeadStepParams {
+  const float* S_up;       // [N][G][I]
+  const float* S_down;     // [N-1][I][G]
+  const int32_t* neurons;  // [N][I], devices 0..L-1
+  int32_t* heads;          // [N][G] out
+  double* score;           // [N] out: the best partition's score
+  int32_t* status;         // [N] out
+  int N, G, I, L;
+  int n_parts;             // G! / ((G/L)!)^L
+};
+hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st);
+
 // ------------------------------------------------------ scaled NT GEMM (MFMA)
 // C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] and Y [N, K] row-major with
 // c contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a

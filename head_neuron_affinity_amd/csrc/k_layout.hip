@@ -18,6 +18,8 @@
 //     that loses least (ties: lowest neuron, then lowest device);
 //   * a swap round performs the best swap over device pairs l1 < l2 if it
 //     gains (ties: first pair, lowest neurons).
+// The head step (given nu_{i-1} and nu_i, the best balanced KV-group map h_i
+// by exhaustive scoring of the labelled balanced partitions) is here too.
 #include <climits>
 #include <cmath>
 
@@ -421,7 +423,173 @@ __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams
   }
 }
 
+// ---------------------------------------------------------------- head step
+// One 1024-thread workgroup per layer.  A[g][l] (fp64, LDS): each group is
+// summed by 16/G waves (one for G > 8); each lane adds its strided neurons, up
+// terms then down terms, a fixed butterfly combines the lanes and the waves'
+// parts are added in order.  Every balanced
+// partition is then scored by unranking its lexicographic rank (multiset
+// permutations of G/L copies of each device), the score being
+// sum_g A[g][h(g)] in increasing g; the best (ties: lowest rank) wins.
+__global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) {
+  __shared__ double A[kHeadMaxGroups * kLayoutMaxDevices];
+  __shared__ double Apart[kLWaves * kLayoutMaxDevices];   // per-wave partial sums
+  __shared__ double red_d[kLWaves];
+  __shared__ int red_i[kLWaves];
+  __shared__ int bad;
+
+  const int layer = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int G = p.G, I = p.I, L = p.L;
+  const bool has_prev = layer > 0;
+  const int32_t* nu = p.neurons + (int64_t)layer * I;
+  const int32_t* nu_prev = has_prev ? p.neurons + (int64_t)(layer - 1) * I : nullptr;
+
+  if (t == 0) bad = 0;
+  __syncthreads();
+  for (int k = t; k < I; k += kLThreads) {
+    const int a = nu[k];
+    if (a < 0 || a >= L) bad = 1;
+    if (has_prev) {
+      const int b = nu_prev[k];
+      if (b < 0 || b >= L) bad = 1;
+    }
+  }
+  __syncthreads();
+  if (bad) {
+    if (t < G) p.heads[(int64_t)layer * G + t] = -1;
+    if (t == 0) {
+      p.status[layer] = kLayoutBadNeurons;
+      p.score[layer] = 0.0;
+    }
+    return;
+  }
+
+  // A[g][l]: the waves split into 16/G parts per group (1 for G > 8); part q
+  // of group g takes the neurons q*64 + lane, stepping by parts*64; the parts
+  // are then added in order
+  const float* Su = p.S_up + (int64_t)layer * G * I;
+  const float* Sd = has_prev ? p.S_down + (int64_t)(layer - 1) * I * G : nullptr;
+  const int parts = G <= kLWaves / 2 ? kLWaves / G : 1;
+  for (int wg = w; wg < G * parts; wg += kLWaves) {
+    const int g = wg / parts, q = wg - g * parts;
+    double acc[kLayoutMaxDevices];
+#pragma unroll
+    for (int l = 0; l < kLayoutMaxDevices; ++l) acc[l] = 0.0;
+#pragma unroll 4
+    for (int k = q * 64 + lane; k < I; k += parts * 64) {
+      const double v = (double)Su[(int64_t)g * I + k];
+      const int dv = nu[k];
+#pragma unroll
+      for (int l = 0; l < kLayoutMaxDevices; ++l)
+        if (l == dv) acc[l] += v;
+    }
+    if (has_prev) {
+#pragma unroll 4
+      for (int k = q * 64 + lane; k < I; k += parts * 64) {
+        const double v = (double)Sd[(int64_t)k * G + g];
+        const int dv = nu_prev[k];
+#pragma unroll
+        for (int l = 0; l < kLayoutMaxDevices; ++l)
+          if (l == dv) acc[l] += v;
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < kLayoutMaxDevices; ++l) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc[l] += __shfl_xor(acc[l], o);
+      if (lane == 0 && l < L) Apart[(g * parts + q) * L + l] = acc[l];
+    }
+  }
+  __syncthreads();
+  if (t < G * L) {
+    const int g = t / L, l = t - g * L;
+    double a = Apart[(g * parts) * L + l];
+    for (int q = 1; q < parts; ++q) a += Apart[(g * parts + q) * L + l];
+    A[g * L + l] = a;
+  }
+  __syncthreads();
+
+  // score the partitions r = t, t + 1024, ...  (ranks fit in an int: at most 2^24)
+  const int per = G / L;
+  const double total = (double)p.n_parts;
+  double bd = -INFINITY;
+  int bi = INT_MAX;
+  for (int r0 = t; r0 < p.n_parts; r0 += kLThreads) {
+    int c[kLayoutMaxDevices];
+#pragma unroll
+    for (int l = 0; l < kLayoutMaxDevices; ++l) c[l] = l < L ? per : 0;
+    double r = (double)r0, mc = total, score = 0.0;
+    for (int q = 0; q < G; ++q) {
+      const double n = (double)(G - q);
+      bool done = false;
+#pragma unroll
+      for (int v = 0; v < kLayoutMaxDevices; ++v) {
+        if (!done && c[v] > 0) {
+          // completions with device v at position q: mc * c_v / n, an exact
+          // integer below 2^53, so fp64 holds every step exactly
+          const double sub = mc * (double)c[v] / n;
+          if (r < sub) {
+            score += A[q * L + v];
+            mc = sub;
+            --c[v];
+            done = true;
+          } else {
+            r -= sub;
+          }
+        }
+      }
+    }
+    if (better(score, r0, bd, bi)) {
+      bd = score;
+      bi = r0;
+    }
+  }
+  wave_best(bd, bi);
+  if (lane == 0) {
+    red_d[w] = bd;
+    red_i[w] = bi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int i = 1; i < kLWaves; ++i)
+      if (better(red_d[i], red_i[i], bd, bi)) {
+        bd = red_d[i];
+        bi = red_i[i];
+      }
+    // unrank the winner into the head devices
+    int c[kLayoutMaxDevices];
+#pragma unroll
+    for (int l = 0; l < kLayoutMaxDevices; ++l) c[l] = l < L ? per : 0;
+    double r = (double)bi, mc = total;
+    for (int q = 0; q < G; ++q) {
+      const double n = (double)(G - q);
+      bool done = false;
+#pragma unroll
+      for (int v = 0; v < kLayoutMaxDevices; ++v) {
+        if (!done && c[v] > 0) {
+          const double sub = mc * (double)c[v] / n;
+          if (r < sub) {
+            p.heads[(int64_t)layer * G + q] = v;
+            mc = sub;
+            --c[v];
+            done = true;
+          } else {
+            r -= sub;
+          }
+        }
+      }
+    }
+    p.score[layer] = bd;
+    p.status[layer] = kLayoutOk;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(head_step_kernel, dim3(p.N), dim3(kLThreads), 0, st, p);
+  return hipGetLastError();
+}
 
 size_t neuron_step_lds_bytes(int I, int L) { return (size_t)I * L * sizeof(double); }
 

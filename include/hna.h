@@ -28,7 +28,8 @@
  *     during the call only.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and runs asynchronously; nothing synchronises the host except
- *     when the environment variable HNA_DEBUG_SYNC=1 is set.
+ *     hna_layout_search (once per sweep) and, for every call, the
+ *     environment variable HNA_DEBUG_SYNC=1.
  *   - Every argument is validated on the host before anything is enqueued.
  *     On failure a negative hna_status is returned, a thread-local message
  *     is available from hna_last_error(), and nothing has been launched.
@@ -240,7 +241,8 @@ enum hna_layout_status {
   HNA_LAYOUT_OK = 0,
   HNA_LAYOUT_BAD_HEADS = 1,   /* a head device of layer i or i+1 is outside [0, L) */
   HNA_LAYOUT_SWAP_LIMIT = 2,  /* the swap phase stopped at max_swaps swaps */
-  HNA_LAYOUT_NO_MOVE = 3      /* non-finite gains left the fix-up without a move */
+  HNA_LAYOUT_NO_MOVE = 3,     /* non-finite gains left the fix-up without a move */
+  HNA_LAYOUT_BAD_NEURONS = 4  /* a neuron device of layer i or i-1 is outside [0, L) */
 };
 
 /*
@@ -273,6 +275,62 @@ enum hna_layout_status {
 int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
                     const float* S_down_hat, const int32_t* head_device, int32_t iters,
                     int32_t max_swaps, int32_t* neuron_device, int32_t* stats, void* stream);
+
+/* ---------------------------------------------- head step and the sweeps */
+
+/*
+ * Head step of the layout search (section 3, paragraph "Optimiser"), for
+ * every layer at once, given the neuron devices of all layers:
+ *   A_i[g, l] = sum_{k: nu_i(k) = l} S_up_hat_i[g, k]
+ *             + sum_{k: nu_{i-1}(k) = l} S_down_hat_{i-1}[k, g]   (no down term for i = 0)
+ *   h_i = the balanced map (G/L groups per device) maximising sum_g A_i[g, h_i(g)],
+ * found by scoring all G!/((G/L)!)^L labelled balanced partitions (2520 for
+ * G = 8, L = 4).  Partitions are ranked in lexicographic order of
+ * (h(0), ..., h(G-1)); ties go to the lowest rank.  A_i and the scores are
+ * fp64.  Inputs (device): S_up_hat [N, G, I], S_down_hat [N-1, I, G] fp32
+ * (S_down_hat may be NULL if N == 1), neuron_device int32 [N, I].  Outputs
+ * (device): head_device int32 [N, G]; score fp64 [N], the best partition's
+ * score (the co-located mass layer i's up edge and layer i-1's down edge
+ * get); status int32 [N] (HNA_LAYOUT_OK, or HNA_LAYOUT_BAD_NEURONS with
+ * head_device = -1 when a neuron device of layer i or i-1 is outside
+ * [0, L)).  Limits: 1 <= L <= 8, G <= 16 and at most 2^24 partitions
+ * (HNA_ERR_UNSUPPORTED otherwise), G and I multiples of L.
+ */
+int hna_head_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
+                  const float* S_down_hat, const int32_t* neuron_device, int32_t* head_device,
+                  double* score, int32_t* status, void* stream);
+
+/* Bytes of device workspace hna_layout_search needs (0 for bad sizes). */
+size_t hna_layout_search_workspace_bytes(int32_t N, int32_t G, int32_t I);
+
+/*
+ * The layout search (section 3, paragraph "Optimiser"): coordinate ascent
+ * over the chain of layers.  Each sweep runs hna_neuron_step for every layer
+ * from the kept head devices, then hna_head_step for every layer from the new
+ * neuron devices, then J (eq. 6) of the new layout.  A sweep is kept while J
+ * strictly increases; the first sweep that does not raise J ends the search
+ * and is discarded, as is everything after max_sweeps sweeps.
+ *   head_device   int32 [N, G] device memory: in, the starting head devices
+ *                 (the pages start from the contiguous map g / (G/L)); out,
+ *                 the kept layout's
+ *   neuron_device int32 [N, I] device memory, out: the kept layout's
+ *   neuron_stats  int32 [N, 4] device memory, out: hna_neuron_step's stats of
+ *                 the kept sweep
+ *   J_history     fp64 [max_sweeps] HOST memory, out: J after each sweep run
+ *   n_sweeps      HOST int32, out: sweeps run (the last one is discarded if it
+ *                 did not raise J)
+ *   workspace     device memory of hna_layout_search_workspace_bytes(N, G, I)
+ * iters and max_swaps are passed to hna_neuron_step (the pages: 300).
+ * Unlike the other calls, this one synchronises `stream` once per sweep to
+ * read J.  Head devices outside [0, L) in the starting map return
+ * HNA_ERR_INVALID_ARG.  Limits: those of hna_neuron_step, hna_head_step and
+ * hna_layout_objective.
+ */
+int hna_layout_search(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_hat,
+                      const float* S_down_hat, int32_t iters, int32_t max_swaps,
+                      int32_t max_sweeps, int32_t* head_device, int32_t* neuron_device,
+                      int32_t* neuron_stats, double* J_history, int32_t* n_sweeps,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

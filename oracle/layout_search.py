@@ -1,6 +1,7 @@
-"""Float64 CPU oracle of the neuron step of the layout search: the gain of
+"""Float64 CPU oracle of the layout search: the neuron step (the gain of
 placing each neuron on each device, and the balanced assignment that
-maximises it.
+maximises it), the head step (the best balanced partition of each layer's KV
+groups) and the coordinate-ascent sweeps that alternate them.
 
 TEST INFRASTRUCTURE ONLY (like affinity.py and objective.py): imported by the
 tests, the smoke check and the benchmark's CPU leg, never by the product path;
@@ -43,18 +44,39 @@ Readings where the pages are silent (each one stated where it is used):
 Every decision compares float64 values computed by the operations written
 here, in this order.
 
+Head step.  Given nu_{i-1} and nu_i, putting KV group g of layer i on device
+l gains
+    A[g, l] = sum_{k: nu_i(k) = l} S_hat_up_i[g, k]
+            + sum_{k: nu_{i-1}(k) = l} S_hat_down_{i-1}[k, g]
+(the first layer has no down term), and the best balanced h_i maximises
+sum_g A[g, h_i(g)] over all G! / ((G/L)!)^L labelled balanced partitions,
+scored exhaustively.  Reading: the partitions are taken in lexicographic order
+of (h(0), ..., h(G-1)) and ties go to the first.
+
+Sweeps.  From the contiguous head assignment, one sweep runs the neuron step
+of every layer (the layers are independent given all head devices), then the
+head step of every layer (independent given all neuron devices), then
+evaluates J.  Reading: sweeps continue while J strictly increases; the first
+sweep that does not raise J is discarded and the search returns the layout
+before it (also after max_sweeps sweeps).
+
 Parity status: pinned by tests/test_layout_search_pins.py (the gain against
 the co-located masses of the objective, the assignment against the Hungarian
 solution on replicated slots and against enumeration of every balanced
 assignment on tiny layers, swap-stability by exhaustive pair check, the fix-up
-on tied gains, invariance under device relabelling).
+on tied gains, invariance under device relabelling; the partition count
+2520, the head step against brute force over all L^G maps and against the
+objective's co-located masses, J never falling across sweeps).
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .objective import layout_objective
+
 __all__ = ["neuron_gain", "dual_ascent", "capacity_fixup", "pairwise_swaps", "neuron_step",
-           "neuron_step_stack", "DUAL_ITERS", "DUAL_DECAY", "DUAL_STEP_FRAC"]
+           "neuron_step_stack", "DUAL_ITERS", "DUAL_DECAY", "DUAL_STEP_FRAC",
+           "balanced_partitions", "head_gain", "head_step", "head_step_stack", "layout_search"]
 
 DUAL_ITERS = 300       # appendix A
 DUAL_DECAY = 0.98      # appendix A
@@ -171,3 +193,104 @@ def neuron_step_stack(S_up_hat, S_down_hat, heads, L: int, iters: int = DUAL_ITE
         out.append(a)
         stats.append(st)
     return np.stack(out), np.stack(stats)
+
+
+# ------------------------------------------------------------------ head step
+def balanced_partitions(G: int, L: int) -> np.ndarray:
+    """All maps {0..G-1} -> {0..L-1} with G/L groups per device, [P, G], in
+    lexicographic order (built device by device, smallest first)."""
+    per = G // L
+    out = []
+
+    def rec(prefix, left):
+        if len(prefix) == G:
+            out.append(list(prefix))
+            return
+        for v in range(L):
+            if left[v]:
+                left[v] -= 1
+                prefix.append(v)
+                rec(prefix, left)
+                prefix.pop()
+                left[v] += 1
+
+    rec([], [per] * L)
+    return np.array(out, dtype=np.int64).reshape(-1, G)
+
+
+def head_gain(S_up_hat, S_down_prev, neurons, neurons_prev, L: int) -> np.ndarray:
+    """A [G, L] float64.  S_up_hat [G, I] of layer i; S_down_prev [I, G] of
+    layer i-1 (None for the first layer) with that layer's neuron devices."""
+    S_up_hat = np.asarray(S_up_hat, dtype=np.float64)
+    G = S_up_hat.shape[0]
+    A = np.zeros((G, L), dtype=np.float64)
+    for l in range(L):
+        A[:, l] = S_up_hat[:, np.asarray(neurons) == l].sum(axis=1)
+        if S_down_prev is not None:
+            A[:, l] += np.asarray(S_down_prev, dtype=np.float64)[np.asarray(neurons_prev) == l].sum(axis=0)
+    return A
+
+
+def head_step(S_up_hat, S_down_prev, neurons, neurons_prev, L: int):
+    """Best balanced head map of one layer by exhaustive scoring.
+
+    Returns (h [G] int32, best score, second-best score (-inf if only one))."""
+    A = head_gain(S_up_hat, S_down_prev, neurons, neurons_prev, L)
+    G = A.shape[0]
+    parts = balanced_partitions(G, L)
+    scores = A[np.arange(G)[None, :], parts].sum(axis=1)
+    best = int(np.argmax(scores))                   # first maximum in lexicographic order
+    rest = np.delete(scores, best)
+    second = float(rest.max()) if rest.size else -np.inf
+    return parts[best].astype(np.int32), float(scores[best]), second
+
+
+def head_step_stack(S_up_hat, S_down_hat, neurons, L: int):
+    """The head step of every layer given all neuron devices.
+
+    Returns (heads [N, G] int32, scores [N], second-best scores [N])."""
+    N = len(S_up_hat)
+    hs, sc, sec = [], [], []
+    for i in range(N):
+        prev = S_down_hat[i - 1] if i > 0 else None
+        nprev = neurons[i - 1] if i > 0 else None
+        h, b, s2 = head_step(S_up_hat[i], prev, neurons[i], nprev, L)
+        hs.append(h)
+        sc.append(b)
+        sec.append(s2)
+    return np.stack(hs), np.array(sc), np.array(sec)
+
+
+# --------------------------------------------------------------------- sweeps
+def layout_search(S_up_hat, S_down_hat, L: int, heads0=None, iters: int = DUAL_ITERS,
+                  max_swaps: int | None = None, max_sweeps: int = 16):
+    """Coordinate ascent over the chain of layers.
+
+    Returns a dict: heads [N, G], neurons [N, I] (the best layout), J (its
+    objective), J_history (J after every sweep run, the last one possibly not
+    kept), sweeps (the number run), head_margin (the smallest relative gap
+    between the best and second-best head partition over all head steps of
+    the kept sweeps), neuron_stats [N, 4] of the last kept sweep."""
+    S_up_hat = np.asarray(S_up_hat)
+    N, G, I = S_up_hat.shape
+    if heads0 is None:
+        heads0 = np.tile(np.arange(G) // (G // L), (N, 1))
+    heads = np.asarray(heads0, dtype=np.int64)
+    best = None
+    history = []
+    margin = np.inf
+    for _ in range(max_sweeps):
+        nu, stats = neuron_step_stack(S_up_hat, S_down_hat, heads, L, iters, max_swaps)
+        h_new, sc, sec = head_step_stack(S_up_hat, S_down_hat, nu, L)
+        J, _, _ = layout_objective(S_up_hat, S_down_hat, h_new, nu)
+        history.append(J)
+        if best is not None and not J > best["J"]:
+            break
+        gap = np.min((sc - sec) / np.maximum(np.abs(sc), 1e-300))
+        best = {"heads": h_new, "neurons": nu, "J": J, "neuron_stats": stats,
+                "head_margin": min(margin, gap)}
+        margin = best["head_margin"]
+        heads = h_new
+    best["J_history"] = np.array(history)
+    best["sweeps"] = len(history)
+    return best

@@ -257,6 +257,45 @@ def test_neuron_step_validates():
     assert ok
 
 
+def test_head_step_and_search_validate():
+    hna = _lib()
+    L = hna.lib()
+    F = ctypes.c_void_p(FAKE)
+    hs = L.hna_head_step
+
+    def head(N=3, G=8, I=3072, Ld=4, up=F, down=F, nu=F, out=F, sc=F, st=F):
+        return hs(N, G, I, Ld, up, down, nu, out, sc, st, None)
+
+    assert head(N=0) == -1
+    assert head(G=6) == -1                  # G not a multiple of L
+    assert head(G=32, Ld=4) == -2           # more than 16 groups
+    assert head(G=16, Ld=4) == -2           # 63,063,000 partitions > 2^24
+    assert head(Ld=16, G=16, I=1024) == -2  # more than 8 devices
+    assert head(up=None) == -1
+    assert head(down=None) == -1
+    assert head(N=1, down=None, sc=ctypes.c_void_p(MIS)) == -3
+    assert head(st=None) == -1
+    assert L.hna_layout_search_workspace_bytes(0, 8, 64) == 0
+    need = L.hna_layout_search_workspace_bytes(3, 8, 3072)
+    assert need >= 3 * 8 * 4 + 3 * 3072 * 4 + 3 * 16
+    hist = (ctypes.c_double * 4)()
+    n = ctypes.c_int32(0)
+    ls = L.hna_layout_search
+
+    def search(N=3, G=8, I=3072, Ld=4, iters=300, ms=100, sweeps=4, h=hist, nn=ctypes.byref(n),
+               ws=F, wsb=need):
+        return ls(N, G, I, Ld, F, F, iters, ms, sweeps, F, F, F, h, nn, ws, wsb, None)
+
+    assert search(sweeps=0) == -1
+    assert search(iters=-1) == -1
+    assert search(G=16) == -2
+    assert search(Ld=8, I=4096) == -2       # the neuron step's LDS limit
+    assert search(h=None) == -1
+    assert search(nn=None) == -1
+    assert search(ws=None) == -1
+    assert search(wsb=need - 1) == -4
+
+
 def test_error_text_is_thread_local():
     hna = _lib()
     call_up(hna, dims(hna, d=20))

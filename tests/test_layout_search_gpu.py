@@ -118,3 +118,104 @@ def test_full_stack_determinism_and_objective(hna):
                                     torch.from_numpy(heads).cuda(), torch.from_numpy(nu).cuda())
     print(f"  J contiguous {float(J0.cpu()[0]):.4f} -> neuron step {float(J1.cpu()[0]):.4f}", flush=True)
     assert float(J1.cpu()[0]) > float(J0.cpu()[0])
+
+
+# ------------------------------------------------------------------ head step
+def oracle_head_check(up, down, nu, L, heads, score):
+    """GPU head maps against the oracle: the best score to 1e-12 (relative);
+    the map itself where the best partition is unique beyond rounding,
+    otherwise the GPU's map must score within 1e-12 of the best."""
+    N = up.shape[0]
+    for i in range(N):
+        prev, nprev = (down[i - 1], nu[i - 1]) if i else (None, None)
+        h, best, second = oracle.head_step(up[i], prev, nu[i], nprev, L)
+        assert abs(score[i] - best) <= 1e-12 * abs(best)
+        if best - second > 1e-12 * abs(best):
+            assert np.array_equal(heads[i], h), i
+        else:
+            A = oracle.head_gain(up[i], prev, nu[i], nprev, L)
+            assert abs(A[np.arange(len(h)), heads[i]].sum() - best) <= 1e-12 * abs(best)
+            assert np.all(np.bincount(heads[i], minlength=L) == len(h) // L)
+
+
+@pytest.mark.parametrize("N,G,I,L,seed", [
+    (4, 8, 3072, 4, 20),    # 2520 partitions, the pages' count
+    (3, 8, 1000, 4, 21),
+    (2, 16, 512, 2, 22),    # 12870 partitions
+    (2, 8, 512, 8, 23),     # 40320 partitions
+    (2, 12, 600, 4, 24),    # 369600 partitions: many per thread
+    (1, 8, 512, 4, 25),     # one layer: no down term
+    (3, 4, 100, 1, 26),     # one device: a single partition
+])
+def test_head_step_matches_oracle(hna, N, G, I, L, seed):
+    up, down = unit_stack(N, G, I, seed)
+    _, nu = synth.random_balanced_layout(N, G, I, L, seed)
+    nu = nu.numpy()
+    heads, score, status = hna.head_step(torch.from_numpy(up).cuda(),
+                                         torch.from_numpy(down).cuda() if N > 1 else None,
+                                         torch.from_numpy(nu).cuda(), L)
+    torch.cuda.synchronize()
+    heads, score, status = heads.cpu().numpy(), score.cpu().numpy(), status.cpu().numpy()
+    print(f"  N={N} G={G} I={I} L={L}: scores {np.round(score, 4).tolist()}", flush=True)
+    assert np.all(status == 0)
+    oracle_head_check(up, down, nu, L, heads, score)
+
+
+def test_head_step_bad_neuron_devices(hna):
+    N, G, I, L = 4, 8, 256, 4
+    up, down = unit_stack(N, G, I, seed=27)
+    nu = synth.random_balanced_layout(N, G, I, L, seed=27)[1].numpy().copy()
+    nu[1, 5] = -3                       # layers 1 and 2 read layer 1's neuron devices
+    heads, score, status = hna.head_step(torch.from_numpy(up).cuda(), torch.from_numpy(down).cuda(),
+                                         torch.from_numpy(nu).cuda(), L)
+    torch.cuda.synchronize()
+    heads, status = heads.cpu().numpy(), status.cpu().numpy()
+    assert status.tolist() == [0, 4, 4, 0]
+    assert np.all(heads[1:3] == -1)
+    for i in (0, 3):
+        h, _, _ = oracle.head_step(up[i], down[i - 1] if i else None, nu[i], nu[i - 1] if i else None, L)
+        assert np.array_equal(heads[i], h)
+
+
+# --------------------------------------------------------------------- sweeps
+def run_search(hna, up, down, L, heads0=None):
+    r = hna.layout_search(torch.from_numpy(up).cuda(), torch.from_numpy(down).cuda(), L,
+                          head_device=None if heads0 is None else torch.from_numpy(heads0).cuda())
+    torch.cuda.synchronize()
+    return r
+
+
+def check_search(hna, up, down, L, heads0=None):
+    r = run_search(hna, up, down, L, heads0)
+    ref = oracle.layout_search(up, down, L, heads0=heads0)
+    print(f"  J {np.round(r['J_history'], 6).tolist()} vs {np.round(ref['J_history'], 6).tolist()}, "
+          f"sweeps {r['sweeps']} vs {ref['sweeps']}, head margin {ref['head_margin']:.2e}", flush=True)
+    assert ref["head_margin"] > 1e-9       # every head decision is unique beyond rounding
+    assert r["sweeps"] == ref["sweeps"]
+    assert np.allclose(r["J_history"], ref["J_history"], rtol=0, atol=1e-9)
+    assert np.array_equal(r["heads"].cpu().numpy(), ref["heads"])
+    assert np.array_equal(r["neurons"].cpu().numpy(), ref["neurons"])
+    assert np.array_equal(r["neuron_stats"].cpu().numpy(), ref["neuron_stats"])
+    return r, ref
+
+
+def test_search_from_contiguous_heads_full_stack(hna):
+    # the 28-layer Qwen3-0.6B stack on 4 devices, as the pages start it
+    up, down = unit_stack(28, 8, 3072, seed=30)
+    r, _ = check_search(hna, up, down, 4)
+    assert 2 <= r["sweeps"] <= 4
+
+
+def test_search_from_random_heads(hna):
+    N, G, I, L = 6, 8, 512, 4
+    up, down = unit_stack(N, G, I, seed=31)
+    heads0 = synth.random_balanced_layout(N, G, I, L, seed=31)[0].numpy()
+    check_search(hna, up, down, L, heads0)
+
+
+def test_search_rejects_bad_start(hna):
+    up, down = unit_stack(3, 8, 256, seed=32)
+    heads0 = synth.contiguous_layout(3, 8, 256, 4)[0].numpy().copy()
+    heads0[2, 0] = 9
+    with pytest.raises(hna.HnaError):
+        run_search(hna, up, down, 4, heads0)

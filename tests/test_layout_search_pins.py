@@ -140,3 +140,64 @@ def test_stack_step_does_not_lower_the_objective():
     assert J1 >= J0 and np.all(stats[:, 0] == 0)
     for i in range(N):
         assert np.array_equal(np.bincount(nu[i], minlength=L), np.full(L, I // L))
+
+
+# ------------------------------------------------------------------ head step
+def test_partition_count_and_order():
+    # the pages count G!/((G/L)!)^L = 2520 labelled balanced partitions for G = 8, L = 4
+    import math
+    for G, L in [(8, 4), (6, 3), (4, 2), (8, 2), (8, 8), (4, 1)]:
+        P = oracle.balanced_partitions(G, L)
+        assert len(P) == math.factorial(G) // math.factorial(G // L) ** L
+        assert np.all(np.stack([np.bincount(p, minlength=L) for p in P]) == G // L)
+        assert len({tuple(p) for p in P}) == len(P)
+        keys = [tuple(p) for p in P]
+        assert keys == sorted(keys)
+    assert len(oracle.balanced_partitions(8, 4)) == 2520
+
+
+def test_head_step_against_brute_force_objective():
+    # every map {0..G-1} -> {0..L-1} is tried; a balanced one's score is the
+    # co-located mass it gives layer i's up edge and layer i-1's down edge, as
+    # the objective measures them
+    N, G, I, L = 3, 8, 96, 4
+    up, down = unit_stack(N, G, I, seed=13, dtype=np.float64)
+    heads, neurons = (t.numpy() for t in synth.random_balanced_layout(N, G, I, L, seed=13))
+    for i in (0, 1, 2):
+        h, best, second = oracle.head_step(up[i], down[i - 1] if i else None, neurons[i],
+                                           neurons[i - 1] if i else None, L)
+        top = -1.0
+        for cand in itertools.product(range(L), repeat=G):
+            cand = np.array(cand)
+            if np.any(np.bincount(cand, minlength=L) != G // L):
+                continue
+            hh = heads.copy()
+            hh[i] = cand
+            _, fu, fd = oracle.layout_objective(up, down, hh, neurons)
+            top = max(top, fu[i] + (fd[i - 1] if i else 0.0))
+        assert abs(best - top) < 1e-12 and second <= best
+        hh = heads.copy()
+        hh[i] = h
+        _, fu, fd = oracle.layout_objective(up, down, hh, neurons)
+        assert abs(fu[i] + (fd[i - 1] if i else 0.0) - best) < 1e-12
+
+
+def test_sweeps_raise_the_objective_and_stop():
+    N, G, I, L = 6, 8, 512, 4
+    up, down = unit_stack(N, G, I, seed=14)
+    res = oracle.layout_search(up, down, L)
+    hist = res["J_history"]
+    kept = hist[:-1] if len(hist) > 1 and not hist[-1] > hist[-2] else hist
+    assert np.all(np.diff(kept) > 0)                  # every kept sweep raised J
+    assert res["J"] == kept[-1]
+    assert 1 <= res["sweeps"] <= 16
+    heads0, nu0 = (t.numpy() for t in synth.contiguous_layout(N, G, I, L))
+    J0, _, _ = oracle.layout_objective(up, down, heads0, nu0)
+    assert res["J"] > J0
+    assert 0 <= res["J"] <= 2 * N - 1
+    for i in range(N):
+        assert np.all(np.bincount(res["heads"][i], minlength=L) == G // L)
+        assert np.all(np.bincount(res["neurons"][i], minlength=L) == I // L)
+    # the reported J is the objective of the returned layout
+    J, _, _ = oracle.layout_objective(up, down, res["heads"], res["neurons"])
+    assert abs(J - res["J"]) < 1e-12
