@@ -115,7 +115,8 @@ def _randn(gen: torch.Generator, shape, device) -> torch.Tensor:
 
 
 def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = True,
-               token_chunk: int = 8192, return_resid: bool = False) -> Dict[str, torch.Tensor]:
+               token_chunk: int = 8192, return_resid: bool = False,
+               with_x: bool = False) -> Dict[str, torch.Tensor]:
     """Draw one synthetic layer.
 
     Returns a dict of tensors on ``device``.  Matrices use the (out, in)
@@ -124,6 +125,9 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
     "f64"), group_of_head is int32 on the CPU.  With ``return_resid`` the
     float64 residuals x (entering the FFN norm) and x_next (entering the next
     layer's norm) are returned too, for forward-pass checks on small layers.
+    With ``with_x`` the residual entering the FFN norm is returned as "x_in",
+    rounded to float32 (float64 for "f64"): the input of the leave-one-out
+    score, which renormalises the residual without a head.
     """
     device = torch.device(device)
     T, D, H, G, d, I = shape.T, shape.hidden, shape.H, shape.G, shape.d, shape.I
@@ -157,6 +161,7 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
     r_out = torch.empty((T,), dtype=scal_dt, device=device)
     rn_out = torch.empty((T,), dtype=scal_dt, device=device) if with_next else None
     x_keep, xn_keep = [], []
+    x_in = torch.empty((T, D), dtype=scal_dt, device=device) if with_x else None
     a_flat = a.reshape(T, H * d)
     for t0 in range(0, T, token_chunk):
         t1 = min(T, t0 + token_chunk)
@@ -177,6 +182,8 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
                 xn_keep.append(xn)
         if return_resid:
             x_keep.append(x)
+        if with_x:
+            x_in[t0:t1] = x.to(scal_dt)
         del x, y, g, u
 
     layer = {
@@ -193,6 +200,8 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
             "W_v": nxt["W_v"].to(out_dt), "gamma_next": nxt["gamma_next"].to(scal_dt),
             "group_of_head_next": default_group_map(H, G),
         })
+    if with_x:
+        layer["x_in"] = x_in
     if return_resid:
         layer["x"] = torch.cat(x_keep)
         if with_next:
@@ -202,14 +211,15 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
 
 def make_config_layer(config: int, layer: int = 0, T: Optional[int] = None,
                       device="cpu", dtype: Optional[str] = None,
-                      with_next: bool = True) -> Dict[str, torch.Tensor]:
+                      with_next: bool = True, with_x: bool = False) -> Dict[str, torch.Tensor]:
     """Layer ``layer`` of workload ``config`` (optionally with T or dtype overridden)."""
     sh = layer_shape(config)
     if T is not None:
         sh = sh.with_tokens(T)
     if dtype is not None:
         sh = sh.with_dtype(dtype)
-    return make_layer(sh, layer_seed(config, layer), device=device, with_next=with_next)
+    return make_layer(sh, layer_seed(config, layer), device=device, with_next=with_next,
+                      with_x=with_x)
 
 
 # ---------------------------------------------------------------------------
