@@ -212,6 +212,34 @@ def search_bench(hna, reps: int):
                                    "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
 
 
+def loo_bench(hna, layer, P, grp, reps: int):
+    """The exact leave-one-out score on the benchmark layer (folded weights
+    already in P.M): average hna_affinity_loo duration over `reps` calls, HIP
+    events on the launch stream.  Algorithmic MFMA work: the contraction
+    a_h . M_h (4 T H d I) plus the head writes W_o^(h) a_h for the moments
+    (2 T H d hidden)."""
+    import torch
+    T, H, d = layer["a"].shape
+    I, D = layer["W_gate"].shape
+    for _ in range(2):
+        P.loo(layer, grp)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        P.loo(layer, grp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * T * H * d * I + 2.0 * T * H * d * D
+    tf = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if layer["a"].dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+    return {"workload": f"same layer, T={T}", "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                         "frac": tf / peak, "traffic": None}}
+
+
 def build_inputs(config: int, T=None):
     import synth
     return synth.make_config_layer(config, T=T, device="cuda")
@@ -245,7 +273,8 @@ def main():
     if args.tokens:
         shape = shape.with_tokens(args.tokens)
     n_layers = shape.layers
-    layers = [synth.make_config_layer(args.config, layer=i, T=args.tokens, device="cuda")
+    layers = [synth.make_config_layer(args.config, layer=i, T=args.tokens, device="cuda",
+                                      with_x=(i == 0))
               for i in range(n_layers)]
     torch.cuda.synchronize()
     L0 = layers[0]
@@ -304,6 +333,7 @@ def main():
         "mfma_frac_whole_step": flops_hot * n_layers / (ms_step * 1e-3) / 1e12 / peak,
         "hot_stream_gbs": stream_bytes / (hot_ms * 1e-3) / 1e9,
     }
+    rec["loo"] = loo_bench(hna, L0, passes[0], grps[0], 5)
     rec["objective"] = objective_bench(hna, 200)
     rec["neuron_step"] = neuron_step_bench(hna, 20)
     rec["layout_search"] = search_bench(hna, 50)

@@ -10,7 +10,8 @@ from ._binding import (HnaError, HNA_BF16, HNA_F32, HNA_ACCUMULATE, hna_dims, hn
                        affinity_up, affinity_add, finalize_up, down_weight_norms, down_combine,
                        up_workspace_bytes, down_workspace_bytes, folded_bytes, status_string,
                        last_error, unit_mass, layout_objective, neuron_step,
-                       head_step, layout_search, DUAL_ITERS)
+                       head_step, layout_search, DUAL_ITERS, loo_workspace_bytes,
+                       affinity_loo)
 from .pipeline import AffinityPass, pass_for_layer, affinity_layer
 
 __all__ = [
@@ -19,5 +20,6 @@ __all__ = [
     "finalize_up", "down_weight_norms", "down_combine", "up_workspace_bytes",
     "down_workspace_bytes", "folded_bytes", "status_string", "last_error", "AffinityPass",
     "pass_for_layer", "affinity_layer", "unit_mass", "layout_objective",
-    "neuron_step", "head_step", "layout_search", "DUAL_ITERS",
+    "neuron_step", "head_step", "layout_search", "DUAL_ITERS", "loo_workspace_bytes",
+    "affinity_loo",
 ]

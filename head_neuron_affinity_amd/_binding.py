@@ -39,7 +39,8 @@ EXPORTED = [
     "hna_up_workspace_bytes", "hna_affinity_up", "hna_affinity_add", "hna_finalize_up",
     "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine", "hna_unit_mass",
     "hna_layout_objective", "hna_neuron_step", "hna_head_step",
-    "hna_layout_search_workspace_bytes", "hna_layout_search",
+    "hna_layout_search_workspace_bytes", "hna_layout_search", "hna_loo_workspace_bytes",
+    "hna_affinity_loo",
 ]
 
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         "hna_neuron_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp]),
         "hna_head_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
         "hna_layout_search_workspace_bytes": (sz, [i32, i32, i32]),
+        "hna_loo_workspace_bytes": (sz, [dp]),
+        "hna_affinity_loo": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, ip, f32, vp, vp, sz, vp]),
         "hna_layout_search": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                                               ctypes.POINTER(ctypes.c_double), ip, vp, sz, vp]),
     }
@@ -403,3 +406,29 @@ def layout_search(S_up_hat: torch.Tensor, S_down_hat: Optional[torch.Tensor], L:
            "hna_layout_search")
     return {"heads": head_device, "neurons": neurons, "neuron_stats": stats,
             "J_history": [hist[i] for i in range(n.value)], "sweeps": n.value}
+
+
+# -------------------------------------------------- exact leave-one-out score
+def loo_workspace_bytes(dims: hna_dims) -> int:
+    return int(lib().hna_loo_workspace_bytes(ctypes.byref(dims)))
+
+
+def affinity_loo(dims: hna_dims, a, g, u, x, W_o, M, group_of_head, scale: float,
+                 S_loo: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S_loo [G, I] fp32: the exact leave-one-out score (section 3, "Affinity scores")."""
+    _need_cuda(a, g, u, x, W_o, M)
+    if x.dtype != torch.float32:
+        raise ValueError("x must be fp32")
+    L = lib()
+    dev = M.device
+    if S_loo is None:
+        S_loo = torch.empty((dims.G, dims.I), dtype=torch.float32, device=dev)
+    wsb = L.hna_loo_workspace_bytes(ctypes.byref(dims))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(L.hna_affinity_loo(ctypes.byref(dims), _ptr(a), _ptr(g), _ptr(u), _ptr(x), _ptr(W_o),
+                              _ptr(M), _map(group_of_head), float(scale), _ptr(S_loo),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(dev)), "hna_affinity_loo")
+    return S_loo

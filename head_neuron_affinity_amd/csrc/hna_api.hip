@@ -508,6 +508,23 @@ int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_u
 
 namespace {
 
+struct LooWorkspace {
+  size_t xx, mom, coef, part, total;
+  int n_nt;
+};
+LooWorkspace loo_workspace(const hna_dims* dm) {
+  const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  LooWorkspace w;
+  w.n_nt = (dm->hidden + 127) / 128;
+  size_t o = 0;
+  w.xx = o;   o += align256((size_t)dm->T * sizeof(float));
+  w.mom = o;  o += align256((size_t)w.n_nt * dm->H * 2 * dm->T * sizeof(float));
+  w.coef = o; o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
+  w.part = o; o += align256((size_t)geo.n_chunks * dm->G * geo.I32 * sizeof(float));
+  w.total = o;
+  return w;
+}
+
 // G! / ((G/L)!)^L, or -1 above kHeadMaxParts
 long long partition_count(int G, int L) {
   // multiply in the multinomial one factor at a time: C(n, per) for each device
@@ -581,6 +598,89 @@ int hna_head_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_up_
                    N, G, I, L, (int)partition_count(G, L)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   return finish(launch_head_step(p, st), st, fn);
+}
+
+size_t hna_loo_workspace_bytes(const hna_dims* dm) {
+  if (check_dims("hna_loo_workspace_bytes", dm)) return 0;
+  return loo_workspace(dm).total;
+}
+
+int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const void* u,
+                     const float* x, const void* W_o, const void* M,
+                     const int32_t* group_of_head, float scale, float* S_loo, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const char* fn = "hna_affinity_loo";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  rc = check_map(fn, group_of_head, dm->H, dm->G);
+  if (rc) return rc;
+  const size_t lds = loo_lds_bytes(dm->H, dm->G, dm->d, dm->dtype);
+  if (lds > (size_t)kLdsBytes)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: needs %zu bytes of LDS (H=%d, G=%d, d=%d) > %d", fn,
+                lds, dm->H, dm->G, dm->d, kLdsBytes);
+  REQUIRE_PTR(M);
+  REQUIRE_PTR(S_loo);
+  REQUIRE_PTR(workspace);
+  const LooWorkspace wl = loo_workspace(dm);
+  if (workspace_bytes < wl.total)
+    return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes,
+                wl.total);
+  if (dm->T > 0) {
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(g);
+    REQUIRE_PTR(u);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(W_o);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* xx = reinterpret_cast<float*>(ws + wl.xx);
+  float* mom = reinterpret_cast<float*>(ws + wl.mom);
+  float2* coef = reinterpret_cast<float2*>(ws + wl.coef);
+  float* part = reinterpret_cast<float*>(ws + wl.part);
+  const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  hipError_t e;
+  if (dm->T > 0) {
+    // 1. |x|^2 and the moments x . o_h, |o_h|^2;  2. alpha, beta per (token, head)
+    if ((e = launch_x_sqnorm(x, dm->T, dm->hidden, xx, st)) != hipSuccess) return hip_fail(e, fn);
+    MomentParams mp{a, W_o, x, mom, dm->T, dm->H, dm->d, dm->hidden,
+                    (int)((dm->T + 127) / 128), wl.n_nt};
+    if ((e = launch_head_moments(mp, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
+    if ((e = launch_loo_coef(mom, xx, dm->T, dm->H, wl.n_nt, dm->hidden, coef, st)) != hipSuccess)
+      return hip_fail(e, fn);
+    // 3. the contraction with the exact epilogue, per token chunk
+    LooParams p{};
+    p.a = a;
+    p.g = g;
+    p.u = u;
+    p.coef = coef;
+    p.M = M;
+    p.part = part;
+    p.T = dm->T;
+    p.H = dm->H;
+    p.G = dm->G;
+    p.d = dm->d;
+    p.I = dm->I;
+    p.I32 = geo.I32;
+    p.n_tt = geo.n_tt;
+    p.n_kt = geo.n_kt;
+    p.n_chunks = geo.n_chunks;
+    p.n_ktg = geo.n_ktg;
+    p.n_st = geo.n_st;
+    int n = 0;
+    for (int gg = 0; gg < dm->G; ++gg)
+      for (int h = 0; h < dm->H; ++h)
+        if (group_of_head[h] == gg) {
+          p.head_order[n] = (int8_t)h;
+          p.head_group[n] = (int8_t)gg;
+          ++n;
+        }
+    if ((e = launch_loo(p, lds, geo.grid, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
+  }
+  // 4. fixed-order sum over the token chunks (zeros for T = 0)
+  return finish(launch_finalize_loo(part, dm->T > 0 ? geo.n_chunks : 0, dm->G, dm->I, geo.I32,
+                                    scale, S_loo, st),
+                st, fn);
 }
 
 size_t hna_layout_search_workspace_bytes(int32_t N, int32_t G, int32_t I) {

@@ -203,6 +203,40 @@ struct GemmParams {
   float* seg_part;     // [n_seg][Mrows]
   int H_next, G_next, d_next;
 };
+// Leave-one-out moments: part[(nt*H + h)*2 + 0][t] and [..+1][t] hold the
+// n-tile nt parts of x_t . o_th and |o_th|^2, o_th = W_o^(h) a_th.
+struct MomentParams {
+  const void* a;       // [T, H, d]
+  const void* W_o;     // [hidden, H*d]
+  const float* x;      // [T, hidden] residual entering the FFN pre-norm
+  float* part;         // [n_nt][H][2][T]
+  int64_t T;
+  int H, d, hidden, n_mt, n_nt;
+};
+hipError_t launch_head_moments(const MomentParams& p, int dtype, hipStream_t st);
+
+// The leave-one-out pass (same work decomposition as the first-order pass).
+struct LooParams {
+  const void* a;
+  const void* g;
+  const void* u;
+  const float2* coef;     // [T][H]: alpha = 1 - r/r_h, beta = 1/r_h
+  const void* M;
+  float* part;            // [n_chunks][G][I32]
+  int64_t T;
+  int H, G, d, I, I32;
+  int n_tt, n_kt, n_chunks, n_ktg, n_st;
+  int8_t head_order[kMaxHeads];
+  int8_t head_group[kMaxHeads];
+};
+size_t loo_lds_bytes(int H, int G, int d, int dtype);
+hipError_t launch_x_sqnorm(const float* x, int64_t T, int D, float* xx, hipStream_t st);
+hipError_t launch_loo_coef(const float* part, const float* xx, int64_t T, int H, int n_nt, int D,
+                           float2* coef, hipStream_t st);
+hipError_t launch_loo(const LooParams& p, size_t lds, int grid, int dtype, hipStream_t st);
+hipError_t launch_finalize_loo(const float* part, int n_chunks, int G, int I, int I32,
+                               float scale, float* S_loo, hipStream_t st);
+
 hipError_t launch_scale_transpose(const void* X, const float* s, void* Xs, int K, int Mrows,
                                   int dtype, hipStream_t st);
 hipError_t launch_gemm(const GemmParams& p, int dtype, int epilogue, dim3 grid,

@@ -71,6 +71,20 @@ class AffinityPass:
                             out=self.n_down, workspace=self.down_ws)
         B.down_combine(self.c_down, self.n_down, out=self.S_down)
 
+    def loo(self, layer, group_of_head: Sequence[int], scale: Optional[float] = None):
+        """The exact leave-one-out score (needs layer["x_in"], and fold() first)."""
+        if not hasattr(self, "S_loo"):
+            import ctypes
+            f32 = dict(dtype=torch.float32, device=self.device)
+            self.S_loo = torch.empty((self.dims.G, self.dims.I), **f32)
+            self.loo_ws = torch.empty(max(16, B.loo_workspace_bytes(self.dims)),
+                                      dtype=torch.uint8, device=self.device)
+        B.affinity_loo(self.dims, layer["a"], layer["g"], layer["u"], layer["x_in"],
+                       layer["W_o"], self.M, group_of_head,
+                       1.0 / max(self.T, 1) if scale is None else scale,
+                       S_loo=self.S_loo, workspace=self.loo_ws)
+        return self.S_loo
+
     # -- whole pass ---------------------------------------------------------
     def run(self, layer: Dict[str, torch.Tensor], scale: Optional[float] = None) -> Dict[str, torch.Tensor]:
         grp = [int(x) for x in layer["group_of_head"].tolist()]

@@ -197,6 +197,36 @@ int hna_down_weight_norms(const hna_down_dims* dims, const void* W_q, const void
 int hna_down_combine(int32_t I, int32_t G_next, const float* c_down, const float* n,
                      float* S_down, void* stream);
 
+/* ------------------------------------------------ exact leave-one-out score */
+
+/* Bytes of workspace hna_affinity_loo needs (0 for invalid dims). */
+size_t hna_loo_workspace_bytes(const hna_dims* dims);
+
+/*
+ * Exact leave-one-out score of the pre-activations (section 3, "Affinity
+ * scores": the variant that keeps the change of the norm's rms when a head
+ * is removed):
+ *   o_h = a_h W_o^(h)T,  r = rms(x),  r_h = rms(x - o_h)
+ *   g_k^(-h) = (gamma * (x - o_h) / r_h) . w^g_k   (u likewise)
+ *   S_loo[g, k] = scale * sum_{h in g} sum_t ((g_k - g_k^(-h))^2 + (u_k - u_k^(-h))^2)
+ * (scale = 1/T gives the mean over tokens).  Computed exactly through
+ *   g_k - g_k^(-h) = (1 - r/r_h) g_k + (a_h . m_hk) / r_h,
+ * with m_hk the folded weights of hna_fold_up_weights (M) and
+ * r_h^2 = (|x|^2 - 2 x.o_h + |o_h|^2) / hidden from x itself.
+ *   a [T, H, d], g, u [T, I], W_o [hidden, H*d], M: the input dtype
+ *   x fp32 [T, hidden]: the residual entering the FFN pre-norm (the g and u
+ *     given must be its pre-activations)
+ *   S_loo fp32 [G, I] output (written, also for T = 0: zeros)
+ * A token whose residual vanishes without head h (r_h = 0) contributes
+ * nothing for that head.  Limits: those of hna_affinity_up, and
+ * 2*128*(slots of d)*16 + 2*128*H*8 + G*1024 bytes of LDS <= 160 KiB
+ * (HNA_ERR_UNSUPPORTED otherwise).  Deterministic (fixed-order sums).
+ */
+int hna_affinity_loo(const hna_dims* dims, const void* a, const void* g, const void* u,
+                     const float* x, const void* W_o, const void* M,
+                     const int32_t* group_of_head, float scale, float* S_loo, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------- layout objective */
 
 /*

@@ -54,11 +54,15 @@ def _rms(v: np.ndarray) -> np.ndarray:
 
 
 def loo_scores(a, x, gamma, W_o, W_gate, W_up, group_of_head, G: int | None = None,
-               token_chunk: int = 2048) -> np.ndarray:
+               token_chunk: int = 2048, neurons=None) -> np.ndarray:
     """S_loo [G, I] float64.  a [T, H, d], x [T, hidden], W_o [hidden, H*d],
-    W_gate, W_up [I, hidden], gamma [hidden], group_of_head [H]."""
+    W_gate, W_up [I, hidden], gamma [hidden], group_of_head [H].  ``neurons``
+    restricts the output to those columns (the same arithmetic on fewer
+    neurons; the result is then [G, len(neurons)])."""
     a, x, gamma = _f64(a), _f64(x), _f64(gamma)
     W_o, W_gate, W_up = _f64(W_o), _f64(W_gate), _f64(W_up)
+    if neurons is not None:
+        W_gate, W_up = W_gate[np.asarray(neurons)], W_up[np.asarray(neurons)]
     grp = np.asarray(group_of_head).reshape(-1)
     T, H, d = a.shape
     I = W_gate.shape[0]

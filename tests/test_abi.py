@@ -296,6 +296,30 @@ def test_head_step_and_search_validate():
     assert search(wsb=need - 1) == -4
 
 
+def test_loo_validates():
+    hna = _lib()
+    L = hna.lib()
+    vp = ctypes.c_void_p
+    F = vp(FAKE)
+    dm = dims(hna)
+    grp = (ctypes.c_int32 * dm.H)(*[h * dm.G // dm.H for h in range(dm.H)])
+    need = L.hna_loo_workspace_bytes(ctypes.byref(dm))
+    assert need > 0
+    loo = L.hna_affinity_loo
+
+    def call(d=dm, a=F, x=F, M=F, S=F, ws=F, wsb=need, g=grp):
+        return loo(ctypes.byref(d), a, F, F, x, F, M, g, 1.0, S, ws, wsb, None)
+
+    assert call(d=dims(hna, d=20)) == -2            # head dim not a multiple of 16
+    assert call(M=None) == -1
+    assert call(S=vp(MIS)) == -3
+    assert call(wsb=need - 1) == -4
+    assert call(x=None) == -1
+    bad = (ctypes.c_int32 * dm.H)(*([0] * (dm.H - 1) + [dm.G]))
+    assert call(g=bad) == -1
+    assert L.hna_loo_workspace_bytes(None) == 0
+
+
 def test_error_text_is_thread_local():
     hna = _lib()
     call_up(hna, dims(hna, d=20))
