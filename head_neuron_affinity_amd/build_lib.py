@@ -29,6 +29,10 @@ EXTRA = {"k_affinity.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "k_layout.hip": ["-ffp-contract=off"]}
 
 
+# rocBLAS runs the two plain token GEMMs of the leave-one-out score
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(line for line in (r.stderr or "").splitlines()
@@ -52,7 +56,7 @@ def build(verbose: bool = False) -> str:
             if verbose and msg.strip():
                 print(msg, file=sys.stderr)
     tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp])
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp, *LIBS])
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}", file=sys.stderr)

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -509,18 +510,28 @@ int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_u
 namespace {
 
 struct LooWorkspace {
-  size_t xx, mom, coef, part, total;
-  int n_nt;
+  size_t xx, mom, coef, As, Y, t1, gram_part, gram, t3, t3_part, blas, total;
+  int n_nt, n_tc;
 };
+constexpr size_t kBlasWorkspace = 64u << 20;   // handed to rocBLAS for its GEMMs
 LooWorkspace loo_workspace(const hna_dims* dm) {
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  const size_t es = esize_of(dm->dtype);
   LooWorkspace w;
   w.n_nt = (dm->hidden + 127) / 128;
+  w.n_tc = t1_chunks(dm->T);
   size_t o = 0;
-  w.xx = o;   o += align256((size_t)dm->T * sizeof(float));
-  w.mom = o;  o += align256((size_t)w.n_nt * dm->H * 2 * dm->T * sizeof(float));
-  w.coef = o; o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
-  w.part = o; o += align256((size_t)geo.n_chunks * dm->G * geo.I32 * sizeof(float));
+  w.xx = o;        o += align256((size_t)dm->T * sizeof(float));
+  w.mom = o;       o += align256((size_t)w.n_nt * dm->H * 2 * dm->T * sizeof(float));
+  w.coef = o;      o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
+  w.As = o;        o += align256((size_t)dm->T * dm->H * dm->d * es);
+  w.Y = o;         o += align256((size_t)2 * dm->H * dm->d * dm->I * sizeof(float));
+  w.t1 = o;        o += align256((size_t)w.n_tc * dm->H * dm->I * sizeof(float));
+  w.gram_part = o; o += geo.gram_part_bytes;
+  w.gram = o;      o += geo.gram_bytes;
+  w.t3 = o;        o += geo.add_bytes;
+  w.t3_part = o;   o += geo.add_part_bytes;
+  w.blas = o;      o += kBlasWorkspace;
   w.total = o;
   return w;
 }
@@ -614,10 +625,8 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   if (rc) return rc;
   rc = check_map(fn, group_of_head, dm->H, dm->G);
   if (rc) return rc;
-  const size_t lds = loo_lds_bytes(dm->H, dm->G, dm->d, dm->dtype);
-  if (lds > (size_t)kLdsBytes)
-    return fail(HNA_ERR_UNSUPPORTED, "%s: needs %zu bytes of LDS (H=%d, G=%d, d=%d) > %d", fn,
-                lds, dm->H, dm->G, dm->d, kLdsBytes);
+  if ((int64_t)dm->T > INT32_MAX)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld exceeds 2^31 - 1", fn, (long long)dm->T);
   REQUIRE_PTR(M);
   REQUIRE_PTR(S_loo);
   REQUIRE_PTR(workspace);
@@ -637,50 +646,88 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   float* xx = reinterpret_cast<float*>(ws + wl.xx);
   float* mom = reinterpret_cast<float*>(ws + wl.mom);
   float2* coef = reinterpret_cast<float2*>(ws + wl.coef);
-  float* part = reinterpret_cast<float*>(ws + wl.part);
+  void* As = ws + wl.As;
+  float* Y = reinterpret_cast<float*>(ws + wl.Y);
+  float* t1 = reinterpret_cast<float*>(ws + wl.t1);
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
+  const int HD = dm->H * dm->d;
+
+  // heads in KV-group order (shared by the quadratic forms and the combine)
+  QuadParams qp{};
+  LooCombineParams cp{};
+  int n = 0;
+  for (int gg = 0; gg < dm->G; ++gg) {
+    qp.group_start[gg] = cp.group_start[gg] = (int16_t)n;
+    for (int h = 0; h < dm->H; ++h)
+      if (group_of_head[h] == gg) {
+        qp.head_order[n] = cp.head_order[n] = (int8_t)h;
+        ++n;
+      }
+  }
+  qp.group_start[dm->G] = cp.group_start[dm->G] = (int16_t)n;
+
   hipError_t e;
   if (dm->T > 0) {
-    // 1. |x|^2 and the moments x . o_h, |o_h|^2;  2. alpha, beta per (token, head)
+    // 1. |x|^2 and the moments x . o_h, |o_h|^2, then alpha, beta per (token, head)
     if ((e = launch_x_sqnorm(x, dm->T, dm->hidden, xx, st)) != hipSuccess) return hip_fail(e, fn);
     MomentParams mp{a, W_o, x, mom, dm->T, dm->H, dm->d, dm->hidden,
                     (int)((dm->T + 127) / 128), wl.n_nt};
     if ((e = launch_head_moments(mp, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
     if ((e = launch_loo_coef(mom, xx, dm->T, dm->H, wl.n_nt, dm->hidden, coef, st)) != hipSuccess)
       return hip_fail(e, fn);
-    // 3. the contraction with the exact epilogue, per token chunk
-    LooParams p{};
-    p.a = a;
-    p.g = g;
-    p.u = u;
-    p.coef = coef;
-    p.M = M;
-    p.part = part;
-    p.T = dm->T;
-    p.H = dm->H;
-    p.G = dm->G;
-    p.d = dm->d;
-    p.I = dm->I;
-    p.I32 = geo.I32;
-    p.n_tt = geo.n_tt;
-    p.n_kt = geo.n_kt;
-    p.n_chunks = geo.n_chunks;
-    p.n_ktg = geo.n_ktg;
-    p.n_st = geo.n_st;
-    int n = 0;
-    for (int gg = 0; gg < dm->G; ++gg)
-      for (int h = 0; h < dm->H; ++h)
-        if (group_of_head[h] == gg) {
-          p.head_order[n] = (int8_t)h;
-          p.head_group[n] = (int8_t)gg;
-          ++n;
-        }
-    if ((e = launch_loo(p, lds, geo.grid, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
+    // 2. T2: Y = (alpha beta a)^T [g | u] over the tokens
+    if ((e = launch_scale_a(a, coef, dm->T, dm->H, dm->d, As, dm->dtype, st)) != hipSuccess)
+      return hip_fail(e, fn);
+    const int bs = loo_gemms(As, g, u, Y, dm->T, HD, dm->I, dm->dtype, ws + wl.blas,
+                             kBlasWorkspace, st);
+    if (bs != 0) return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
+    // 3. T1
+    if ((e = launch_t1(g, u, coef, dm->T, dm->H, dm->I, t1, dm->dtype, st)) != hipSuccess)
+      return hip_fail(e, fn);
+    // 4. T3: Gram matrices weighted by beta^2, their quadratic forms, group sums
+    GramParams gp{};
+    gp.a = a;
+    gp.r = nullptr;
+    gp.coef = coef;
+    gp.part = reinterpret_cast<float*>(ws + wl.gram_part);
+    gp.T = dm->T;
+    gp.H = dm->H;
+    gp.d = dm->d;
+    gp.n_gc = geo.n_gc;
+    gp.chunk_tokens = geo.gram_chunk;
+    if ((e = launch_gram(gp, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
+    void* C = ws + wl.gram;
+    if ((e = launch_gram_reduce(gp.part, geo.n_gc, (int64_t)dm->H * dm->d * dm->d, C, dm->dtype,
+                                st)) != hipSuccess)
+      return hip_fail(e, fn);
+    qp.C = C;
+    qp.M = M;
+    qp.add = reinterpret_cast<float*>(ws + wl.t3);
+    qp.add_part = reinterpret_cast<float*>(ws + wl.t3_part);
+    qp.H = dm->H;
+    qp.G = dm->G;
+    qp.d = dm->d;
+    qp.KB = geo.I32 / 32;
+    if ((e = launch_quad(qp, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
   }
-  // 4. fixed-order sum over the token chunks (zeros for T = 0)
-  return finish(launch_finalize_loo(part, dm->T > 0 ? geo.n_chunks : 0, dm->G, dm->I, geo.I32,
-                                    scale, S_loo, st),
-                st, fn);
+  // 5. S_loo = scale * (sum over the group's heads of T1 + 2 T2, plus T3); with
+  // no tokens the same kernel writes zeros (no terms)
+  const bool any = dm->T > 0;
+  cp.M = M;
+  cp.Y = any ? Y : nullptr;
+  cp.t1 = t1;
+  cp.t3 = any ? reinterpret_cast<const float*>(ws + wl.t3) : nullptr;
+  cp.S_loo = S_loo;
+  cp.scale = scale;
+  cp.H = dm->H;
+  cp.G = dm->G;
+  cp.d = dm->d;
+  cp.I = dm->I;
+  cp.I32 = geo.I32;
+  cp.KB = geo.I32 / 32;
+  cp.S = dm->d / 16;
+  cp.n_tc = any ? wl.n_tc : 0;
+  return finish(launch_loo_combine(cp, dm->dtype, st), st, fn);
 }
 
 size_t hna_layout_search_workspace_bytes(int32_t N, int32_t G, int32_t I) {

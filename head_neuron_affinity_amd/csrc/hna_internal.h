@@ -95,6 +95,7 @@ struct UpParams {
 struct GramParams {
   const void* a;
   const float* r;
+  const float2* coef;     // [T][H] (alpha, beta): weights beta^2 instead of 1/r^2 (or NULL)
   float* part;            // [n_gc][H][d][d]
   int64_t T;
   int H, d, n_gc;
@@ -215,27 +216,30 @@ struct MomentParams {
 };
 hipError_t launch_head_moments(const MomentParams& p, int dtype, hipStream_t st);
 
-// The leave-one-out pass (same work decomposition as the first-order pass).
-struct LooParams {
-  const void* a;
-  const void* g;
-  const void* u;
-  const float2* coef;     // [T][H]: alpha = 1 - r/r_h, beta = 1/r_h
-  const void* M;
-  float* part;            // [n_chunks][G][I32]
-  int64_t T;
-  int H, G, d, I, I32;
-  int n_tt, n_kt, n_chunks, n_ktg, n_st;
+// The leave-one-out score through its split T1 + 2 T2 + T3 (see k_loo.hip).
+struct LooCombineParams {
+  const void* M;          // folded weights
+  const float* Y;         // [2][I][H*d]: Y^g then Y^u, column-major H*d x I
+  const float* t1;        // [n_tc][H][I]
+  const float* t3;        // [G][I32]: the group sums of the weighted quadratic forms
+  float* S_loo;           // [G][I]
+  float scale;
+  int H, G, d, I, I32, KB, S, n_tc;
   int8_t head_order[kMaxHeads];
-  int8_t head_group[kMaxHeads];
+  int16_t group_start[kMaxHeads + 1];
 };
-size_t loo_lds_bytes(int H, int G, int d, int dtype);
 hipError_t launch_x_sqnorm(const float* x, int64_t T, int D, float* xx, hipStream_t st);
 hipError_t launch_loo_coef(const float* part, const float* xx, int64_t T, int H, int n_nt, int D,
                            float2* coef, hipStream_t st);
-hipError_t launch_loo(const LooParams& p, size_t lds, int grid, int dtype, hipStream_t st);
-hipError_t launch_finalize_loo(const float* part, int n_chunks, int G, int I, int I32,
-                               float scale, float* S_loo, hipStream_t st);
+hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, int d, void* As,
+                          int dtype, hipStream_t st);
+int t1_chunks(int64_t T);
+hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T, int H, int I,
+                     float* t1, int dtype, hipStream_t st);
+hipError_t launch_loo_combine(const LooCombineParams& p, int dtype, hipStream_t st);
+// rocBLAS status (0 = success, -1 = no device)
+int loo_gemms(const void* As, const void* g, const void* u, float* Y, int64_t T, int HD, int I,
+              int dtype, void* blas_ws, size_t blas_ws_bytes, hipStream_t st);
 
 hipError_t launch_scale_transpose(const void* X, const float* s, void* Xs, int K, int Mrows,
                                   int dtype, hipStream_t st);

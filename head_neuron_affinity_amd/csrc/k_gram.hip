@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
     for (int j = 0; j < 4; ++j) {
       const int64_t t = ts + 4 * tq + j;
       if (has_item && t < t_end) {
-        rr[j] = p.r[t];
+        // per-token 1/r^2, or per-(token, head) beta^2 when a table is given
+        rr[j] = p.coef ? p.coef[t * H + h].y : p.r[t];
         const char* src = static_cast<const char*>(p.a) + ((t * H + h) * d + 8 * fo) * sizeof(E);
 #pragma unroll
         for (int v = 0; v < NV; ++v) raw[j][v] = reinterpret_cast<const uint4*>(src)[v];
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
       float wt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        wt[j] = rr[j] != 0.f ? 1.0f / (rr[j] * rr[j]) : 0.f;
+        wt[j] = p.coef ? rr[j] * rr[j] : (rr[j] != 0.f ? 1.0f / (rr[j] * rr[j]) : 0.f);
         if constexpr (sizeof(E) == 2) {
           const uint32_t wv[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
 #pragma unroll

@@ -4,19 +4,24 @@
 // the residual x and the norm's rms is recomputed,
 //   S_loo[g, k] = sum_{h in g} E_t[(g_k - g_k^(-h))^2 + (u_k - u_k^(-h))^2].
 // With r = rms(x) and r_h = rms(x - o_h), the change splits exactly into
-//   g_k - g_k^(-h) = alpha_th g_k + beta_th (a_h . m_hk),
+//   g_k - g_k^(-h) = alpha_th g_k + beta_th P_thk,   P_thk = a_th . m^g_hk,
 //   alpha_th = 1 - r / r_h,  beta_th = 1 / r_h,
-// where a_h . m_hk = (gamma * o_h) . w^g_k comes from the folded weights M and
-// r_h^2 = (|x|^2 - 2 x . o_h + |o_h|^2) / hidden needs only two moments per
-// (token, head) (head_moments_kernel, in k_gemm.hip).  Kernels here:
-//   x_sqnorm_kernel   |x_t|^2 (both ratios use the same x, so alpha vanishes
-//                     exactly when the head's removal leaves the rms alone)
-//   loo_coef_kernel   the moments summed over column tiles in order -> alpha, beta
-//   loo_kernel        a_h . M_h on the matrix cores per token tile and head, with
-//                     the epilogue (alpha g + beta Pg)^2 + (alpha u + beta Pu)^2
-//                     summed over the group's heads into per-chunk partials
-//   finalize_loo      fixed-order float64 sum of the partials
+// (m_hk the folded weights; u likewise), so that per head and neuron
+//   sum_t (...)^2 = T1 + 2 T2 + T3,
+//   T1 = sum_t alpha^2 (g^2 + u^2)                      (t1_kernel)
+//   T2 = m^g_hk . Y^g_h[:, k] + m^u_hk . Y^u_h[:, k],  Y_h = sum_t alpha beta a_th g_t^T
+//        (two plain GEMMs over the tokens, by rocBLAS, on a scaled by alpha beta)
+//   T3 = m^T C_h m,  C_h = sum_t beta_th^2 a_th a_th^T   (the Gram and quadratic-
+//        form kernels of the ADD score, weighted per token and head)
+// r_h^2 = (|x|^2 - 2 x . o_h + |o_h|^2) / hidden needs two moments per (token,
+// head) (head_moments_kernel, in k_gemm.hip) and |x|^2 (x_sqnorm_kernel).  All
+// three terms are non-cancelling in practice (T3 dominates; T2 is a fraction of
+// it), so rounding a * alpha beta to bf16 for the GEMMs costs far less than the
+// bf16 tolerance.
+#include <rocblas/rocblas.h>
+
 #include <cmath>
+#include <mutex>
 
 #include "hna_internal.h"
 
@@ -74,245 +79,98 @@ __global__ __launch_bounds__(256) void loo_coef_kernel(const float* __restrict__
   coef[t * H + h] = c;
 }
 
-template <typename T> struct LTraits;
-template <> struct LTraits<__bf16> {
-  static constexpr int kBytes = 2, kChunksPerStep = 2, kQuads = 1;
-};
-template <> struct LTraits<float> {
-  static constexpr int kBytes = 4, kChunksPerStep = 4, kQuads = 2;
-};
-
 __device__ inline float load_elem(const __bf16* p, int64_t i) {
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 __device__ inline float load_elem(const float* p, int64_t i) { return p[i]; }
 
-constexpr int pow2_slots(int cpr) { return cpr <= 8 ? 8 : (cpr <= 16 ? 16 : 32); }
-
-// Work decomposition as in the first-order pass: a workgroup owns 128 neurons
-// (4 waves x 32) and a chunk of up to 8 consecutive token tiles of 128 tokens;
-// per tile each lane keeps g and u of its 64 (t, k) pairs in registers, the
-// tile's (alpha, beta) table [128][H] sits in LDS, and for every head (in KV
-// group order) a_h . M_h runs on the matrix cores from an LDS-staged a tile.
-template <typename E, int S>
-__global__ __launch_bounds__(256) void loo_kernel(const LooParams p) {
-  using Tr = LTraits<E>;
-  constexpr int Q = Tr::kQuads;
-  constexpr int CPS = Tr::kChunksPerStep;
-  constexpr int CPR = S * CPS;              // 16-byte chunks per row of a_h
-  constexpr int SLOTS = pow2_slots(CPR);
-  constexpr int ROWB = SLOTS * 16;
-  constexpr int BUFB = kTileTokens * ROWB;
-  constexpr int CPT = CPR / 2;              // chunks staged per thread per tile
-
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char* abuf = lds;                                       // [2][128][ROWB]
-  float2* cbuf = reinterpret_cast<float2*>(lds + 2 * BUFB);        // [2][128][H]
-  float* accl = reinterpret_cast<float*>(cbuf + 2 * kTileTokens * p.H);  // [G][256]
-
-  // workgroup -> (neuron tile, token chunk); consecutive ids alternate XCDs
-  const int id = blockIdx.x;
-  const int xcd = id & 7, wi = id >> 3;
-  const int st = xcd + 8 * (wi >> 5), mem = wi & 31;
-  if (st >= p.n_st) return;
-  const int kt = (st % p.n_ktg) * kSuperKt + (mem & 3);
-  const int chunk = (st / p.n_ktg) * kSuperChunks + (mem >> 2);
-  if (kt >= p.n_kt || chunk >= p.n_chunks) return;
-
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int H = p.H, G = p.G, I = p.I, d = p.d;
-  const int64_t NT = p.T;
-  const int KB = p.I32 >> 5;
-  const int nb = kt * 4 + w;
-  const int nbc = nb < KB ? nb : KB - 1;     // clamped so that M reads stay in bounds
-  const int k = nb * 32 + (l & 31);
-  const bool kvalid = nb < KB && k < I;
-  const E* a = static_cast<const E*>(p.a);
-  const E* gp = static_cast<const E*>(p.g);
-  const E* up = static_cast<const E*>(p.u);
-  const E* M = static_cast<const E*>(p.M);
-
-  for (int x = tid; x < G * 256; x += 256) accl[x] = 0.f;
-
-  const int tt0 = chunk * kTilesPerChunk;
-  const int ntile = min(kTilesPerChunk, p.n_tt - tt0);
-  const int nsteps = ntile * H;
-
-  uint4 stage[CPT];
-  auto load_stage = [&](int step) {
-    const int ti = step / H;
-    const int h = p.head_order[step - ti * H];
-    const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = tid + 256 * c;
-      const int row = q / CPR, col = q - (q / CPR) * CPR;
-      const int64_t t = t0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < NT) v = *reinterpret_cast<const uint4*>(a + ((t * H + h) * d) + col * (16 / Tr::kBytes));
-      stage[c] = v;
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = tid + 256 * c;
-      const int row = q / CPR, col = q - (q / CPR) * CPR;
-      const int off = row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4);
-      *reinterpret_cast<uint4*>(abuf + buf * BUFB + off) = stage[c];
-    }
-  };
-  // the tile's (alpha, beta) rows; tokens past the end get zeros
-  auto stage_coef = [&](int ti, int buf) {
-    const int64_t t0 = (int64_t)(tt0 + ti) * kTileTokens;
-    const int64_t valid = (NT - t0 < kTileTokens ? NT - t0 : kTileTokens) * H;
-    float2* dst = cbuf + buf * kTileTokens * H;
-    for (int e = tid; e < kTileTokens * H; e += 256)
-      dst[e] = e < valid ? p.coef[t0 * H + e] : make_float2(0.f, 0.f);
-  };
-
-  load_stage(0);
-  stage_coef(0, 0);
-  store_stage(0);
-  __syncthreads();
-
-  f32x16 accG[4], accU[4];
-  float gv[4][16], uv[4][16];
-  float run[4] = {0.f, 0.f, 0.f, 0.f};
-  const int64_t slab = (int64_t)64 * 8;            // elements per (h, kb, gu, s)
-  const E* Mw = M + (int64_t)nbc * 2 * S * slab + l * 8;
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const int ti = step / H, hi = step - ti * H;
-    const int h = p.head_order[hi];
-    const int grp = p.head_group[hi];
-    const bool has_next = step + 1 < nsteps;
-    if (has_next) load_stage(step + 1);
-
-    if (hi == 0) {
-      // the tile's pre-activations, shared by all heads
-      const int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = tb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-          const int64_t t = tbase + row;
-          const bool ok = kvalid && t < NT;
-          gv[tb][v] = ok ? load_elem(gp, t * I + k) : 0.f;
-          uv[tb][v] = ok ? load_elem(up, t * I + k) : 0.f;
-        }
-      }
-    }
-    if (hi == H - 1 && ti + 1 < ntile) stage_coef(ti + 1, (ti + 1) & 1);
-
-    // a_h (128 x d) . M_h (d x [32 gate | 32 up]) on the matrix cores
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      accG[tb] = f32x16{};
-      accU[tb] = f32x16{};
-    }
-    const unsigned char* ab = abuf + buf * BUFB;
-    const E* Mh = Mw + (int64_t)h * KB * 2 * S * slab;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      uint4 bg[Q], bu[Q];
-#pragma unroll
-      for (int qq = 0; qq < Q; ++qq) {
-        bg[qq] = *reinterpret_cast<const uint4*>(Mh + s * slab + qq * (16 / Tr::kBytes));
-        bu[qq] = *reinterpret_cast<const uint4*>(Mh + (S + s) * slab + qq * (16 / Tr::kBytes));
-      }
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int row = tb * 32 + (l & 31);
-        uint4 af[Q];
-#pragma unroll
-        for (int qq = 0; qq < Q; ++qq) {
-          const int col = s * CPS + (l >> 5) * Q + qq;
-          af[qq] = *reinterpret_cast<const uint4*>(ab + row * ROWB + ((col ^ (row & (SLOTS - 1))) << 4));
-        }
-        mma(accG[tb], af, bg);
-        mma(accU[tb], af, bu);
-      }
-    }
-
-    // epilogue: the exact pre-activation changes and their squares
-    const float2* cb = cbuf + (ti & 1) * kTileTokens * H + h;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = tb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        const float2 c = cb[row * H];
-        const float dg = fmaf(c.x, gv[tb][v], c.y * accG[tb][v]);
-        const float du = fmaf(c.x, uv[tb][v], c.y * accU[tb][v]);
-        run[tb] = fmaf(dg, dg, fmaf(du, du, run[tb]));
-      }
-    }
-    if (hi == H - 1 || p.head_group[hi + 1] != grp) {
-      accl[grp * 256 + tid] += (run[0] + run[1]) + (run[2] + run[3]);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) run[tb] = 0.f;
-    }
-    if (has_next) store_stage(buf ^ 1);
-    __syncthreads();
-  }
-
-  // lanes l and l+32 hold the same neuron: combine and write the partial sums
-  if (l < 32 && nb < KB) {
-    const int kk = nb * 32 + l;
-    float* out = p.part + (int64_t)chunk * G * p.I32;
-    for (int gg = 0; gg < G; ++gg)
-      out[(int64_t)gg * p.I32 + kk] = accl[gg * 256 + tid] + accl[gg * 256 + tid + 32];
-  }
-}
-
-// S_loo[g, k] = scale * sum over chunks (in order, float64) of the partials
-__global__ __launch_bounds__(256) void finalize_loo_kernel(const float* __restrict__ part,
-                                                           int n_chunks, int G, int I, int I32,
-                                                           float scale, float* S_loo) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)G * I) return;
-  const int g = (int)(idx / I), k = (int)(idx - (int64_t)g * I);
-  double s = 0.0;
-  for (int c = 0; c < n_chunks; ++c) s += part[((int64_t)c * G + g) * I32 + k];
-  S_loo[idx] = (float)(s * (double)scale);
-}
-
-template <typename E, int S>
-hipError_t launch_loo_typed(const LooParams& p, size_t lds, int grid, hipStream_t st) {
-  auto fn = loo_kernel<E, S>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, st, p);
-  return hipGetLastError();
-}
-
+// As[t][h*d + j] = alpha_th beta_th a[t][h][j] (rounded to the input dtype)
 template <typename E>
-hipError_t launch_loo_steps(const LooParams& p, size_t lds, int grid, hipStream_t st) {
-  switch (p.d / 16) {
-    case 1: return launch_loo_typed<E, 1>(p, lds, grid, st);
-    case 2: return launch_loo_typed<E, 2>(p, lds, grid, st);
-    case 3: return launch_loo_typed<E, 3>(p, lds, grid, st);
-    case 4: return launch_loo_typed<E, 4>(p, lds, grid, st);
-    case 5: return launch_loo_typed<E, 5>(p, lds, grid, st);
-    case 6: return launch_loo_typed<E, 6>(p, lds, grid, st);
-    case 7: return launch_loo_typed<E, 7>(p, lds, grid, st);
-    case 8: return launch_loo_typed<E, 8>(p, lds, grid, st);
-    default: return hipErrorInvalidValue;
+__global__ __launch_bounds__(256) void scale_a_kernel(const E* __restrict__ a,
+                                                      const float2* __restrict__ coef, int64_t T,
+                                                      int H, int d, E* __restrict__ As) {
+  const int64_t n = T * H * d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t th = i / d;
+    const float2 c = coef[th];
+    const float v = load_elem(a, i) * (c.x * c.y);
+    if constexpr (sizeof(E) == 2) reinterpret_cast<uint16_t*>(As)[i] = (uint16_t)f32_to_bf16_bits(v);
+    else As[i] = v;
   }
+}
+
+// T1 partial sums: t1[tc][h][k] = sum over token chunk tc of alpha_th^2 (g_tk^2 + u_tk^2);
+// heads in blocks of 16, the chunk's alphas staged in LDS 256 tokens at a time
+constexpr int kT1Chunk = 2048, kT1Stage = 256, kT1Heads = 16;
+template <typename E>
+__global__ __launch_bounds__(256) void t1_kernel(const E* __restrict__ g, const E* __restrict__ u,
+                                                 const float2* __restrict__ coef, int64_t T,
+                                                 int H, int I, float* __restrict__ t1) {
+  __shared__ float al2[kT1Stage][kT1Heads];
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  const int tc = blockIdx.y;
+  const int64_t t0 = (int64_t)tc * kT1Chunk, t1e = min(T, t0 + kT1Chunk);
+  for (int h0 = 0; h0 < H; h0 += kT1Heads) {
+    const int nh = min(kT1Heads, H - h0);
+    float acc[kT1Heads];
+#pragma unroll
+    for (int i = 0; i < kT1Heads; ++i) acc[i] = 0.f;
+    for (int64_t ts = t0; ts < t1e; ts += kT1Stage) {
+      __syncthreads();
+      for (int e = threadIdx.x; e < kT1Stage * kT1Heads; e += 256) {
+        const int tt = e / kT1Heads, hh = e - tt * kT1Heads;
+        const int64_t t = ts + tt;
+        float a2 = 0.f;
+        if (t < t1e && hh < nh) {
+          const float al = coef[t * H + h0 + hh].x;
+          a2 = al * al;
+        }
+        al2[tt][hh] = a2;
+      }
+      __syncthreads();
+      if (k < I) {
+        const int n = (int)min((int64_t)kT1Stage, t1e - ts);
+        for (int tt = 0; tt < n; ++tt) {
+          const int64_t t = ts + tt;
+          const float gv = load_elem(g, t * I + k), uv = load_elem(u, t * I + k);
+          const float q = fmaf(gv, gv, uv * uv);
+#pragma unroll
+          for (int i = 0; i < kT1Heads; ++i) acc[i] = fmaf(al2[tt][i], q, acc[i]);
+        }
+      }
+    }
+    if (k < I)
+      for (int i = 0; i < nh; ++i) t1[((int64_t)tc * H + h0 + i) * I + k] = acc[i];
+  }
+}
+
+// S_loo[g][k] = scale * (sum_{h in g} (T1 + 2 T2) + T3[g][k]), float64, heads in
+// group order and every inner sum in a fixed order
+template <typename E>
+__global__ __launch_bounds__(256) void loo_combine_kernel(const LooCombineParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.G * p.I) return;
+  const int grp = (int)(idx / p.I), k = (int)(idx - (int64_t)grp * p.I);
+  const E* M = static_cast<const E*>(p.M);
+  const int HD = p.H * p.d;
+  double s = 0.0;
+  for (int q = p.group_start[grp]; q < p.group_start[grp + 1]; ++q) {
+    const int h = p.head_order[q];
+    double t1 = 0.0;
+    for (int tc = 0; tc < p.n_tc; ++tc) t1 += (double)p.t1[((int64_t)tc * p.H + h) * p.I + k];
+    double t2 = 0.0;
+    for (int gu = 0; gu < (p.Y ? 2 : 0); ++gu) {
+      const float* Y = p.Y + (int64_t)gu * HD * p.I + (int64_t)k * HD + (int64_t)h * p.d;
+      for (int j = 0; j < p.d; ++j)
+        t2 += (double)load_elem(M, folded_index(h, j, k, gu, p.KB, p.S)) * (double)Y[j];
+    }
+    s += t1 + 2.0 * t2;
+  }
+  if (p.t3) s += (double)p.t3[(int64_t)grp * p.I32 + k];
+  p.S_loo[idx] = (float)(s * (double)p.scale);
 }
 
 }  // namespace
-
-size_t loo_lds_bytes(int H, int G, int d, int dtype) {
-  const int cpr = (d / 16) * (dtype == 1 ? 2 : 4);
-  const int slots = pow2_slots(cpr);
-  return (size_t)2 * kTileTokens * slots * 16 + (size_t)2 * kTileTokens * H * sizeof(float2) +
-         (size_t)G * 256 * sizeof(float);
-}
 
 hipError_t launch_x_sqnorm(const float* x, int64_t T, int D, float* xx, hipStream_t st) {
   if (T == 0) return hipSuccess;
@@ -330,18 +188,77 @@ hipError_t launch_loo_coef(const float* part, const float* xx, int64_t T, int H,
   return hipGetLastError();
 }
 
-hipError_t launch_loo(const LooParams& p, size_t lds, int grid, int dtype, hipStream_t st) {
-  if (grid == 0) return hipSuccess;
-  return dtype == 1 ? launch_loo_steps<__bf16>(p, lds, grid, st)
-                    : launch_loo_steps<float>(p, lds, grid, st);
+hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, int d, void* As,
+                          int dtype, hipStream_t st) {
+  const int64_t n = T * H * d;
+  if (n == 0) return hipSuccess;
+  const int64_t nb = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(nb < 65536 ? nb : 65536);
+  if (dtype == 1)
+    hipLaunchKernelGGL(scale_a_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const __bf16*>(a), coef, T, H, d, static_cast<__bf16*>(As));
+  else
+    hipLaunchKernelGGL(scale_a_kernel<float>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const float*>(a), coef, T, H, d, static_cast<float*>(As));
+  return hipGetLastError();
 }
 
-hipError_t launch_finalize_loo(const float* part, int n_chunks, int G, int I, int I32,
-                               float scale, float* S_loo, hipStream_t st) {
-  const int64_t n = (int64_t)G * I;
-  hipLaunchKernelGGL(finalize_loo_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     part, n_chunks, G, I, I32, scale, S_loo);
+int t1_chunks(int64_t T) { return (int)((T + kT1Chunk - 1) / kT1Chunk); }
+
+hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T, int H, int I,
+                     float* t1, int dtype, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((I + 255) / 256, t1_chunks(T));
+  if (dtype == 1)
+    hipLaunchKernelGGL(t1_kernel<__bf16>, grid, dim3(256), 0, st, static_cast<const __bf16*>(g),
+                       static_cast<const __bf16*>(u), coef, T, H, I, t1);
+  else
+    hipLaunchKernelGGL(t1_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(g),
+                       static_cast<const float*>(u), coef, T, H, I, t1);
   return hipGetLastError();
+}
+
+hipError_t launch_loo_combine(const LooCombineParams& p, int dtype, hipStream_t st) {
+  const int64_t n = (int64_t)p.G * p.I;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dtype == 1) hipLaunchKernelGGL(loo_combine_kernel<__bf16>, grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(loo_combine_kernel<float>, grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// ---- the two token GEMMs, Y^g = As^T g and Y^u = As^T u, by rocBLAS
+namespace {
+std::mutex g_blas_mu;
+rocblas_handle g_blas[64] = {};
+}  // namespace
+
+int loo_gemms(const void* As, const void* g, const void* u, float* Y, int64_t T, int HD, int I,
+              int dtype, void* blas_ws, size_t blas_ws_bytes, hipStream_t st) {
+  if (T == 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lock(g_blas_mu);
+  if (!g_blas[dev]) {
+    rocblas_status cs = rocblas_create_handle(&g_blas[dev]);
+    if (cs != rocblas_status_success) {
+      g_blas[dev] = nullptr;
+      return (int)cs;
+    }
+  }
+  rocblas_handle hb = g_blas[dev];
+  rocblas_status bs = rocblas_set_stream(hb, st);
+  if (bs == rocblas_status_success) bs = rocblas_set_workspace(hb, blas_ws, blas_ws_bytes);
+  const rocblas_datatype in_t = dtype == 1 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  const float one = 1.0f, zero = 0.0f;
+  // column-major: As is HD x T (lda HD), g and u are I x T (ldb I), Y is HD x I
+  for (int gu = 0; gu < 2 && bs == rocblas_status_success; ++gu) {
+    float* Yg = Y + (int64_t)gu * HD * I;
+    bs = rocblas_gemm_ex(hb, rocblas_operation_none, rocblas_operation_transpose, HD, I, (int)T,
+                         &one, As, in_t, HD, gu ? u : g, in_t, I, &zero, Yg,
+                         rocblas_datatype_f32_r, HD, Yg, rocblas_datatype_f32_r, HD,
+                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  }
+  return (int)bs;
 }
 
 }  // namespace hna
