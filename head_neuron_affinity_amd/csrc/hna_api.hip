@@ -510,23 +510,26 @@ int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_u
 namespace {
 
 struct LooWorkspace {
-  size_t xx, mom, coef, As, Y, t1, gram_part, gram, t3, t3_part, blas, total;
-  int n_nt, n_tc;
+  size_t xx, xl, ZA, U, Q, coef, Y, t1, t1r, gram_part, gram, t3, t3_part, blas, total;
+  int n_tc;
 };
 constexpr size_t kBlasWorkspace = 64u << 20;   // handed to rocBLAS for its GEMMs
 LooWorkspace loo_workspace(const hna_dims* dm) {
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
   const size_t es = esize_of(dm->dtype);
+  const size_t thd = (size_t)dm->T * dm->H * dm->d;
   LooWorkspace w;
-  w.n_nt = (dm->hidden + 127) / 128;
   w.n_tc = t1_chunks(dm->T);
   size_t o = 0;
   w.xx = o;        o += align256((size_t)dm->T * sizeof(float));
-  w.mom = o;       o += align256((size_t)w.n_nt * dm->H * 2 * dm->T * sizeof(float));
+  w.xl = o;        o += dm->dtype == HNA_BF16 ? align256((size_t)dm->T * dm->hidden * 2) : 0;
+  w.ZA = o;        o += align256(thd * es);   // x W_o, then a scaled by alpha beta
+  w.U = o;         o += align256(thd * es);
+  w.Q = o;         o += align256((size_t)dm->H * dm->d * dm->d * es);
   w.coef = o;      o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
-  w.As = o;        o += align256((size_t)dm->T * dm->H * dm->d * es);
   w.Y = o;         o += align256((size_t)2 * dm->H * dm->d * dm->I * sizeof(float));
   w.t1 = o;        o += align256((size_t)w.n_tc * dm->H * dm->I * sizeof(float));
+  w.t1r = o;       o += align256((size_t)dm->H * dm->I * sizeof(double));
   w.gram_part = o; o += geo.gram_part_bytes;
   w.gram = o;      o += geo.gram_bytes;
   w.t3 = o;        o += geo.add_bytes;
@@ -644,13 +647,17 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* xx = reinterpret_cast<float*>(ws + wl.xx);
-  float* mom = reinterpret_cast<float*>(ws + wl.mom);
+  void* xl = ws + wl.xl;
+  void* ZA = ws + wl.ZA;
+  void* U = ws + wl.U;
+  void* Q = ws + wl.Q;
   float2* coef = reinterpret_cast<float2*>(ws + wl.coef);
-  void* As = ws + wl.As;
   float* Y = reinterpret_cast<float*>(ws + wl.Y);
   float* t1 = reinterpret_cast<float*>(ws + wl.t1);
+  void* bws = ws + wl.blas;
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
-  const int HD = dm->H * dm->d;
+  const int HD = dm->H * dm->d, dt = dm->dtype, T = (int)dm->T, d = dm->d, D = dm->hidden;
+  const bool bf = dt == HNA_BF16;
 
   // heads in KV-group order (shared by the quadratic forms and the combine)
   QuadParams qp{};
@@ -667,22 +674,34 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   qp.group_start[dm->G] = cp.group_start[dm->G] = (int16_t)n;
 
   hipError_t e;
+  int bs = 0;
   if (dm->T > 0) {
-    // 1. |x|^2 and the moments x . o_h, |o_h|^2, then alpha, beta per (token, head)
-    if ((e = launch_x_sqnorm(x, dm->T, dm->hidden, xx, st)) != hipSuccess) return hip_fail(e, fn);
-    MomentParams mp{a, W_o, x, mom, dm->T, dm->H, dm->d, dm->hidden,
-                    (int)((dm->T + 127) / 128), wl.n_nt};
-    if ((e = launch_head_moments(mp, dm->dtype, st)) != hipSuccess) return hip_fail(e, fn);
-    if ((e = launch_loo_coef(mom, xx, dm->T, dm->H, wl.n_nt, dm->hidden, coef, st)) != hipSuccess)
+    // 1. |x|^2 (and x in bf16 for the GEMM); the moments x . o_h and |o_h|^2
+    //    through Z = x W_o, Q_h = W_o^(h)T W_o^(h), U_h = Q_h a_h (column-major
+    //    views: W_o is HD x hidden, x is hidden x T, a and Z and U are HD x T)
+    if ((e = launch_x_prep(x, dm->T, D, xx, bf ? xl : nullptr, st)) != hipSuccess)
       return hip_fail(e, fn);
-    // 2. T2: Y = (alpha beta a)^T [g | u] over the tokens
-    if ((e = launch_scale_a(a, coef, dm->T, dm->H, dm->d, As, dm->dtype, st)) != hipSuccess)
+    const void* xg = bf ? xl : static_cast<const void*>(x);
+    if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, false, HD, T, D, W_o, dt, HD, 0, xg, dt, D,
+                        0, ZA, dt, HD, 0, 1)) != 0 ||
+        (bs = blas_gemm(st, bws, kBlasWorkspace, false, true, d, d, D, W_o, dt, HD, d, W_o, dt, HD,
+                        d, Q, dt, d, (int64_t)d * d, dm->H)) != 0 ||
+        (bs = blas_gemm(st, bws, kBlasWorkspace, false, false, d, T, d, Q, dt, d, (int64_t)d * d, a,
+                        dt, HD, d, U, dt, HD, d, dm->H)) != 0)
+      return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
+    if ((e = launch_loo_coef(a, ZA, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess)
       return hip_fail(e, fn);
-    const int bs = loo_gemms(As, g, u, Y, dm->T, HD, dm->I, dm->dtype, ws + wl.blas,
-                             kBlasWorkspace, st);
-    if (bs != 0) return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
+    // 2. T2: Y^g = (alpha beta a)^T g and Y^u likewise, over the tokens
+    if ((e = launch_scale_a(a, coef, dm->T, dm->H, d, ZA, dt, st)) != hipSuccess)
+      return hip_fail(e, fn);
+    for (int gu = 0; gu < 2; ++gu)
+      if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, dm->I, T, ZA, dt, HD, 0,
+                          gu ? u : g, dt, dm->I, 0, Y + (int64_t)gu * HD * dm->I, 0, HD, 0, 1)) != 0)
+        return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
     // 3. T1
-    if ((e = launch_t1(g, u, coef, dm->T, dm->H, dm->I, t1, dm->dtype, st)) != hipSuccess)
+    if ((e = launch_t1(g, u, coef, dm->T, dm->H, dm->I, t1, dm->dtype, st)) != hipSuccess ||
+        (e = launch_t1_reduce(t1, wl.n_tc, (int64_t)dm->H * dm->I,
+                              reinterpret_cast<double*>(ws + wl.t1r), st)) != hipSuccess)
       return hip_fail(e, fn);
     // 4. T3: Gram matrices weighted by beta^2, their quadratic forms, group sums
     GramParams gp{};
@@ -715,7 +734,7 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   const bool any = dm->T > 0;
   cp.M = M;
   cp.Y = any ? Y : nullptr;
-  cp.t1 = t1;
+  cp.t1r = any ? reinterpret_cast<const double*>(ws + wl.t1r) : nullptr;
   cp.t3 = any ? reinterpret_cast<const float*>(ws + wl.t3) : nullptr;
   cp.S_loo = S_loo;
   cp.scale = scale;
@@ -726,7 +745,6 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   cp.I32 = geo.I32;
   cp.KB = geo.I32 / 32;
   cp.S = dm->d / 16;
-  cp.n_tc = any ? wl.n_tc : 0;
   return finish(launch_loo_combine(cp, dm->dtype, st), st, fn);
 }
 

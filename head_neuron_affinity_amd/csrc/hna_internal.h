@@ -204,42 +204,36 @@ struct GemmParams {
   float* seg_part;     // [n_seg][Mrows]
   int H_next, G_next, d_next;
 };
-// Leave-one-out moments: part[(nt*H + h)*2 + 0][t] and [..+1][t] hold the
-// n-tile nt parts of x_t . o_th and |o_th|^2, o_th = W_o^(h) a_th.
-struct MomentParams {
-  const void* a;       // [T, H, d]
-  const void* W_o;     // [hidden, H*d]
-  const float* x;      // [T, hidden] residual entering the FFN pre-norm
-  float* part;         // [n_nt][H][2][T]
-  int64_t T;
-  int H, d, hidden, n_mt, n_nt;
-};
-hipError_t launch_head_moments(const MomentParams& p, int dtype, hipStream_t st);
+
 
 // The leave-one-out score through its split T1 + 2 T2 + T3 (see k_loo.hip).
 struct LooCombineParams {
   const void* M;          // folded weights
   const float* Y;         // [2][I][H*d]: Y^g then Y^u, column-major H*d x I
-  const float* t1;        // [n_tc][H][I]
+  const double* t1r;      // [H][I]: T1 summed over the token chunks (NULL: no tokens)
   const float* t3;        // [G][I32]: the group sums of the weighted quadratic forms
   float* S_loo;           // [G][I]
   float scale;
-  int H, G, d, I, I32, KB, S, n_tc;
+  int H, G, d, I, I32, KB, S;
   int8_t head_order[kMaxHeads];
   int16_t group_start[kMaxHeads + 1];
 };
-hipError_t launch_x_sqnorm(const float* x, int64_t T, int D, float* xx, hipStream_t st);
-hipError_t launch_loo_coef(const float* part, const float* xx, int64_t T, int H, int n_nt, int D,
-                           float2* coef, hipStream_t st);
+hipError_t launch_t1_reduce(const float* t1, int n_tc, int64_t HI, double* t1r, hipStream_t st);
+hipError_t launch_x_prep(const float* x, int64_t T, int D, float* xx, void* xl, hipStream_t st);
+hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const float* xx, int64_t T,
+                           int H, int d, int D, float2* coef, int dtype, hipStream_t st);
 hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, int d, void* As,
                           int dtype, hipStream_t st);
 int t1_chunks(int64_t T);
 hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T, int H, int I,
                      float* t1, int dtype, hipStream_t st);
 hipError_t launch_loo_combine(const LooCombineParams& p, int dtype, hipStream_t st);
-// rocBLAS status (0 = success, -1 = no device)
-int loo_gemms(const void* As, const void* g, const void* u, float* Y, int64_t T, int HD, int I,
-              int dtype, void* blas_ws, size_t blas_ws_bytes, hipStream_t st);
+// C = op(A) op(B) per batch entry, column-major, fp32 accumulation, by rocBLAS;
+// types 0 = fp32, 1 = bf16.  Returns the rocBLAS status (0 = success, -1 = no
+// device).
+int blas_gemm(hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb, int m, int n, int k,
+              const void* A, int at, int lda, int64_t sa, const void* B, int bt, int ldb,
+              int64_t sb, void* C, int ct, int ldc, int64_t sc, int batch);
 
 hipError_t launch_scale_transpose(const void* X, const float* s, void* Xs, int K, int Mrows,
                                   int dtype, hipStream_t st);

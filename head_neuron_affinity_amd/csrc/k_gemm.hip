@@ -14,7 +14,6 @@
 // fp32), so each product is one MFMA; fp32 inputs use fp32 MFMA.  Tile
 // 128 x 128 x 32, 4 waves (2 x 2, 64 x 64 each), LDS double buffer with
 // XOR-swizzled 16-byte chunks.  The fragment reads from LDS bound the loop.
-// The head-moment kernel of the leave-one-out score shares this staging.
 #include "hna_internal.h"
 
 namespace hna {
@@ -308,158 +307,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   }
 }
 
-// Moments of a head's write into the residual, for the leave-one-out score
-// (section 3, "Affinity scores"): for a tile of 128 tokens x 128 residual
-// columns and every head h, O = a_h W_o^(h)T on the matrix cores (K = d; the
-// same staging and fragment order as gemm_kernel), then per token the tile's
-// parts of x . o_h = sum_n O[t, n] x[t, n] and |o_h|^2 = sum_n O[t, n]^2.
-// The x tile is read once, into registers in the accumulator layout.  Block
-// b runs on XCD b % 8; the n tiles of one token tile share that XCD, so its
-// a rows are fetched from HBM once per XCD.
-template <typename T>
-__global__ __launch_bounds__(256) void head_moments_kernel(const MomentParams p) {
-  using Tr = GT<T>;
-  constexpr int CR = Tr::kCR;
-  constexpr int CPT = BM * CR / 256;
-  constexpr int EPC = 16 / Tr::kBytes;
-  constexpr int Q = Tr::kQ;
-  constexpr int TILE_CHUNKS = BM * CR;
-
-  __shared__ uint4 xs[2][TILE_CHUNKS];
-  __shared__ uint4 ys[2][TILE_CHUNKS];
-  __shared__ float red[2][2][BM];
-
-  const int b = blockIdx.x;
-  const int xcd = b & 7, wi = b >> 3;
-  const int nt = wi % p.n_nt, mt = xcd + 8 * (wi / p.n_nt);
-  if (mt >= p.n_mt) return;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
-  const int64_t NT = p.T;
-  const int D = p.hidden, K = p.d, ld = p.H * p.d;
-
-  float xr[2][2][16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t t = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        const int n = n0 + wn * 64 + j * 32 + (l & 31);
-        xr[i][j][v] = (t < NT && n < D) ? p.x[t * D + n] : 0.f;
-      }
-
-  for (int h = 0; h < p.H; ++h) {
-    const T* X = static_cast<const T*>(p.a) + (int64_t)h * p.d;
-    const T* Y = static_cast<const T*>(p.W_o) + (int64_t)h * p.d;
-    uint4 xq[CPT], yq[CPT];
-    auto load = [&](int k0) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int q = tid + 256 * c;
-        const int row = q / CR, col = q % CR;
-        const int kc = k0 + col * EPC;
-        const bool okx = m0 + row < NT && kc < K;
-        xq[c] = okx ? *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + row) * ld + kc)
-                    : make_uint4(0, 0, 0, 0);
-        const bool oky = n0 + row < D && kc < K;
-        yq[c] = oky ? *reinterpret_cast<const uint4*>(Y + (int64_t)(n0 + row) * ld + kc)
-                    : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int q = tid + 256 * c;
-        const int o = swz<CR>(q / CR, q % CR);
-        xs[buf][o] = xq[c];
-        ys[buf][o] = yq[c];
-      }
-    };
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    const int nk = (K + BK - 1) / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) load((kt + 1) * BK);
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        uint4 af[2][Q], bf[2][Q];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int ra = wm * 64 + i * 32 + (l & 31);
-          const int rb = wn * 64 + i * 32 + (l & 31);
-#pragma unroll
-          for (int qq = 0; qq < Q; ++qq) {
-            const int col = s * Tr::kCPS + (l >> 5) * Q + qq;
-            af[i][qq] = xs[buf][swz<CR>(ra, col)];
-            bf[i][qq] = ys[buf][swz<CR>(rb, col)];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) mma(acc[i][j], af[i], bf[j]);
-      }
-      if (kt + 1 < nk) store(buf ^ 1);
-      __syncthreads();
-    }
-
-    // per token: sum over this wave's 64 columns, then over the two column halves
-    float sx[2][16], so[2][16];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sx[i][v] = fmaf(acc[i][0][v], xr[i][0][v], acc[i][1][v] * xr[i][1][v]);
-        so[i][v] = fmaf(acc[i][0][v], acc[i][0][v], acc[i][1][v] * acc[i][1][v]);
-      }
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          sx[i][v] += __shfl_xor(sx[i][v], off);
-          so[i][v] += __shfl_xor(so[i][v], off);
-        }
-    if ((l & 31) == 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-          red[0][wn][row] = sx[i][v];
-          red[1][wn][row] = so[i][v];
-        }
-    }
-    __syncthreads();
-    if (tid < BM && m0 + tid < NT) {
-      float* dst = p.part + ((int64_t)(nt * p.H + h) * 2) * NT + m0 + tid;
-      dst[0] = red[0][0][tid] + red[0][1][tid];
-      dst[NT] = red[1][0][tid] + red[1][1][tid];
-    }
-    __syncthreads();
-  }
-}
-
 }  // namespace
-
-hipError_t launch_head_moments(const MomentParams& p, int dtype, hipStream_t st) {
-  if (p.T == 0) return hipSuccess;
-  const int grid = round_up(p.n_mt, 8) * p.n_nt;
-  if (dtype == 1) hipLaunchKernelGGL(head_moments_kernel<__bf16>, dim3(grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL(head_moments_kernel<float>, dim3(grid), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
 
 hipError_t launch_scale_transpose(const void* in, const float* s, void* out, int rows, int cols,
                                   int dtype, hipStream_t st) {

@@ -55,6 +55,7 @@ def check(got, ref, tol, metric):
 @pytest.mark.parametrize("shape,tol,metric", [
     (synth.LayerShape("tiny-fp32", 256, 64, 4, 2, 16, 128, "f32", 0.5), FP32_TOL, "max"),
     (synth.LayerShape("ragged-fp32", 300, 96, 6, 3, 32, 100, "f32", 0.5), FP32_TOL, "max"),
+    (synth.LayerShape("odd-I-fp32", 200, 64, 4, 2, 16, 102, "f32", 0.5), FP32_TOL, "max"),
     (synth.LayerShape("ragged-bf16", 1000, 136, 4, 2, 48, 200, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("mid-bf16", 2048, 256, 8, 4, 64, 384, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("d128-bf16", 512, 512, 16, 8, 128, 256, "bf16", 0.5), BF16_TOL, "fro"),
