@@ -23,8 +23,9 @@
  *     they are float32.  gamma, gamma_next, r, r_next, wd_sq and every output
  *     are float32 in both cases.  Accumulation is float32.
  *   - Every tensor pointer is a device pointer owned by the caller; the
- *     library allocates no memory and keeps no state between calls.  Scratch
- *     space is the caller's workspace.  group maps are host arrays, read
+ *     library allocates no memory and keeps no state between calls (except
+ *     the rocBLAS handle of hna_affinity_loo, see there).  Scratch space is
+ *     the caller's workspace.  group maps are host arrays, read
  *     during the call only.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and runs asynchronously; nothing synchronises the host except
@@ -36,8 +37,9 @@
  *     Launch failures return HNA_ERR_HIP.  Nothing prints, aborts or throws.
  *   - Device pointers must be 16-byte aligned (HNA_ERR_ALIGNMENT otherwise).
  *   - The library is reentrant; its only global mutable state is the
- *     thread-local error text.  Calls that share a workspace or an output
- *     must be ordered on one stream by the caller.
+ *     thread-local error text and hna_affinity_loo's rocBLAS handles.  Calls
+ *     that share a workspace or an output must be ordered on one stream by
+ *     the caller.
  *
  * Supported shapes: H <= 128, 1 <= G <= H, H % G == 0, 0 <= group_of_head[h]
  * < G; d a multiple of 16 with d <= 128; hidden >= 1; I >= 1; T >= 0.
@@ -210,17 +212,25 @@ size_t hna_loo_workspace_bytes(const hna_dims* dims);
  *   g_k^(-h) = (gamma * (x - o_h) / r_h) . w^g_k   (u likewise)
  *   S_loo[g, k] = scale * sum_{h in g} sum_t ((g_k - g_k^(-h))^2 + (u_k - u_k^(-h))^2)
  * (scale = 1/T gives the mean over tokens).  Computed exactly through
- *   g_k - g_k^(-h) = (1 - r/r_h) g_k + (a_h . m_hk) / r_h,
- * with m_hk the folded weights of hna_fold_up_weights (M) and
- * r_h^2 = (|x|^2 - 2 x.o_h + |o_h|^2) / hidden from x itself.
+ *   g_k - g_k^(-h) = alpha_th g_k + beta_th (a_h . m_hk),
+ *   alpha_th = 1 - r/r_h,  beta_th = 1/r_h,
+ * with m_hk the folded weights of hna_fold_up_weights (M) and r_h from |x|^2,
+ * x . o_h and |o_h|^2; the square is summed as three terms (alpha^2 g^2, the
+ * cross term through two token GEMMs, beta^2 P^2 through weighted Gram
+ * matrices).
  *   a [T, H, d], g, u [T, I], W_o [hidden, H*d], M: the input dtype
  *   x fp32 [T, hidden]: the residual entering the FFN pre-norm (the g and u
  *     given must be its pre-activations)
  *   S_loo fp32 [G, I] output (written, also for T = 0: zeros)
  * A token whose residual vanishes without head h (r_h = 0) contributes
- * nothing for that head.  Limits: those of hna_affinity_up, and
- * 2*128*(slots of d)*16 + 2*128*H*8 + G*1024 bytes of LDS <= 160 KiB
- * (HNA_ERR_UNSUPPORTED otherwise).  Deterministic (fixed-order sums).
+ * nothing for that head.  Limits: those of hna_affinity_up and T < 2^31.
+ * Deterministic (fixed-order sums in the library's own kernels; the plain
+ * GEMMs run through rocBLAS).
+ * rocBLAS: this call runs five plain GEMMs through one rocBLAS handle per
+ * device, created at the first call on that device and kept until the
+ * process ends (calls are serialised on it); rocBLAS's workspace is a slice
+ * of the caller's workspace.  This is the library's only state besides the
+ * thread-local error text.
  */
 int hna_affinity_loo(const hna_dims* dims, const void* a, const void* g, const void* u,
                      const float* x, const void* W_o, const void* M,
