@@ -59,6 +59,8 @@ def check(got, ref, tol, metric):
     (synth.LayerShape("ragged-bf16", 1000, 136, 4, 2, 48, 200, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("mid-bf16", 2048, 256, 8, 4, 64, 384, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("d128-bf16", 512, 512, 16, 8, 128, 256, "bf16", 0.5), BF16_TOL, "fro"),
+    # the Danube3-500M layer shape (head dim 96), fewer tokens and neurons
+    (synth.LayerShape("danube-shape-bf16", 1024, 1536, 16, 8, 96, 512, "bf16", 0.5), BF16_TOL, "fro"),
 ])
 def test_loo_matches_oracle(hna, shape, tol, metric):
     layer = synth.make_layer(shape, seed=17, device="cuda", with_next=False, with_x=True)
