@@ -14,9 +14,11 @@
 //   gram_reduce   fixed-order sum over the token chunks;
 //   quad_kernel   Y = C_h M_h(:, block) on the matrix cores, then
 //                 add[g][k] = sum_{h in g} sum_{gate, up} m_hk . Y(:, k).
-// bf16 path: the scaled operand a / r^2 and the reduced fp32 Gram entries are
-// split into two bf16 terms (hi + lo), so products stay exact in fp32 and the
-// split leaves a relative error near 2^-16.  f32 path: fp32 MFMA throughout.
+// bf16 path: a itself is exact; the scaled operand a / r^2 is rounded to bf16
+// once (an unbiased relative error <= 2^-9 per product, averaged over the
+// token sum), and the reduced fp32 Gram entries are split into two bf16 terms
+// (hi + lo) for the quadratic forms, a relative error near 2^-16 there.  f32
+// path: fp32 MFMA throughout.
 #include "hna_internal.h"
 
 namespace hna {
@@ -27,7 +29,7 @@ constexpr int kGThreads = 256;
 template <typename E> struct GramLds;
 template <> struct GramLds<__bf16> {
   static constexpr int kPitch = kGramStage + 8;   // elements; 144-byte rows
-  static constexpr int kBufs = 3;                 // a, (a / r^2) hi, (a / r^2) lo
+  static constexpr int kBufs = 2;                 // a, a / r^2 (rounded to bf16)
   static constexpr int kQ = 1;
 };
 template <> struct GramLds<float> {
@@ -128,18 +130,12 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
           }
           const uint32_t x01 = __builtin_amdgcn_perm(r[1], r[0], w0);
           const uint32_t x23 = __builtin_amdgcn_perm(r[3], r[2], w0);
-          float y[4], yl[4];
+          float y[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] = x[j][e] * wt[j];
-          const uint32_t h01 = pack_bf16x2(y[0], y[1]), h23 = pack_bf16x2(y[2], y[3]);
-          yl[0] = y[0] - bf16_bits_to_f32(h01 & 0xffffu);
-          yl[1] = y[1] - __uint_as_float(h01 & 0xffff0000u);
-          yl[2] = y[2] - bf16_bits_to_f32(h23 & 0xffffu);
-          yl[3] = y[3] - __uint_as_float(h23 & 0xffff0000u);
           *reinterpret_cast<uint2*>(&xs[0][base]) = make_uint2(x01, x23);
-          *reinterpret_cast<uint2*>(&xs[1][base]) = make_uint2(h01, h23);
-          *reinterpret_cast<uint2*>(&xs[2][base]) =
-              make_uint2(pack_bf16x2(yl[0], yl[1]), pack_bf16x2(yl[2], yl[3]));
+          *reinterpret_cast<uint2*>(&xs[1][base]) =
+              make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
         } else {
           *reinterpret_cast<float4*>(&xs[0][base]) = make_float4(x[0][e], x[1][e], x[2][e], x[3][e]);
           *reinterpret_cast<float4*>(&xs[1][base]) = make_float4(
@@ -167,11 +163,6 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
                                                      qq * (16 / sizeof(E)));
           }
           mma(acc[ti], af, bh);
-          if constexpr (sizeof(E) == 2) {
-            uint4 bl[1];
-            bl[0] = *reinterpret_cast<const uint4*>(&xs[2][(jt * 32 + (l & 31)) * TP + col]);
-            mma(acc[ti], af, bl);
-          }
         }
       }
     }
