@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "hna.h")
 def _lib():
     import head_neuron_affinity_amd as hna
     if not os.path.exists(hna.LIB_PATH):
-        pytest.skip("libhna.so not built (run __graft_entry__.build())")
+        pytest.skip("libhna.so not built (python -m head_neuron_affinity_amd.build_lib)")
     return hna
 
 
