@@ -524,7 +524,7 @@ LooWorkspace loo_workspace(const hna_dims* dm) {
   w.xx = o;        o += align256((size_t)dm->T * sizeof(float));
   w.xl = o;        o += dm->dtype == HNA_BF16 ? align256((size_t)dm->T * dm->hidden * 2) : 0;
   w.ZA = o;        o += align256(thd * es);   // x W_o, then a scaled by alpha beta
-  w.U = o;         o += align256(thd * es);
+  w.U = o;         o += loo_coef_fused(dm->d, dm->dtype) ? 0 : align256(thd * es);
   w.Q = o;         o += align256((size_t)dm->H * dm->d * dm->d * es);
   w.coef = o;      o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
   w.Y = o;         o += align256((size_t)2 * dm->H * dm->d * dm->I * sizeof(float));
@@ -682,18 +682,23 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
     if ((e = launch_x_prep(x, dm->T, D, xx, bf ? xl : nullptr, st)) != hipSuccess)
       return hip_fail(e, fn);
     const void* xg = bf ? xl : static_cast<const void*>(x);
+    const bool fused = loo_coef_fused(d, dt);
     if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, false, HD, T, D, W_o, dt, HD, 0, xg, dt, D,
                         0, ZA, dt, HD, 0, 1)) != 0 ||
         (bs = blas_gemm(st, bws, kBlasWorkspace, false, true, d, d, D, W_o, dt, HD, d, W_o, dt, HD,
                         d, Q, dt, d, (int64_t)d * d, dm->H)) != 0 ||
-        (bs = blas_gemm(st, bws, kBlasWorkspace, false, false, d, T, d, Q, dt, d, (int64_t)d * d, a,
-                        dt, HD, d, U, dt, HD, d, dm->H)) != 0)
+        (!fused && (bs = blas_gemm(st, bws, kBlasWorkspace, false, false, d, T, d, Q, dt, d,
+                                   (int64_t)d * d, a, dt, HD, d, U, dt, HD, d, dm->H)) != 0))
       return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
-    if ((e = launch_loo_coef(a, ZA, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess)
+    // 2. T2: Y^g = (alpha beta a)^T g and Y^u likewise, over the tokens, with
+    //    alpha beta a written over Z
+    if (fused) {
+      if ((e = launch_loo_coef_fused(a, ZA, Q, xx, dm->T, dm->H, d, D, coef, st)) != hipSuccess)
+        return hip_fail(e, fn);
+    } else if ((e = launch_loo_coef(a, ZA, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess ||
+               (e = launch_scale_a(a, coef, dm->T, dm->H, d, ZA, dt, st)) != hipSuccess) {
       return hip_fail(e, fn);
-    // 2. T2: Y^g = (alpha beta a)^T g and Y^u likewise, over the tokens
-    if ((e = launch_scale_a(a, coef, dm->T, dm->H, d, ZA, dt, st)) != hipSuccess)
-      return hip_fail(e, fn);
+    }
     for (int gu = 0; gu < 2; ++gu)
       if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, dm->I, T, ZA, dt, HD, 0,
                           gu ? u : g, dt, dm->I, 0, Y + (int64_t)gu * HD * dm->I, 0, HD, 0, 1)) != 0)

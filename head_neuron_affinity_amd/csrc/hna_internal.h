@@ -222,6 +222,12 @@ hipError_t launch_t1_reduce(const float* t1, int n_tc, int64_t HI, double* t1r, 
 hipError_t launch_x_prep(const float* x, int64_t T, int D, float* xx, void* xl, hipStream_t st);
 hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const float* xx, int64_t T,
                            int H, int d, int D, float2* coef, int dtype, hipStream_t st);
+// bf16 with d a multiple of 32 up to 128: the moments (|o_h|^2 on the matrix
+// cores from Q_h = W_o^(h)T W_o^(h)), alpha and beta, and alpha beta a written
+// over Z (ZA holds Z = x W_o on entry), in one kernel
+bool loo_coef_fused(int d, int dtype);
+hipError_t launch_loo_coef_fused(const void* a, void* ZA, const void* Q, const float* xx, int64_t T,
+                                 int H, int d, int D, float2* coef, hipStream_t st);
 hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, int d, void* As,
                           int dtype, hipStream_t st);
 int t1_chunks(int64_t T);

@@ -8,7 +8,7 @@
 //   alpha_th = 1 - r / r_h,  beta_th = 1 / r_h,
 // (m_hk the folded weights; u likewise), so that per head and neuron
 //   sum_t (...)^2 = T1 + 2 T2 + T3,
-//   T1 = sum_t alpha^2 (g^2 + u^2)                      (t1_kernel)
+//   T1 = sum_t alpha^2 (g^2 + u^2)      (t1_kernel, fp32 matrix cores)
 //   T2 = m^g_hk . Y^g_h[:, k] + m^u_hk . Y^u_h[:, k],  Y_h = sum_t alpha beta a_th g_t^T
 //        (two plain GEMMs over the tokens, by rocBLAS, on a scaled by alpha beta)
 //   T3 = m^T C_h m,  C_h = sum_t beta_th^2 a_th a_th^T   (the Gram and quadratic-
@@ -152,100 +152,239 @@ __global__ __launch_bounds__(256) void scale_a_kernel(const E* __restrict__ a,
   }
 }
 
-// T1 partial sums: t1[tc][h][k] = sum over token chunk tc of alpha_th^2 (g_tk^2 + u_tk^2);
-// heads in blocks of 16, the chunk's squared alphas staged in LDS 256 tokens at
-// a time; V consecutive neurons per thread (V = 4 needs I % 4 == 0), eight
-// tokens' loads in flight
-constexpr int kT1Chunk = 512, kT1Stage = 256, kT1Heads = 16;
-
-__device__ inline void load_v(const __bf16* p, float (&v)[4]) {
-  const uint2 q = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
-  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+// bf16 element e of 8 packed in a uint4
+__device__ inline float bf16_at(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
-__device__ inline void load_v(const float* p, float (&v)[4]) {
-  const float4 q = *reinterpret_cast<const float4*>(p);
-  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-}
-__device__ inline void load_v(const __bf16* p, float (&v)[1]) { v[0] = load_elem(p, 0); }
-__device__ inline void load_v(const float* p, float (&v)[1]) { v[0] = p[0]; }
 
-template <typename E, int V>
-__global__ __launch_bounds__(256) void t1_kernel(const E* __restrict__ g, const E* __restrict__ u,
-                                                 const float2* __restrict__ coef, int64_t T,
-                                                 int H, int I, float* __restrict__ t1) {
-  __shared__ __attribute__((aligned(16))) float al2[kT1Stage][kT1Heads];
-  const int k0 = (blockIdx.x * 256 + threadIdx.x) * V;
-  const int tc = blockIdx.y;
-  const int64_t t0 = (int64_t)tc * kT1Chunk, t1e = min(T, t0 + kT1Chunk);
-  for (int h0 = 0; h0 < H; h0 += kT1Heads) {
-    const int nh = min(kT1Heads, H - h0);
-    float acc[V][kT1Heads];
+// bf16 inputs with d = 32 ND: the moments, alpha and beta, and the scaled
+// head outputs in one pass over a and Z, with |o_h|^2 = a . (Q_h a) on the
+// matrix cores.  One workgroup per (token range, head) stages Q_h in LDS (Q_h
+// is symmetric, so its column-major GEMM output reads as row-major); each
+// wave takes 32 tokens at a time and forms V^T = Q_h a^T with 32x32x16 MFMAs:
+// lane l holds, as the B operand, features 16 kk + 8 (l / 32) .. + 7 of token
+// l % 32, and MFMA row m of tile mt stands for Q_h row
+// 32 mt + 16 (m / 16) + 8 ((m / 4) % 2) + 4 ((m / 8) % 2) + m % 4, which puts
+// every entry of V that a lane receives on a feature whose a value the lane
+// already holds.  x . o_h = Z . a is dotted over the same features; one
+// exchange between the wave's halves completes both sums.  Z is overwritten,
+// in place, by alpha beta a (rounded to bf16).
+constexpr int kCoefBlocksPerHead = 64;
+
+template <int ND>
+__global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __restrict__ a,
+                                                            __bf16* ZA,
+                                                            const __bf16* __restrict__ Q,
+                                                            const float* __restrict__ xx,
+                                                            int64_t T, int H, int D,
+                                                            float2* __restrict__ coef) {
+  constexpr int d = 32 * ND, KK = 2 * ND, QS = d + 8;  // LDS row stride, elements
+  __shared__ __attribute__((aligned(16))) uint16_t qs[d * QS];
+  const int h = blockIdx.y;
+  const uint16_t* qh = reinterpret_cast<const uint16_t*>(Q) + (int64_t)h * d * d;
+  for (int i = threadIdx.x; i < d * d / 8; i += 256) {
+    const int r = (i * 8) / d, c = i * 8 - r * d;
+    *reinterpret_cast<uint4*>(qs + r * QS + c) = *reinterpret_cast<const uint4*>(qh + i * 8);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, hh = lane >> 5, tl = lane & 31;
+  const int prow = 16 * (tl >> 4) + 8 * ((tl >> 2) & 1) + 4 * ((tl >> 3) & 1) + (tl & 3);
+  const uint16_t* ap = reinterpret_cast<const uint16_t*>(a);
+  uint16_t* zp = reinterpret_cast<uint16_t*>(ZA);
+  const int64_t n_tiles = (T + 31) / 32;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tile < n_tiles;
+       tile += (int64_t)gridDim.x * 4) {
+    const int64_t t = tile * 32 + tl;
+    const bool ok = t < T;
+    const int64_t base = ((ok ? t : 0) * H + h) * d + 8 * hh;
+    // re-read the Q_h fragments from LDS on every tile rather than holding all
+    // of them in registers across the loop (an opaque offset stops the hoist)
+    int qoff = prow * QS + 8 * hh;
+    asm volatile("" : "+v"(qoff));
+    uint4 ar[KK];
 #pragma unroll
-    for (int c = 0; c < V; ++c)
+    for (int kk = 0; kk < KK; ++kk)
+      ar[kk] = ok ? *reinterpret_cast<const uint4*>(ap + base + 16 * kk) : make_uint4(0, 0, 0, 0);
+    float oo = 0.f, xo = 0.f;
 #pragma unroll
-      for (int i = 0; i < kT1Heads; ++i) acc[c][i] = 0.f;
-    for (int64_t ts = t0; ts < t1e; ts += kT1Stage) {
-      __syncthreads();
-      for (int e = threadIdx.x; e < kT1Stage * kT1Heads; e += 256) {
-        const int tt = e / kT1Heads, hh = e - tt * kT1Heads;
-        const int64_t t = ts + tt;
-        float a2 = 0.f;
-        if (t < t1e && hh < nh) {
-          const float al = coef[t * H + h0 + hh].x;
-          a2 = al * al;
-        }
-        al2[tt][hh] = a2;
+    for (int mt = 0; mt < ND; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(qs + qoff + 32 * mt * QS + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa),
+                                                      __builtin_bit_cast(bf16x8, ar[kk]), acc, 0, 0, 0);
       }
-      __syncthreads();
-      if (k0 < I) {
-        const int n = (int)min((int64_t)kT1Stage, t1e - ts);
-        for (int tt0 = 0; tt0 < n; tt0 += 8) {
-          float q[8][V];
+      // entry r: row 8 (r / 4) + 4 hh + r % 4, i.e. element 4 ((r / 4) % 2) + r % 4
+      // of chunk 2 mt + r / 8
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int64_t t = ts + (tt0 + e < n ? tt0 + e : 0);   // past n: row ts, weight 0
-            float gv[V], uv[V];
-            load_v(g + t * I + k0, gv);
-            load_v(u + t * I + k0, uv);
-#pragma unroll
-            for (int c = 0; c < V; ++c) q[e][c] = tt0 + e < n ? fmaf(gv[c], gv[c], uv[c] * uv[c]) : 0.f;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-#pragma unroll
-            for (int i4 = 0; i4 < kT1Heads / 4; ++i4) {
-              const float4 w = *reinterpret_cast<const float4*>(&al2[tt0 + e][4 * i4]);
-#pragma unroll
-              for (int c = 0; c < V; ++c) {
-                acc[c][4 * i4] = fmaf(w.x, q[e][c], acc[c][4 * i4]);
-                acc[c][4 * i4 + 1] = fmaf(w.y, q[e][c], acc[c][4 * i4 + 1]);
-                acc[c][4 * i4 + 2] = fmaf(w.z, q[e][c], acc[c][4 * i4 + 2]);
-                acc[c][4 * i4 + 3] = fmaf(w.w, q[e][c], acc[c][4 * i4 + 3]);
-              }
-            }
-          }
-        }
-      }
+      for (int r = 0; r < 16; ++r)
+        oo = fmaf(acc[r], bf16_at(ar[2 * mt + (r >> 3)], 4 * ((r >> 2) & 1) + (r & 3)), oo);
     }
-    if (k0 < I) {
 #pragma unroll
-      for (int i = 0; i < kT1Heads; ++i)   // compile-time indices keep acc in registers
-        if (i < nh)
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 z = ok ? *reinterpret_cast<const uint4*>(zp + base + 16 * kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int c = 0; c < V; ++c) t1[((int64_t)tc * H + h0 + i) * I + k0 + c] = acc[c][i];
+      for (int e = 0; e < 8; ++e) xo = fmaf(bf16_at(z, e), bf16_at(ar[kk], e), xo);
+    }
+    xo += __shfl_xor(xo, 32);
+    oo += __shfl_xor(oo, 32);
+    if (!ok) continue;
+    const double x2 = (double)xx[t];
+    const double den = x2 - 2.0 * (double)xo + (double)oo;
+    float2 c = make_float2(0.f, 0.f);
+    if (den > 0.0 && x2 > 0.0) {
+      c.x = (float)(1.0 - sqrt(x2 / den));
+      c.y = (float)sqrt((double)D / den);
+    }
+    if (hh == 0) coef[t * H + h] = c;
+    const float w = c.x * c.y;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 v = ar[kk];
+      *reinterpret_cast<uint4*>(zp + base + 16 * kk) =
+          make_uint4(pack_bf16x2(bf16_at(v, 0) * w, bf16_at(v, 1) * w),
+                     pack_bf16x2(bf16_at(v, 2) * w, bf16_at(v, 3) * w),
+                     pack_bf16x2(bf16_at(v, 4) * w, bf16_at(v, 5) * w),
+                     pack_bf16x2(bf16_at(v, 6) * w, bf16_at(v, 7) * w));
     }
   }
 }
 
-// t1r[h][k] = sum over the token chunks, in order, of t1[tc][h][k] (float64)
+// T1 partial sums: t1[tc][h][k] = sum over token chunk tc of alpha_th^2 (g_tk^2 + u_tk^2),
+// a [heads x tokens] x [tokens x neurons] product, on the fp32 matrix cores
+// (16x16x4: 16 heads x 16 neuron columns, 4 tokens per step).  One wave per
+// 128 neurons and chunk: lane l takes token l/16 of each step of 4 and the 8
+// consecutive neurons 8 (l % 16) .. +7 (one 16-byte load of g and of u for
+// bf16), so that MFMA e of a step sees column n as neuron 8 n + e; its A
+// operand is alpha^2 of (token l/16, head l % 16).  Token and neuron tails and
+// heads past H enter as zeros; heads in blocks of 16.  VEC (I % 8 == 0) loads
+// the 8 neurons at once, else one at a time.
+constexpr int kT1Chunk = 512, kT1Cols = 128, kT1Steps = 2;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive g or u elements of one row as raw words (bf16 pairs when VEC,
+// else fp32 bit patterns), zeros where ok is false or past the row's end
+template <typename E, bool VEC>
+constexpr int raw_words() { return (VEC && sizeof(E) == 2) ? 4 : 8; }
+
+template <typename E, bool VEC>
+__device__ inline void load_raw(const E* __restrict__ p, int64_t row, int c0, int I, bool ok,
+                                uint32_t (&r)[raw_words<E, VEC>()]) {
+  if constexpr (VEC && sizeof(E) == 2) {
+    const uint4 q = ok ? *reinterpret_cast<const uint4*>(p + row * I + c0) : make_uint4(0, 0, 0, 0);
+    r[0] = q.x; r[1] = q.y; r[2] = q.z; r[3] = q.w;
+  } else if constexpr (VEC) {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 a = ok ? reinterpret_cast<const float4*>(p + row * I + c0)[0] : z;
+    const float4 b = ok ? reinterpret_cast<const float4*>(p + row * I + c0)[1] : z;
+    r[0] = __float_as_uint(a.x); r[1] = __float_as_uint(a.y); r[2] = __float_as_uint(a.z);
+    r[3] = __float_as_uint(a.w); r[4] = __float_as_uint(b.x); r[5] = __float_as_uint(b.y);
+    r[6] = __float_as_uint(b.z); r[7] = __float_as_uint(b.w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      r[e] = __float_as_uint((ok && c0 + e < I) ? load_elem(p, row * I + c0 + e) : 0.f);
+  }
+}
+
+template <typename E, bool VEC>
+__device__ inline float raw_at(const uint32_t (&r)[raw_words<E, VEC>()], int e) {
+  if constexpr (VEC && sizeof(E) == 2)
+    return __uint_as_float((e & 1) ? (r[e >> 1] & 0xffff0000u) : (r[e >> 1] << 16));
+  else
+    return __uint_as_float(r[e]);
+}
+
+template <typename E, bool VEC>
+__global__ __launch_bounds__(256) void t1_kernel(const E* __restrict__ g, const E* __restrict__ u,
+                                                 const float2* __restrict__ coef, int64_t T,
+                                                 int H, int I, float* __restrict__ t1) {
+  constexpr int NW = raw_words<E, VEC>();
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile * kT1Cols >= I) return;  // whole wave
+  const int c0 = tile * kT1Cols + 8 * (lane & 15);
+  const int kq = lane >> 4;
+  const bool col_ok = c0 < I;
+  const int64_t t0 = (int64_t)blockIdx.y * kT1Chunk, te = min(T, t0 + kT1Chunk);
+  for (int h0 = 0; h0 < H; h0 += 16) {
+    const int ha = h0 + (lane & 15);  // head of this lane's A element
+    f32x4 acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the next group of 4 kT1Steps tokens is fetched before this group's MFMAs
+    uint32_t rg[kT1Steps][NW], ru[kT1Steps][NW];
+    float al[kT1Steps];
+    auto fetch = [&](int64_t t) {
+#pragma unroll
+      for (int s = 0; s < kT1Steps; ++s) {
+        const int64_t tt = t + 4 * s + kq;
+        const bool ok = tt < te;
+        const int64_t row = ok ? tt : t0;  // rows past the chunk read row t0 and weigh 0
+        load_raw<E, VEC>(g, row, c0, I, col_ok, rg[s]);
+        load_raw<E, VEC>(u, row, c0, I, col_ok, ru[s]);
+        al[s] = (ok && ha < H) ? coef[row * H + ha].x : 0.f;
+      }
+    };
+    fetch(t0);
+    for (int64_t t = t0; t < te; t += 4 * kT1Steps) {
+      float w[kT1Steps][8], a2[kT1Steps];
+#pragma unroll
+      for (int s = 0; s < kT1Steps; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float gv = raw_at<E, VEC>(rg[s], e), uv = raw_at<E, VEC>(ru[s], e);
+          w[s][e] = fmaf(gv, gv, uv * uv);
+        }
+        a2[s] = al[s] * al[s];
+      }
+      if (t + 4 * kT1Steps < te) fetch(t + 4 * kT1Steps);
+#pragma unroll
+      for (int s = 0; s < kT1Steps; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[s], w[s][e], acc[e], 0, 0, 0);
+    }
+    // lane l holds rows 4 (l / 16) + r (heads) of column l % 16 (neurons c0 + e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = h0 + 4 * kq + r;
+      if (h >= H) continue;
+      float* dst = t1 + ((int64_t)blockIdx.y * H + h) * I + c0;
+      if (VEC) {
+        if (col_ok) {
+          reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+          reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c0 + e < I) dst[e] = acc[e][r];
+      }
+    }
+  }
+}
+
+// t1r[h][k] = sum over the token chunks of t1[tc][h][k] (float64): four threads
+// per output each sum a quarter of the chunks in order, then the quarters are
+// added in order
 __global__ __launch_bounds__(256) void t1_reduce_kernel(const float* __restrict__ t1, int n_tc,
                                                         int64_t HI, double* __restrict__ t1r) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= HI) return;
+  __shared__ double part[4][64];
+  const int o = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + o;
+  const int per = (n_tc + 3) / 4;
+  const int b = q * per, e = min(n_tc, b + per);
   double s = 0.0;
-  for (int tc = 0; tc < n_tc; ++tc) s += (double)t1[(int64_t)tc * HI + i];
-  t1r[i] = s;
+  if (i < HI) {
+#pragma unroll 8
+    for (int tc = b; tc < e; ++tc) s += (double)t1[(int64_t)tc * HI + i];
+  }
+  part[q][o] = s;
+  __syncthreads();
+  if (q == 0 && i < HI) t1r[i] = ((part[0][o] + part[1][o]) + part[2][o]) + part[3][o];
 }
 
 // S_loo[g][k] = scale * (sum_{h in g} (T1 + 2 T2) + T3[g][k]).  One wave per
@@ -326,31 +465,52 @@ hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, i
   return hipGetLastError();
 }
 
+bool loo_coef_fused(int d, int dtype) { return dtype == 1 && d % 32 == 0 && d >= 32 && d <= 128; }
+
+hipError_t launch_loo_coef_fused(const void* a, void* ZA, const void* Q, const float* xx, int64_t T,
+                                 int H, int d, int D, float2* coef, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int64_t n_tiles = (T + 31) / 32;
+  const int64_t bx = (n_tiles + 3) / 4;
+  const dim3 grid((unsigned)(bx < kCoefBlocksPerHead ? bx : kCoefBlocksPerHead), (unsigned)H);
+  const auto* ab = static_cast<const __bf16*>(a);
+  auto* zb = static_cast<__bf16*>(ZA);
+  const auto* qb = static_cast<const __bf16*>(Q);
+  switch (d / 32) {
+    case 1: hipLaunchKernelGGL(loo_coef_mfma_kernel<1>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
+    case 2: hipLaunchKernelGGL(loo_coef_mfma_kernel<2>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
+    case 3: hipLaunchKernelGGL(loo_coef_mfma_kernel<3>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
+    case 4: hipLaunchKernelGGL(loo_coef_mfma_kernel<4>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 int t1_chunks(int64_t T) { return (int)((T + kT1Chunk - 1) / kT1Chunk); }
 
 hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T, int H, int I,
                      float* t1, int dtype, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  const bool vec = I % 4 == 0;
-  const int per = vec ? 4 : 1;
-  const dim3 grid((I / per + 255) / 256 + ((I % per) ? 1 : 0), t1_chunks(T));
+  if (T == 0 || I == 0) return hipSuccess;
+  const bool vec = I % 8 == 0;
+  const int tiles = (I + kT1Cols - 1) / kT1Cols;
+  const dim3 grid((tiles + 3) / 4, t1_chunks(T));
   if (dtype == 1) {
     const auto* gb = static_cast<const __bf16*>(g);
     const auto* ub = static_cast<const __bf16*>(u);
-    if (vec) hipLaunchKernelGGL((t1_kernel<__bf16, 4>), grid, dim3(256), 0, st, gb, ub, coef, T, H, I, t1);
-    else hipLaunchKernelGGL((t1_kernel<__bf16, 1>), grid, dim3(256), 0, st, gb, ub, coef, T, H, I, t1);
+    if (vec) hipLaunchKernelGGL((t1_kernel<__bf16, true>), grid, dim3(256), 0, st, gb, ub, coef, T, H, I, t1);
+    else hipLaunchKernelGGL((t1_kernel<__bf16, false>), grid, dim3(256), 0, st, gb, ub, coef, T, H, I, t1);
   } else {
     const auto* gf = static_cast<const float*>(g);
     const auto* uf = static_cast<const float*>(u);
-    if (vec) hipLaunchKernelGGL((t1_kernel<float, 4>), grid, dim3(256), 0, st, gf, uf, coef, T, H, I, t1);
-    else hipLaunchKernelGGL((t1_kernel<float, 1>), grid, dim3(256), 0, st, gf, uf, coef, T, H, I, t1);
+    if (vec) hipLaunchKernelGGL((t1_kernel<float, true>), grid, dim3(256), 0, st, gf, uf, coef, T, H, I, t1);
+    else hipLaunchKernelGGL((t1_kernel<float, false>), grid, dim3(256), 0, st, gf, uf, coef, T, H, I, t1);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_t1_reduce(const float* t1, int n_tc, int64_t HI, double* t1r, hipStream_t st) {
   if (HI == 0) return hipSuccess;
-  hipLaunchKernelGGL(t1_reduce_kernel, dim3((unsigned)((HI + 255) / 256)), dim3(256), 0, st, t1,
+  hipLaunchKernelGGL(t1_reduce_kernel, dim3((unsigned)((HI + 63) / 64)), dim3(256), 0, st, t1,
                      n_tc, HI, t1r);
   return hipGetLastError();
 }

@@ -58,6 +58,8 @@ def check(got, ref, tol, metric):
     (synth.LayerShape("odd-I-fp32", 200, 64, 4, 2, 16, 102, "f32", 0.5), FP32_TOL, "max"),
     (synth.LayerShape("ragged-bf16", 1000, 136, 4, 2, 48, 200, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("mid-bf16", 2048, 256, 8, 4, 64, 384, "bf16", 0.5), BF16_TOL, "fro"),
+    # head dim 32 and a token count off the 32-token tile
+    (synth.LayerShape("d32-ragged-bf16", 999, 128, 4, 2, 32, 200, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("d128-bf16", 512, 512, 16, 8, 128, 256, "bf16", 0.5), BF16_TOL, "fro"),
     # the Danube3-500M layer shape (head dim 96), fewer tokens and neurons
     (synth.LayerShape("danube-shape-bf16", 1024, 1536, 16, 8, 96, 512, "bf16", 0.5), BF16_TOL, "fro"),
