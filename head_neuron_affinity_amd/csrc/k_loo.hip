@@ -30,6 +30,8 @@
 namespace hna {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kXRows = 4;  // rows of x per 256-thread block (one wave each)
 
 // |x_t|^2 (one wave per row, fixed order) and, when xl is given, x rounded to
@@ -162,15 +164,15 @@ __device__ inline float bf16_at(const uint4& v, int e) {
 // head outputs in one pass over a and Z, with |o_h|^2 = a . (Q_h a) on the
 // matrix cores.  One workgroup per (token range, head) stages Q_h in LDS (Q_h
 // is symmetric, so its column-major GEMM output reads as row-major); each
-// wave takes 32 tokens at a time and forms V^T = Q_h a^T with 32x32x16 MFMAs:
-// lane l holds, as the B operand, features 16 kk + 8 (l / 32) .. + 7 of token
-// l % 32, and MFMA row m of tile mt stands for Q_h row
-// 32 mt + 16 (m / 16) + 8 ((m / 4) % 2) + 4 ((m / 8) % 2) + m % 4, which puts
-// every entry of V that a lane receives on a feature whose a value the lane
-// already holds.  x . o_h = Z . a is dotted over the same features; one
-// exchange between the wave's halves completes both sums.  Z is overwritten,
-// in place, by alpha beta a (rounded to bf16).
-constexpr int kCoefBlocksPerHead = 64;
+// wave takes 16 tokens at a time and forms V^T = Q_h a^T with 16x16x32 MFMAs:
+// lane l holds, as the B operand, features 32 ks + 8 (l / 16) .. + 7 of token
+// l % 16, and row m of MFMA tile mt stands for Q_h row
+// 32 (mt / 2) + 8 (m / 4) + 4 (mt % 2) + m % 4, which puts every entry of V
+// that a lane receives on a feature whose a value the lane already holds.
+// x . o_h = Z . a is dotted over the same features; two exchanges across the
+// wave's quarters complete both sums.  Z is overwritten, in place, by
+// alpha beta a (rounded to bf16).
+constexpr int kCoefBlocksPerHead = 128;
 
 template <int ND>
 __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __restrict__ a,
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
                                                             const float* __restrict__ xx,
                                                             int64_t T, int H, int D,
                                                             float2* __restrict__ coef) {
-  constexpr int d = 32 * ND, KK = 2 * ND, QS = d + 8;  // LDS row stride, elements
+  constexpr int d = 32 * ND, QS = d + 8;  // LDS row stride, elements
   __shared__ __attribute__((aligned(16))) uint16_t qs[d * QS];
   const int h = blockIdx.y;
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(Q) + (int64_t)h * d * d;
@@ -188,46 +190,57 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
     *reinterpret_cast<uint4*>(qs + r * QS + c) = *reinterpret_cast<const uint4*>(qh + i * 8);
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, hh = lane >> 5, tl = lane & 31;
-  const int prow = 16 * (tl >> 4) + 8 * ((tl >> 2) & 1) + 4 * ((tl >> 3) & 1) + (tl & 3);
+  const int lane = threadIdx.x & 63, qq = lane >> 4, tl = lane & 15;
   const uint16_t* ap = reinterpret_cast<const uint16_t*>(a);
   uint16_t* zp = reinterpret_cast<uint16_t*>(ZA);
-  const int64_t n_tiles = (T + 31) / 32;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)gridDim.x * 4) {
-    const int64_t t = tile * 32 + tl;
+  const int64_t n_tiles = (T + 15) / 16;
+  const int64_t step = (int64_t)gridDim.x * 4;
+  int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  uint4 ar[ND], zr[ND];
+  auto fetch = [&](int64_t tt) {
+    const int64_t t = tt * 16 + tl;
+    const bool ok = tt < n_tiles && t < T;
+    const int64_t base = ((ok ? t : 0) * H + h) * d + 8 * qq;
+#pragma unroll
+    for (int ks = 0; ks < ND; ++ks) {
+      ar[ks] = ok ? *reinterpret_cast<const uint4*>(ap + base + 32 * ks) : make_uint4(0, 0, 0, 0);
+      zr[ks] = ok ? *reinterpret_cast<const uint4*>(zp + base + 32 * ks) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(tile);
+  for (; tile < n_tiles; tile += step) {
+    uint4 a_cur[ND], z_cur[ND];
+#pragma unroll
+    for (int ks = 0; ks < ND; ++ks) { a_cur[ks] = ar[ks]; z_cur[ks] = zr[ks]; }
+    if (tile + step < n_tiles) fetch(tile + step);  // the next tile loads under this one's work
+    const int64_t t = tile * 16 + tl;
     const bool ok = t < T;
-    const int64_t base = ((ok ? t : 0) * H + h) * d + 8 * hh;
+    const int64_t base = ((ok ? t : 0) * H + h) * d + 8 * qq;
     // re-read the Q_h fragments from LDS on every tile rather than holding all
     // of them in registers across the loop (an opaque offset stops the hoist)
-    int qoff = prow * QS + 8 * hh;
+    int qoff = (8 * (tl >> 2) + (tl & 3)) * QS + 8 * qq;
     asm volatile("" : "+v"(qoff));
-    uint4 ar[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      ar[kk] = ok ? *reinterpret_cast<const uint4*>(ap + base + 16 * kk) : make_uint4(0, 0, 0, 0);
     float oo = 0.f, xo = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < ND; ++mt) {
-      f32x16 acc = {};
+    for (int mt = 0; mt < 2 * ND; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int rbase = 32 * (mt >> 1) + 4 * (mt & 1);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(qs + qoff + 32 * mt * QS + 16 * kk);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa),
-                                                      __builtin_bit_cast(bf16x8, ar[kk]), acc, 0, 0, 0);
+      for (int ks = 0; ks < ND; ++ks) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(qs + qoff + rbase * QS + 32 * ks);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa),
+                                                      __builtin_bit_cast(bf16x8, a_cur[ks]), acc, 0, 0, 0);
       }
-      // entry r: row 8 (r / 4) + 4 hh + r % 4, i.e. element 4 ((r / 4) % 2) + r % 4
-      // of chunk 2 mt + r / 8
+      // entry r is row 4 qq + r: element 4 (mt % 2) + r of chunk mt / 2
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        oo = fmaf(acc[r], bf16_at(ar[2 * mt + (r >> 3)], 4 * ((r >> 2) & 1) + (r & 3)), oo);
+      for (int r = 0; r < 4; ++r) oo = fmaf(acc[r], bf16_at(a_cur[mt >> 1], 4 * (mt & 1) + r), oo);
     }
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint4 z = ok ? *reinterpret_cast<const uint4*>(zp + base + 16 * kk) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < ND; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xo = fmaf(bf16_at(z, e), bf16_at(ar[kk], e), xo);
-    }
+      for (int e = 0; e < 8; ++e) xo = fmaf(bf16_at(z_cur[ks], e), bf16_at(a_cur[ks], e), xo);
+    xo += __shfl_xor(xo, 16);
+    oo += __shfl_xor(oo, 16);
     xo += __shfl_xor(xo, 32);
     oo += __shfl_xor(oo, 32);
     if (!ok) continue;
@@ -238,12 +251,12 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
       c.x = (float)(1.0 - sqrt(x2 / den));
       c.y = (float)sqrt((double)D / den);
     }
-    if (hh == 0) coef[t * H + h] = c;
+    if (qq == 0) coef[t * H + h] = c;
     const float w = c.x * c.y;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint4 v = ar[kk];
-      *reinterpret_cast<uint4*>(zp + base + 16 * kk) =
+    for (int ks = 0; ks < ND; ++ks) {
+      const uint4 v = a_cur[ks];
+      *reinterpret_cast<uint4*>(zp + base + 32 * ks) =
           make_uint4(pack_bf16x2(bf16_at(v, 0) * w, bf16_at(v, 1) * w),
                      pack_bf16x2(bf16_at(v, 2) * w, bf16_at(v, 3) * w),
                      pack_bf16x2(bf16_at(v, 4) * w, bf16_at(v, 5) * w),
@@ -262,7 +275,6 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
 // heads past H enter as zeros; heads in blocks of 16.  VEC (I % 8 == 0) loads
 // the 8 neurons at once, else one at a time.
 constexpr int kT1Chunk = 512, kT1Cols = 128, kT1Steps = 2;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 8 consecutive g or u elements of one row as raw words (bf16 pairs when VEC,
 // else fp32 bit patterns), zeros where ok is false or past the row's end
@@ -470,7 +482,7 @@ bool loo_coef_fused(int d, int dtype) { return dtype == 1 && d % 32 == 0 && d >=
 hipError_t launch_loo_coef_fused(const void* a, void* ZA, const void* Q, const float* xx, int64_t T,
                                  int H, int d, int D, float2* coef, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const int64_t n_tiles = (T + 31) / 32;
+  const int64_t n_tiles = (T + 15) / 16;
   const int64_t bx = (n_tiles + 3) / 4;
   const dim3 grid((unsigned)(bx < kCoefBlocksPerHead ? bx : kCoefBlocksPerHead), (unsigned)H);
   const auto* ab = static_cast<const __bf16*>(a);
