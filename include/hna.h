@@ -226,7 +226,8 @@ size_t hna_loo_workspace_bytes(const hna_dims* dims);
  * nothing for that head.  Limits: those of hna_affinity_up and T < 2^31.
  * Deterministic (fixed-order sums in the library's own kernels; the plain
  * GEMMs run through rocBLAS).
- * rocBLAS: this call runs five plain GEMMs through one rocBLAS handle per
+ * rocBLAS: this call runs four plain GEMMs (five for fp32 inputs or a head
+ * dim that is not 32, 64, 96 or 128) through one rocBLAS handle per
  * device, created at the first call on that device and kept until the
  * process ends (calls are serialised on it); rocBLAS's workspace is a slice
  * of the caller's workspace.  This is the library's only state besides the
