@@ -40,8 +40,27 @@ template <> struct GramLds<float> {
 
 __device__ inline uint16_t bf16_rn(float x) { return (uint16_t)f32_to_bf16_bits(x); }
 
+// Output tiles of 32 x 32 owned by wave w (NT x NT tiles in all): with NT >= 3
+// a 2 x 2 block, tiles (2 (w / 2) + x, 2 (w % 2) + y), so that each MFMA
+// operand fragment read from LDS serves two MFMAs; with NT <= 2 the single
+// tile (w / NT, w % NT).  Slot s of the wave's accumulators is (x, y) =
+// (s / 2, s % 2); tiles past NT are skipped.
+template <int NT>
+__device__ inline bool gram_tile(int w, int s, int& it, int& jt) {
+  if constexpr (NT >= 3) {
+    it = 2 * (w >> 1) + (s >> 1);
+    jt = 2 * (w & 1) + (s & 1);
+    return NT == 4 || (it < NT && jt < NT);   // NT = 4: every slot (w < 4)
+  } else {
+    it = w / NT;
+    jt = w % NT;
+    return s == 0 && w < NT * NT;
+  }
+}
+
 // grid: n_gc * H workgroups (head fastest); C_part[gc][h] = sum over chunk gc.
-template <typename E>
+// NT = ceil(d / 32).
+template <typename E, int NT>
 __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
   using L = GramLds<E>;
   constexpr int TP = L::kPitch;
@@ -51,8 +70,7 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
   const int h = blockIdx.x % p.H;
   const int gc = blockIdx.x / p.H;
   const int d = p.d;
-  const int d32 = (d + 31) & ~31;
-  const int nt = d32 >> 5;
+  const int d32 = 32 * NT;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int64_t t_begin = (int64_t)gc * p.chunk_tokens;
   const int64_t t_end = min(p.T, t_begin + p.chunk_tokens);
@@ -67,40 +85,64 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
-  // One (4 tokens) x (8 features) item per thread (d <= 128); the next
-  // stage's item is loaded into registers while the current stage's MFMAs run.
+  // One (4 tokens) x (8 features) item per thread (d <= 128).  Items are
+  // loaded into registers two stages ahead (two register sets in turn), so
+  // that two stages' loads are in flight under each stage's MFMAs.
   const int items = (kGramStage / 4) * (d / 8);
   const bool has_item = tid < items;
   const int tq = tid % (kGramStage / 4), fo = tid / (kGramStage / 4);
   constexpr int NV = sizeof(E) == 2 ? 1 : 2;   // 16-byte loads per token
-  uint4 raw[4][NV];
-  float rr[4];
-  auto load_item = [&](int64_t ts) __attribute__((always_inline)) {
+  uint4 rawA[4][NV], rawB[4][NV];
+  float rrA[4], rrB[4];
+  int okA, okB;   // bit j: token j of the item lies in the chunk
+  // the weight per token: 1/r^2 from r, or beta^2 per (token, head) from the
+  // coefficient table (its second component)
+  const bool weighted = p.coef != nullptr;
+  const float* wsrc = weighted ? reinterpret_cast<const float*>(p.coef) + 2 * h + 1 : p.r;
+  const int64_t wstride = weighted ? 2 * H : 1;
+  const int fo_c = has_item ? fo : 0;
+  // Unconditional loads (a token outside the chunk reads row t_begin); the
+  // in-chunk bits are applied where the data is used, so that nothing waits
+  // on a load at issue time and the wait before the LDS writes covers only
+  // the stage being written, not the one loading behind it.
+  // this thread's first token of a stage (t_begin + 4 tq at the first) and
+  // row t_begin, which always exists, for tokens outside the chunk
+  const int64_t rs = H * d;
+  const E* pa_safe = static_cast<const E*>(p.a) + (t_begin * H + h) * d + 8 * fo_c;
+  const E* pa0 = pa_safe + 4 * tq * rs;
+  const float* pw_safe = wsrc + t_begin * wstride;
+  const float* pw0 = pw_safe + 4 * tq * wstride;
+  auto load_item = [&](uint4 (&raw)[4][NV], float (&rr)[4], int& ok, int64_t ts) __attribute__((always_inline)) {
+    const int64_t o = ts - t_begin;
+    const E* pa = pa0 + o * rs;
+    const float* pw = pw0 + o * wstride;
+    const int64_t tq0 = ts + 4 * tq;
+    ok = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t t = ts + 4 * tq + j;
-      if (has_item && t < t_end) {
-        // per-token 1/r^2, or per-(token, head) beta^2 when a table is given
-        rr[j] = p.coef ? p.coef[t * H + h].y : p.r[t];
-        const char* src = static_cast<const char*>(p.a) + ((t * H + h) * d + 8 * fo) * sizeof(E);
+      const bool in = has_item && tq0 + j < t_end;
+      ok |= (int)in << j;
+      rr[j] = *(in ? pw + j * wstride : pw_safe);
+      const uint4* src = reinterpret_cast<const uint4*>(in ? pa + j * rs : pa_safe);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) raw[j][v] = reinterpret_cast<const uint4*>(src)[v];
-      } else {
-        rr[j] = 0.f;   // marks a token outside the chunk: weight 0, values 0
-#pragma unroll
-        for (int v = 0; v < NV; ++v) raw[j][v] = make_uint4(0, 0, 0, 0);
-      }
+      for (int v = 0; v < NV; ++v) raw[j][v] = src[v];
     }
   };
-  load_item(t_begin);
-  for (int64_t ts = t_begin; ts < t_end; ts += kGramStage) {
+  auto stage = [&](uint4 (&raw)[4][NV], float (&rr)[4], int& ok, int64_t ts) __attribute__((always_inline)) {
     __syncthreads();   // the previous stage has been read
     if (has_item) {
+      // tokens outside the chunk get weight 0: each product pairs a value with
+      // a weighted value, so their (finite, row t_begin) values add nothing
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rr[j] = ((ok >> j) & 1) ? rr[j] : 0.f;
       float x[4][8];
       float wt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        wt[j] = p.coef ? rr[j] * rr[j] : (rr[j] != 0.f ? 1.0f / (rr[j] * rr[j]) : 0.f);
+        // hardware reciprocal (about 1 ulp): the product is rounded to bf16
+        // on the bf16 path, and 1 ulp is far inside the fp32 tolerance
+        const float inv = rr[j] != 0.f ? __builtin_amdgcn_rcpf(rr[j] * rr[j]) : 0.f;
+        wt[j] = weighted ? rr[j] * rr[j] : inv;
         if constexpr (sizeof(E) == 2) {
           const uint32_t wv[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
 #pragma unroll
@@ -144,41 +186,55 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
       }
     }
     __syncthreads();
-    if (ts + kGramStage < t_end) load_item(ts + kGramStage);
+    load_item(raw, rr, ok, ts + 2 * kGramStage);   // past the chunk: masked off
     // C[i][j] += sum_t x[i][t] * (x[j][t] / r_t^2): A rows i, B rows j
 #pragma unroll
     for (int q = 0; q < kGramStage / 16; ++q) {
       const int col = 16 * q + 8 * (l >> 5);
+      uint4 af[2][Q], bh[2][Q];
+      // the fragments of the wave's row tiles (A) and column tiles (B)
+      auto frag = [&](uint4 (&f)[Q], int buf, int tile) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        const int tile = w + 4 * ti;
-        if (tile < nt * nt) {
-          const int it = tile / nt, jt = tile - it * nt;
-          const E* arow = &xs[0][(it * 32 + (l & 31)) * TP + col];
-          uint4 af[Q], bh[Q];
+        for (int qq = 0; qq < Q; ++qq)
+          f[qq] = *reinterpret_cast<const uint4*>(&xs[buf][(tile * 32 + (l & 31)) * TP + col] +
+                                                  qq * (16 / sizeof(E)));
+      };
+      if constexpr (NT >= 3) {
+        const int it0 = 2 * (w >> 1), jt0 = 2 * (w & 1);
 #pragma unroll
-          for (int qq = 0; qq < Q; ++qq) {
-            af[qq] = *reinterpret_cast<const uint4*>(arow + qq * (16 / sizeof(E)));
-            bh[qq] = *reinterpret_cast<const uint4*>(&xs[1][(jt * 32 + (l & 31)) * TP + col] +
-                                                     qq * (16 / sizeof(E)));
-          }
-          mma(acc[ti], af, bh);
+        for (int x = 0; x < 2; ++x) {
+          if (it0 + x < NT) frag(af[x], 0, it0 + x);
+          if (jt0 + x < NT) frag(bh[x], 1, jt0 + x);
         }
+      } else if (w < NT * NT) {
+        frag(af[0], 0, w / NT);
+        frag(bh[0], 1, w % NT);
+      }
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        int it, jt;
+        if (gram_tile<NT>(w, sl, it, jt)) mma(acc[sl], af[sl >> 1], bh[sl & 1]);
       }
     }
+  };
+  load_item(rawA, rrA, okA, t_begin);
+  load_item(rawB, rrB, okB, t_begin + kGramStage);
+  // two stages per trip (a stage past the chunk adds zeros)
+  for (int64_t ts = t_begin; ts < t_end; ts += 2 * kGramStage) {
+    stage(rawA, rrA, okA, ts);
+    stage(rawB, rrB, okB, ts + kGramStage);
   }
   // write the tiles (C layout: column l & 31, row 8 (v / 4) + 4 (l / 32) + v % 4)
   float* out = p.part + ((int64_t)gc * p.H + h) * d * d;
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti) {
-    const int tile = w + 4 * ti;
-    if (tile < nt * nt) {
-      const int it = tile / nt, jt = tile - it * nt;
+  for (int sl = 0; sl < 4; ++sl) {
+    int it, jt;
+    if (gram_tile<NT>(w, sl, it, jt)) {
       const int j = jt * 32 + (l & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = it * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        if (i < d && j < d) out[(int64_t)i * d + j] = acc[ti][v];
+        if (i < d && j < d) out[(int64_t)i * d + j] = acc[sl][v];
       }
     }
   }
@@ -373,8 +429,18 @@ hipError_t launch_quad_e(const QuadParams& p, hipStream_t st) {
 hipError_t launch_gram(const GramParams& p, int dtype, hipStream_t st) {
   if (p.n_gc == 0) return hipSuccess;
   const dim3 grid(p.n_gc * p.H);
-  if (dtype == 1) hipLaunchKernelGGL(gram_kernel<__bf16>, grid, dim3(kGThreads), 0, st, p);
-  else hipLaunchKernelGGL(gram_kernel<float>, grid, dim3(kGThreads), 0, st, p);
+  const int nt = (p.d + 31) / 32;
+#define HNA_GRAM(NT)                                                                    \
+  if (dtype == 1) hipLaunchKernelGGL((gram_kernel<__bf16, NT>), grid, dim3(kGThreads), 0, st, p); \
+  else hipLaunchKernelGGL((gram_kernel<float, NT>), grid, dim3(kGThreads), 0, st, p);
+  switch (nt) {
+    case 1: HNA_GRAM(1) break;
+    case 2: HNA_GRAM(2) break;
+    case 3: HNA_GRAM(3) break;
+    case 4: HNA_GRAM(4) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef HNA_GRAM
   return hipGetLastError();
 }
 
