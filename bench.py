@@ -215,9 +215,11 @@ def search_bench(hna, reps: int):
 def loo_bench(hna, layer, P, grp, reps: int):
     """The exact leave-one-out score on the benchmark layer (folded weights
     already in P.M): average hna_affinity_loo duration over `reps` calls, HIP
-    events on the launch stream.  Algorithmic MFMA work: the contraction
-    a_h . M_h (4 T H d I) plus the head writes W_o^(h) a_h for the moments
-    (2 T H d hidden)."""
+    events on the launch stream.  Algorithmic matrix work of the call's
+    formulation: x W_o and R = ((alpha beta / r) a)^T x (4 T H d hidden), the
+    moments a_h . Q_h a_h and the beta^2-weighted Gram matrices (4 T H d^2),
+    Y = R diag(gamma) [W_gate; W_up]^T (4 H d hidden I), the quadratic forms
+    (4 H d^2 I) and T1 (2 T H I)."""
     import torch
     T, H, d = layer["a"].shape
     I, D = layer["W_gate"].shape
@@ -232,7 +234,8 @@ def loo_bench(hna, layer, P, grp, reps: int):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    flops = 4.0 * T * H * d * I + 2.0 * T * H * d * D
+    flops = (4.0 * T * H * d * D + 4.0 * T * H * d * d + 4.0 * H * d * D * I
+             + 4.0 * H * d * d * I + 2.0 * T * H * I)
     tf = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if layer["a"].dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
     return {"workload": f"same layer, T={T}", "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),

@@ -98,7 +98,8 @@ def lib() -> ctypes.CDLL:
         "hna_head_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
         "hna_layout_search_workspace_bytes": (sz, [i32, i32, i32]),
         "hna_loo_workspace_bytes": (sz, [dp]),
-        "hna_affinity_loo": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, ip, f32, vp, vp, sz, vp]),
+        "hna_affinity_loo": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, f32, vp, vp,
+                                            sz, vp]),
         "hna_layout_search": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                                               ctypes.POINTER(ctypes.c_double), ip, vp, sz, vp]),
     }
@@ -413,13 +414,13 @@ def loo_workspace_bytes(dims: hna_dims) -> int:
     return int(lib().hna_loo_workspace_bytes(ctypes.byref(dims)))
 
 
-def affinity_loo(dims: hna_dims, a, g, u, x, W_o, M, group_of_head, scale: float,
-                 S_loo: Optional[torch.Tensor] = None,
+def affinity_loo(dims: hna_dims, a, g, u, x, W_o, gamma, W_gate, W_up, M, group_of_head,
+                 scale: float, S_loo: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """S_loo [G, I] fp32: the exact leave-one-out score (section 3, "Affinity scores")."""
-    _need_cuda(a, g, u, x, W_o, M)
-    if x.dtype != torch.float32:
-        raise ValueError("x must be fp32")
+    _need_cuda(a, g, u, x, W_o, gamma, W_gate, W_up, M)
+    if x.dtype != torch.float32 or gamma.dtype != torch.float32:
+        raise ValueError("x and gamma must be fp32")
     L = lib()
     dev = M.device
     if S_loo is None:
@@ -428,7 +429,8 @@ def affinity_loo(dims: hna_dims, a, g, u, x, W_o, M, group_of_head, scale: float
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     _check(L.hna_affinity_loo(ctypes.byref(dims), _ptr(a), _ptr(g), _ptr(u), _ptr(x), _ptr(W_o),
-                              _ptr(M), _map(group_of_head), float(scale), _ptr(S_loo),
+                              _ptr(gamma), _ptr(W_gate), _ptr(W_up), _ptr(M),
+                              _map(group_of_head), float(scale), _ptr(S_loo),
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(dev)), "hna_affinity_loo")
     return S_loo

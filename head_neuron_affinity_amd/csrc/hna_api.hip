@@ -510,7 +510,7 @@ int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_u
 namespace {
 
 struct LooWorkspace {
-  size_t xx, xl, ZA, U, Q, coef, Y, t1, t1r, gram_part, gram, t3, t3_part, blas, total;
+  size_t xx, xl, ZA, U, Q, coef, R, Rs, Y, t1, t1r, gram_part, gram, t3, t3_part, blas, total;
   int n_tc;
 };
 constexpr size_t kBlasWorkspace = 64u << 20;   // handed to rocBLAS for its GEMMs
@@ -527,6 +527,10 @@ LooWorkspace loo_workspace(const hna_dims* dm) {
   w.U = o;         o += loo_coef_fused(dm->d, dm->dtype) ? 0 : align256(thd * es);
   w.Q = o;         o += align256((size_t)dm->H * dm->d * dm->d * es);
   w.coef = o;      o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
+  const int64_t r_split = loo_r_split(dm->T);
+  const int r_parts = (int)r_split + (dm->T % r_split ? 1 : 0);
+  w.R = o;         o += align256((size_t)r_parts * dm->H * dm->d * dm->hidden * sizeof(float));
+  w.Rs = o;        o += align256((size_t)dm->H * dm->d * dm->hidden * es);
   w.Y = o;         o += align256((size_t)2 * dm->H * dm->d * dm->I * sizeof(float));
   w.t1 = o;        o += align256((size_t)w.n_tc * dm->H * dm->I * sizeof(float));
   w.t1r = o;       o += align256((size_t)dm->H * dm->I * sizeof(double));
@@ -620,9 +624,9 @@ size_t hna_loo_workspace_bytes(const hna_dims* dm) {
 }
 
 int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const void* u,
-                     const float* x, const void* W_o, const void* M,
-                     const int32_t* group_of_head, float scale, float* S_loo, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     const float* x, const void* W_o, const float* gamma, const void* W_gate,
+                     const void* W_up, const void* M, const int32_t* group_of_head, float scale,
+                     float* S_loo, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "hna_affinity_loo";
   int rc = check_dims(fn, dm);
   if (rc) return rc;
@@ -643,6 +647,9 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
     REQUIRE_PTR(u);
     REQUIRE_PTR(x);
     REQUIRE_PTR(W_o);
+    REQUIRE_PTR(gamma);
+    REQUIRE_PTR(W_gate);
+    REQUIRE_PTR(W_up);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -653,6 +660,8 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   void* Q = ws + wl.Q;
   float2* coef = reinterpret_cast<float2*>(ws + wl.coef);
   float* Y = reinterpret_cast<float*>(ws + wl.Y);
+  float* R = reinterpret_cast<float*>(ws + wl.R);
+  void* Rs = ws + wl.Rs;
   float* t1 = reinterpret_cast<float*>(ws + wl.t1);
   void* bws = ws + wl.blas;
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
@@ -690,18 +699,36 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
         (!fused && (bs = blas_gemm(st, bws, kBlasWorkspace, false, false, d, T, d, Q, dt, d,
                                    (int64_t)d * d, a, dt, HD, d, U, dt, HD, d, dm->H)) != 0))
       return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
-    // 2. T2: Y^g = (alpha beta a)^T g and Y^u likewise, over the tokens, with
-    //    alpha beta a written over Z
+    // 2. T2: Y^g = (alpha beta a)^T g and Y^u likewise.  With g_t = W_g (gamma x_t) / r_t,
+    //    Y^g = R diag(gamma) W_g^T where R = ((alpha beta / r) a)^T x: the scaled
+    //    head outputs are written over Z, R is one GEMM over the tokens
+    //    (HD x hidden), and Y^g, Y^u are two GEMMs over hidden
     if (fused) {
       if ((e = launch_loo_coef_fused(a, ZA, Q, xx, dm->T, dm->H, d, D, coef, st)) != hipSuccess)
         return hip_fail(e, fn);
     } else if ((e = launch_loo_coef(a, ZA, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess ||
-               (e = launch_scale_a(a, coef, dm->T, dm->H, d, ZA, dt, st)) != hipSuccess) {
+               (e = launch_scale_a(a, coef, xx, dm->T, dm->H, d, D, ZA, dt, st)) != hipSuccess) {
       return hip_fail(e, fn);
     }
+    // R in token chunks (strided batch), the remainder as one more part
+    const int rs = loo_r_split(dm->T);
+    const int tk = T / rs, rem = T - rs * tk;
+    const int64_t hdD = (int64_t)HD * D;
+    const size_t esz = esize_of(dt);
+    if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, D, tk, ZA, dt, HD,
+                        (int64_t)tk * HD, xg, dt, D, (int64_t)tk * D, R, 0, HD, hdD, rs)) != 0 ||
+        (rem > 0 &&
+         (bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, D, rem,
+                         static_cast<const char*>(ZA) + (size_t)rs * tk * HD * esz, dt, HD, 0,
+                         static_cast<const char*>(xg) + (size_t)rs * tk * D * esz, dt, D, 0,
+                         R + rs * hdD, 0, HD, 0, 1)) != 0))
+      return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
+    if ((e = launch_scale_cols(R, rs + (rem > 0 ? 1 : 0), gamma, HD, D, Rs, dt, st)) != hipSuccess)
+      return hip_fail(e, fn);
     for (int gu = 0; gu < 2; ++gu)
-      if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, dm->I, T, ZA, dt, HD, 0,
-                          gu ? u : g, dt, dm->I, 0, Y + (int64_t)gu * HD * dm->I, 0, HD, 0, 1)) != 0)
+      if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, false, HD, dm->I, D, Rs, dt, HD, 0,
+                          gu ? W_up : W_gate, dt, D, 0, Y + (int64_t)gu * HD * dm->I, 0, HD, 0,
+                          1)) != 0)
         return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
     // 3. T1
     if ((e = launch_t1(g, u, coef, dm->T, dm->H, dm->I, t1, dm->dtype, st)) != hipSuccess ||

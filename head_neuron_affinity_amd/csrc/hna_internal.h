@@ -228,8 +228,16 @@ hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const fl
 bool loo_coef_fused(int d, int dtype);
 hipError_t launch_loo_coef_fused(const void* a, void* ZA, const void* Q, const float* xx, int64_t T,
                                  int H, int d, int D, float2* coef, hipStream_t st);
-hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, int d, void* As,
-                          int dtype, hipStream_t st);
+hipError_t launch_scale_a(const void* a, const float2* coef, const float* xx, int64_t T, int H,
+                          int d, int D, void* As, int dtype, hipStream_t st);
+// R = ((alpha beta / r) a)^T x over the tokens is split into this many equal
+// token chunks (a batched GEMM, so that its few output tiles still fill the
+// chip), plus one part for the remainder when T is not a multiple
+int loo_r_split(int64_t T);
+// Rs = (sum of `parts` parts of R) diag(gamma) in the input dtype, each part
+// column-major [HD x D] fp32
+hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int HD, int D,
+                             void* Rs, int dtype, hipStream_t st);
 int t1_chunks(int64_t T);
 hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T, int H, int I,
                      float* t1, int dtype, hipStream_t st);

@@ -9,8 +9,11 @@
 // (m_hk the folded weights; u likewise), so that per head and neuron
 //   sum_t (...)^2 = T1 + 2 T2 + T3,
 //   T1 = sum_t alpha^2 (g^2 + u^2)      (t1_kernel, fp32 matrix cores)
-//   T2 = m^g_hk . Y^g_h[:, k] + m^u_hk . Y^u_h[:, k],  Y_h = sum_t alpha beta a_th g_t^T
-//        (two plain GEMMs over the tokens, by rocBLAS, on a scaled by alpha beta)
+//   T2 = m^g_hk . Y^g_h[:, k] + m^u_hk . Y^u_h[:, k],  Y_h = sum_t alpha beta a_th g_t^T.
+//        g_t = W_g (gamma * x_t) / r_t exactly (g is the pre-activation of x), so
+//        Y^g_h = R_h diag(gamma) W_g^T with R_h = sum_t (alpha beta / r_t) a_th x_t^T:
+//        one token GEMM of width hidden shared by gate and up, then two small
+//        weight GEMMs (rocBLAS), instead of two token GEMMs of width I
 //   T3 = m^T C_h m,  C_h = sum_t beta_th^2 a_th a_th^T   (the Gram and quadratic-
 //        form kernels of the ADD score, weighted per token and head)
 // r_h^2 = (|x|^2 - 2 x . o_h + |o_h|^2) / hidden needs |x|^2 (x_prep_kernel)
@@ -18,8 +21,8 @@
 // |o_h|^2 = a_h . (Q_h a_h) with Q_h = W_o^(h)T W_o^(h), from three more plain
 // GEMMs (x W_o, the Q_h, Q_h a_h; rocBLAS) and the dots in loo_coef_kernel.  All
 // three terms are non-cancelling in practice (T3 dominates; T2 is a fraction of
-// it), so rounding a * alpha beta to bf16 for the GEMMs costs far less than the
-// bf16 tolerance.
+// it), so rounding a * alpha beta / r and R_h diag(gamma) to bf16 for the GEMMs
+// costs far less than the bf16 tolerance.
 #include <rocblas/rocblas.h>
 
 #include <cmath>
@@ -130,17 +133,23 @@ __device__ inline float load_elem(const __bf16* p, int64_t i) {
 }
 __device__ inline float load_elem(const float* p, int64_t i) { return p[i]; }
 
-// As[t][h*d + j] = alpha_th beta_th a[t][h][j] (rounded to the input dtype), 8
-// elements per thread (d is a multiple of 16)
+// 1 / r_t = sqrt(hidden / |x_t|^2) (0 for a zero residual, whose coefficients are 0)
+__device__ inline float inv_rms(float x2, int D) {
+  return x2 > 0.f ? (float)sqrt((double)D / (double)x2) : 0.f;
+}
+
+// As[t][h*d + j] = (alpha_th beta_th / r_t) a[t][h][j] (rounded to the input
+// dtype), 8 elements per thread (d is a multiple of 16)
 template <typename E>
 __global__ __launch_bounds__(256) void scale_a_kernel(const E* __restrict__ a,
-                                                      const float2* __restrict__ coef, int64_t T,
-                                                      int H, int d, E* __restrict__ As) {
+                                                      const float2* __restrict__ coef,
+                                                      const float* __restrict__ xx, int64_t T,
+                                                      int H, int d, int D, E* __restrict__ As) {
   const int64_t n8 = T * H * d / 8;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
     const int64_t th = (i * 8) / d;
     const float2 c = coef[th];
-    const float w = c.x * c.y;
+    const float w = c.x * c.y * inv_rms(xx[th / H], D);
     float v[8];
     load8(a + i * 8, v);
     if constexpr (sizeof(E) == 2) {
@@ -171,7 +180,7 @@ __device__ inline float bf16_at(const uint4& v, int e) {
 // that a lane receives on a feature whose a value the lane already holds.
 // x . o_h = Z . a is dotted over the same features; two exchanges across the
 // wave's quarters complete both sums.  Z is overwritten, in place, by
-// alpha beta a (rounded to bf16).
+// (alpha beta / r) a (rounded to bf16).
 constexpr int kCoefBlocksPerHead = 128;
 
 template <int ND>
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
       c.y = (float)sqrt((double)D / den);
     }
     if (qq == 0) coef[t * H + h] = c;
-    const float w = c.x * c.y;
+    const float w = c.x * c.y * inv_rms((float)x2, D);
 #pragma unroll
     for (int ks = 0; ks < ND; ++ks) {
       const uint4 v = a_cur[ks];
@@ -262,6 +271,29 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
                      pack_bf16x2(bf16_at(v, 4) * w, bf16_at(v, 5) * w),
                      pack_bf16x2(bf16_at(v, 6) * w, bf16_at(v, 7) * w));
     }
+  }
+}
+
+// Rs = (sum of the token-chunk parts of R) diag(gamma) in the input dtype: each
+// part is column-major [HD x hidden] fp32 (column c, the hidden index, is
+// scaled by gamma[c]); the parts are added in order; 4 entries per thread
+template <typename E>
+__global__ __launch_bounds__(256) void scale_cols_kernel(const float* __restrict__ R, int parts,
+                                                         const float* __restrict__ gamma, int HD,
+                                                         int64_t n, E* __restrict__ Rs) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;   // n and HD are multiples of 16
+  float4 v = *reinterpret_cast<const float4*>(R + i);
+  for (int q = 1; q < parts; ++q) {
+    const float4 w = *reinterpret_cast<const float4*>(R + (int64_t)q * n + i);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const float gm = gamma[i / HD];
+  if constexpr (sizeof(E) == 2) {
+    *reinterpret_cast<uint2*>(Rs + i) = make_uint2(pack_bf16x2(v.x * gm, v.y * gm),
+                                                   pack_bf16x2(v.z * gm, v.w * gm));
+  } else {
+    *reinterpret_cast<float4*>(Rs + i) = make_float4(v.x * gm, v.y * gm, v.z * gm, v.w * gm);
   }
 }
 
@@ -462,18 +494,39 @@ hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const fl
   return hipGetLastError();
 }
 
-hipError_t launch_scale_a(const void* a, const float2* coef, int64_t T, int H, int d, void* As,
-                          int dtype, hipStream_t st) {
+hipError_t launch_scale_a(const void* a, const float2* coef, const float* xx, int64_t T, int H,
+                          int d, int D, void* As, int dtype, hipStream_t st) {
   const int64_t n = T * H * d / 8;
   if (n == 0) return hipSuccess;
   const int64_t nb = (n + 255) / 256;
   const unsigned blocks = (unsigned)(nb < 65536 ? nb : 65536);
   if (dtype == 1)
     hipLaunchKernelGGL(scale_a_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const __bf16*>(a), coef, T, H, d, static_cast<__bf16*>(As));
+                       static_cast<const __bf16*>(a), coef, xx, T, H, d, D,
+                       static_cast<__bf16*>(As));
   else
     hipLaunchKernelGGL(scale_a_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const float*>(a), coef, T, H, d, static_cast<float*>(As));
+                       static_cast<const float*>(a), coef, xx, T, H, d, D,
+                       static_cast<float*>(As));
+  return hipGetLastError();
+}
+
+int loo_r_split(int64_t T) {
+  const int64_t s = T / 4096;
+  return (int)(s < 1 ? 1 : (s > 16 ? 16 : s));
+}
+
+hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int HD, int D,
+                             void* Rs, int dtype, hipStream_t st) {
+  const int64_t n = (int64_t)HD * D;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n / 4 + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(scale_cols_kernel<__bf16>, grid, dim3(256), 0, st, R, parts, gamma, HD, n,
+                       static_cast<__bf16*>(Rs));
+  else
+    hipLaunchKernelGGL(scale_cols_kernel<float>, grid, dim3(256), 0, st, R, parts, gamma, HD, n,
+                       static_cast<float*>(Rs));
   return hipGetLastError();
 }
 

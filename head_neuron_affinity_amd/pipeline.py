@@ -80,7 +80,8 @@ class AffinityPass:
             self.loo_ws = torch.empty(max(16, B.loo_workspace_bytes(self.dims)),
                                       dtype=torch.uint8, device=self.device)
         B.affinity_loo(self.dims, layer["a"], layer["g"], layer["u"], layer["x_in"],
-                       layer["W_o"], self.M, group_of_head,
+                       layer["W_o"], layer["gamma"], layer["W_gate"], layer["W_up"], self.M,
+                       group_of_head,
                        1.0 / max(self.T, 1) if scale is None else scale,
                        S_loo=self.S_loo, workspace=self.loo_ws)
         return self.S_loo

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define HNA_ABI_VERSION 1
+#define HNA_ABI_VERSION 2
 
 typedef enum hna_status {
   HNA_OK = 0,
@@ -216,11 +216,15 @@ size_t hna_loo_workspace_bytes(const hna_dims* dims);
  *   alpha_th = 1 - r/r_h,  beta_th = 1/r_h,
  * with m_hk the folded weights of hna_fold_up_weights (M) and r_h from |x|^2,
  * x . o_h and |o_h|^2; the square is summed as three terms (alpha^2 g^2, the
- * cross term through two token GEMMs, beta^2 P^2 through weighted Gram
- * matrices).
- *   a [T, H, d], g, u [T, I], W_o [hidden, H*d], M: the input dtype
+ * cross term, beta^2 P^2 through weighted Gram matrices).  The cross term
+ * uses g_t = W_gate (gamma * x_t) / r_t: sum_t alpha beta a_th g_tk equals
+ * (R_h diag(gamma) w^g_k) with R_h = sum_t (alpha beta / r_t) a_th x_t^T, one
+ * GEMM over the tokens of width hidden (shared by gate and up) followed by
+ * two GEMMs over hidden.
+ *   a [T, H, d], g, u [T, I], W_o [hidden, H*d], W_gate, W_up [I, hidden], M:
+ *     the input dtype; gamma fp32 [hidden] (the pre-norm weight of the fold)
  *   x fp32 [T, hidden]: the residual entering the FFN pre-norm (the g and u
- *     given must be its pre-activations)
+ *     given must be its pre-activations, g = W_gate (gamma * x / rms(x)))
  *   S_loo fp32 [G, I] output (written, also for T = 0: zeros)
  * A token whose residual vanishes without head h (r_h = 0) contributes
  * nothing for that head.  Limits: those of hna_affinity_up and T < 2^31.
@@ -234,9 +238,9 @@ size_t hna_loo_workspace_bytes(const hna_dims* dims);
  * thread-local error text.
  */
 int hna_affinity_loo(const hna_dims* dims, const void* a, const void* g, const void* u,
-                     const float* x, const void* W_o, const void* M,
-                     const int32_t* group_of_head, float scale, float* S_loo, void* workspace,
-                     size_t workspace_bytes, void* stream);
+                     const float* x, const void* W_o, const float* gamma, const void* W_gate,
+                     const void* W_up, const void* M, const int32_t* group_of_head, float scale,
+                     float* S_loo, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------- layout objective */
 

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     hna = _lib()
     L = hna.lib()
-    assert L.hna_abi_version() == 1
+    assert L.hna_abi_version() == 2
     assert hna.status_string(0) == "HNA_OK"
     assert hna.status_string(-4) == "HNA_ERR_WORKSPACE"
     assert hna.status_string(-99) == "HNA_ERR_UNKNOWN"
@@ -307,14 +307,17 @@ def test_loo_validates():
     assert need > 0
     loo = L.hna_affinity_loo
 
-    def call(d=dm, a=F, x=F, M=F, S=F, ws=F, wsb=need, g=grp):
-        return loo(ctypes.byref(d), a, F, F, x, F, M, g, 1.0, S, ws, wsb, None)
+    def call(d=dm, a=F, x=F, gamma=F, Wg=F, Wu=F, M=F, S=F, ws=F, wsb=need, g=grp):
+        return loo(ctypes.byref(d), a, F, F, x, F, gamma, Wg, Wu, M, g, 1.0, S, ws, wsb, None)
 
     assert call(d=dims(hna, d=20)) == -2            # head dim not a multiple of 16
     assert call(M=None) == -1
     assert call(S=vp(MIS)) == -3
     assert call(wsb=need - 1) == -4
     assert call(x=None) == -1
+    assert call(gamma=None) == -1
+    assert call(Wg=None) == -1
+    assert call(Wu=vp(MIS)) == -3
     bad = (ctypes.c_int32 * dm.H)(*([0] * (dm.H - 1) + [dm.G]))
     assert call(g=bad) == -1
     assert L.hna_loo_workspace_bytes(None) == 0
