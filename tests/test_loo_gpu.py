@@ -3,8 +3,9 @@ GPU, through the C ABI, against the float64 oracle's literal ablation.
 
 Tolerances as for the other scores: fp32 inputs, max|dS| / max|S| <= 1e-4;
 bf16 inputs (fp32 accumulation), relative Frobenius <= 1e-2.  The GPU uses the
-layer's stored g and u for the full pass, the oracle recomputes them from the
-same fp32 residual x; the difference is the storage rounding of g and u.
+layer's stored g and u for the alpha^2 g^2 term and x with the gate and up
+weights for the cross term; the oracle recomputes g and u from the same fp32
+residual x, so the difference is the storage rounding of g and u.
 """
 import numpy as np
 import pytest
