@@ -61,6 +61,10 @@ def check(got, ref, tol, metric):
     (synth.LayerShape("mid-bf16", 2048, 256, 8, 4, 64, 384, "bf16", 0.5), BF16_TOL, "fro"),
     # head dim 32 and a token count off the 32-token tile
     (synth.LayerShape("d32-ragged-bf16", 999, 128, 4, 2, 32, 200, "bf16", 0.5), BF16_TOL, "fro"),
+    # token counts that split the cross term's token GEMM into equal chunks
+    # plus a one-token remainder part (2 x 4097 + 1 and 3 x 4096 + 1)
+    (synth.LayerShape("split-remainder-bf16", 8195, 128, 4, 2, 32, 200, "bf16", 0.5), BF16_TOL, "fro"),
+    (synth.LayerShape("split-remainder-fp32", 12289, 64, 4, 2, 16, 128, "f32", 0.5), FP32_TOL, "max"),
     (synth.LayerShape("d128-bf16", 512, 512, 16, 8, 128, 256, "bf16", 0.5), BF16_TOL, "fro"),
     # the Danube3-500M layer shape (head dim 96), fewer tokens and neurons
     (synth.LayerShape("danube-shape-bf16", 1024, 1536, 16, 8, 96, 512, "bf16", 0.5), BF16_TOL, "fro"),
