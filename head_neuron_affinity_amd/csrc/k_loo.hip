@@ -513,7 +513,7 @@ hipError_t launch_scale_a(const void* a, const float2* coef, const float* xx, in
 
 int loo_r_split(int64_t T) {
   const int64_t s = T / 4096;
-  return (int)(s < 1 ? 1 : (s > 16 ? 16 : s));
+  return (int)(s < 1 ? 1 : (s > 8 ? 8 : s));
 }
 
 hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int HD, int D,
