@@ -101,12 +101,11 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
   const float* wsrc = weighted ? reinterpret_cast<const float*>(p.coef) + 2 * h + 1 : p.r;
   const int64_t wstride = weighted ? 2 * H : 1;
   const int fo_c = has_item ? fo : 0;
-  // Unconditional loads (a token outside the chunk reads row t_begin); the
-  // in-chunk bits are applied where the data is used, so that nothing waits
-  // on a load at issue time and the wait before the LDS writes covers only
-  // the stage being written, not the one loading behind it.
-  // this thread's first token of a stage (t_begin + 4 tq at the first) and
-  // row t_begin, which always exists, for tokens outside the chunk
+  // The loads are unconditional: a token outside the chunk reads row t_begin
+  // (which always exists), and its in-chunk bit is applied where the data is
+  // used.  Nothing then waits on a load at issue time, and the wait before a
+  // stage's LDS writes covers that stage only, not the one loading behind it.
+  // pa0 / pw0: this thread's first token of the first stage (t_begin + 4 tq).
   const int64_t rs = H * d;
   const E* pa_safe = static_cast<const E*>(p.a) + (t_begin * H + h) * d + 8 * fo_c;
   const E* pa0 = pa_safe + 4 * tq * rs;
@@ -129,6 +128,7 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
     }
   };
   auto stage = [&](uint4 (&raw)[4][NV], float (&rr)[4], int& ok, int64_t ts) __attribute__((always_inline)) {
+    // (ok is refilled by the load of stage ts + 2 kGramStage below)
     __syncthreads();   // the previous stage has been read
     if (has_item) {
       // tokens outside the chunk get weight 0: each product pairs a value with
