@@ -76,12 +76,17 @@ def test_loo_matches_oracle(hna, shape, tol, metric):
     check(got, ref, tol, metric)
 
 
-def test_loo_full_qwen_layer_sampled_neurons(hna):
-    # the 65,536-token Qwen3-0.6B-shaped layer in the benchmark's launch
-    # configuration; the oracle computes 8 sampled neurons over every token
-    layer = synth.make_config_layer(1, device="cuda", with_next=False, with_x=True)
+@pytest.mark.parametrize("config,cols", [
+    # the 65,536-token Qwen3-0.6B-shaped layer in the benchmark's launch configuration
+    (1, [0, 1, 517, 1024, 2047, 2048, 3000, 3071]),
+    # the 65,536-token Danube3-500M-shaped layer (head dim 96, hidden 1536)
+    (2, [0, 3, 1000, 2048, 3333, 4095]),
+])
+def test_loo_full_layer_sampled_neurons(hna, config, cols):
+    # full token count; the oracle computes the sampled neurons over every token
+    layer = synth.make_config_layer(config, device="cuda", with_next=False, with_x=True)
     got = run_loo(hna, layer)
-    cols = np.array([0, 1, 517, 1024, 2047, 2048, 3000, 3071])
+    cols = np.array(cols)
     cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in layer.items()}
     ref = oracle_loo(cpu, neurons=cols)
     check(got[:, cols], ref, BF16_TOL, "fro")
