@@ -347,12 +347,13 @@ __global__ __launch_bounds__(256) void t1_kernel(const E* __restrict__ g, const 
                                                  int H, int I, float* __restrict__ t1) {
   constexpr int NW = raw_words<E, VEC>();
   const int lane = threadIdx.x & 63;
-  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // grid: x = token chunk (no 65,535 limit on long inputs), y = groups of 4 neuron tiles
+  const int tile = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (tile * kT1Cols >= I) return;  // whole wave
   const int c0 = tile * kT1Cols + 8 * (lane & 15);
   const int kq = lane >> 4;
   const bool col_ok = c0 < I;
-  const int64_t t0 = (int64_t)blockIdx.y * kT1Chunk, te = min(T, t0 + kT1Chunk);
+  const int64_t t0 = (int64_t)blockIdx.x * kT1Chunk, te = min(T, t0 + kT1Chunk);
   for (int h0 = 0; h0 < H; h0 += 16) {
     const int ha = h0 + (lane & 15);  // head of this lane's A element
     f32x4 acc[8];
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256) void t1_kernel(const E* __restrict__ g, const 
     for (int r = 0; r < 4; ++r) {
       const int h = h0 + 4 * kq + r;
       if (h >= H) continue;
-      float* dst = t1 + ((int64_t)blockIdx.y * H + h) * I + c0;
+      float* dst = t1 + ((int64_t)blockIdx.x * H + h) * I + c0;
       if (VEC) {
         if (col_ok) {
           reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
@@ -558,7 +559,7 @@ hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T
   if (T == 0 || I == 0) return hipSuccess;
   const bool vec = I % 8 == 0;
   const int tiles = (I + kT1Cols - 1) / kT1Cols;
-  const dim3 grid((tiles + 3) / 4, t1_chunks(T));
+  const dim3 grid(t1_chunks(T), (tiles + 3) / 4);
   if (dtype == 1) {
     const auto* gb = static_cast<const __bf16*>(g);
     const auto* ub = static_cast<const __bf16*>(u);
