@@ -164,6 +164,7 @@ struct NeuronStepParams {
   int32_t* neurons;       // [N][I] out
   int32_t* stats;         // [N][4] out: status, excess after the dual ascent, moves, swaps
   int N, G, I, L, iters, max_swaps;
+  int qtab;               // set by the launcher: the dual quotients come from an LDS table
 };
 size_t neuron_step_lds_bytes(int I, int L);
 hipError_t launch_neuron_step(const NeuronStepParams& p, hipStream_t st);

@@ -151,7 +151,13 @@ __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams
     mm[0][w] = mx;
     mm[1][w] = mn;
   }
-  __syncthreads();  // also publishes Ms
+  // The dual step's quotient (c - cap) / cap takes only the values c = 0..I:
+  // when LDS allows, they are divided once here and looked up in the loop
+  // (the same fp64 division, so the same values)
+  double* qtab = Ms + (size_t)L * I;
+  if (p.qtab)
+    for (int c = t; c <= I; c += kLThreads) qtab[c] = (double)(c - cap) / (double)cap;
+  __syncthreads();  // also publishes Ms and the quotients
   mx = mm[0][0];
   mn = mm[1][0];
   for (int i = 1; i < kLWaves; ++i) {
@@ -260,7 +266,8 @@ __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams
   for (int it = 0; it < p.iters; ++it) {
     assign_argmax();
     const int c = count(false);
-    lam_lane = lam_lane + step * ((double)(c - cap) / (double)cap);
+    const double q = p.qtab ? qtab[c] : (double)(c - cap) / (double)cap;   // 0 <= c <= I
+    lam_lane = lam_lane + step * q;
 #pragma unroll
     for (int l = 0; l < LMAX; ++l) lam[l] = l < L ? readlane_f64(lam_lane, l) : INFINITY;
     step = step * kStepDecay;
@@ -593,12 +600,22 @@ hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st) {
 
 size_t neuron_step_lds_bytes(int I, int L) { return (size_t)I * L * sizeof(double); }
 
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;   // gfx950
+
 template <int NPT_MAX, int LMAX, bool CACHE>
-static hipError_t launch_ns(const NeuronStepParams& p, hipStream_t st) {
-  const size_t lds = neuron_step_lds_bytes(p.I, p.L);
+static hipError_t launch_ns(const NeuronStepParams& p0, hipStream_t st) {
   auto fn = neuron_step_kernel<NPT_MAX, LMAX, CACHE>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
+  if (e != hipSuccess) return e;
+  // M, plus the quotient table when static + dynamic LDS still fit
+  NeuronStepParams p = p0;
+  size_t lds = neuron_step_lds_bytes(p.I, p.L);
+  const size_t tab = (size_t)(p.I + 1) * sizeof(double);
+  p.qtab = attr.sharedSizeBytes + lds + tab <= kLdsPerWorkgroup;
+  if (p.qtab) lds += tab;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(p.N), dim3(kLThreads), lds, st, p);
   return hipGetLastError();
