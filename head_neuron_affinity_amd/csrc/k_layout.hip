@@ -70,7 +70,7 @@ template <int NPT_MAX, int LMAX, bool CACHE>
 __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams p) {
   extern __shared__ double Ms[];  // [L][I]
   __shared__ int hs[kMaxHeads], hn[kMaxHeads];
-  __shared__ int cnt_s[3][LMAX];  // rotating device counts
+  __shared__ int cnt_w[2][kLWaves][LMAX];  // per-wave device counts, two buffers in turn
   __shared__ double red_d[2][kLWaves][kMaxPairs];
   __shared__ int red_i[2][kLWaves][kMaxPairs];
   __shared__ double mm[2][kLWaves];
@@ -85,7 +85,6 @@ __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams
 
   // ---- head devices of this layer and the next; ids outside [0, L) fail the layer
   if (t == 0) bad = 0;
-  if (t < 3 * LMAX) cnt_s[t / LMAX][t % LMAX] = 0;
   __syncthreads();
   if (t < G) {
     const int a = p.heads[(int64_t)layer * G + t];
@@ -228,34 +227,44 @@ __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams
       }
     }
   };
-  // Device counts: each wave adds its ballot counts into cnt_s[rot] (integer
-  // LDS atomics, so the total is exact), one barrier, then every thread reads
-  // the L totals.  Three buffers rotate: the one two counts ahead is cleared
-  // here, after its last reader passed the barrier and before its next
-  // writers can pass the following one.
+  // Device counts: each wave writes its ballot counts of the L devices into
+  // its own slot of cnt_w[rot] (every slot is rewritten, so nothing is
+  // cleared), one barrier, then each reader adds the waves' slots in wave
+  // order (integers: exact).  Two buffers alternate: a wave writes a buffer
+  // again only after passing the next barrier, which every reader of that
+  // buffer reaches after its reads.
   int cnt[LMAX];
   int rot = 0;
   // returns the count of device `lane` (cap in lanes >= L); fills cnt[] if asked
   auto count = [&](bool all) -> int {
 #pragma unroll
     for (int l = 0; l < LMAX; ++l) {
-      if (CACHE || l < L) {   // (padding devices count zero)
+      if (CACHE || l < L) {   // (padding devices count zero and are never read)
         int c = 0;
 #pragma unroll
         for (int j = 0; j < NPT_MAX; ++j)
           if (j < npt) c += __popcll(__ballot(a[j] == l));
-        if (lane == 0 && c) atomicAdd(&cnt_s[rot][l], c);
+        if (lane == 0) cnt_w[rot][w][l] = c;
       }
     }
     __syncthreads();
-    const int mine = lane < L ? cnt_s[rot][lane] : cap;
+    int mine = cap;
+    if (lane < L) {
+      mine = 0;
+#pragma unroll
+      for (int v = 0; v < kLWaves; ++v) mine += cnt_w[rot][v][lane];
+    }
     if (all) {
 #pragma unroll
-      for (int l = 0; l < LMAX; ++l) cnt[l] = l < L ? cnt_s[rot][l] : 0;
+      for (int l = 0; l < LMAX; ++l) {
+        int c = 0;
+        if (l < L)
+#pragma unroll
+          for (int v = 0; v < kLWaves; ++v) c += cnt_w[rot][v][l];
+        cnt[l] = c;
+      }
     }
-    const int clear = rot == 0 ? 2 : rot - 1;
-    if (t < LMAX) cnt_s[clear][t] = 0;
-    rot = rot == 2 ? 0 : rot + 1;
+    rot ^= 1;
     return mine;
   };
 
