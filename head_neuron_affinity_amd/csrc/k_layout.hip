@@ -440,6 +440,22 @@ __global__ __launch_bounds__(kLThreads) void neuron_step_kernel(NeuronStepParams
 }
 
 // ---------------------------------------------------------------- head step
+// Exact quotient x / n for x a multiple of n, 1 <= n <= 16, in 32-bit
+// integers: the power of two of n is shifted out and the odd part's inverse
+// mod 2^32 multiplies (Newton-Hensel iteration x <- x (2 - o x), which doubles
+// the correct low bits from 3 to 48 in four steps)
+struct ExactDiv {
+  uint32_t tz, inv;
+};
+__device__ inline ExactDiv exact_div_by(uint32_t n) {
+  const uint32_t tz = (uint32_t)__builtin_ctz(n), o = n >> tz;
+  uint32_t x = o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x *= 2u - o * x;
+  return {tz, x};
+}
+__device__ inline uint32_t exact_div(uint32_t x, ExactDiv d) { return (x >> d.tz) * d.inv; }
+
 // One 1024-thread workgroup per layer.  A[g][l] (fp64, LDS): each group is
 // summed by 16/G waves (one for G > 8); each lane adds its strided neurons, up
 // terms then down terms, a fixed butterfly combines the lanes and the waves'
@@ -527,23 +543,24 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
 
   // score the partitions r = t, t + 1024, ...  (ranks fit in an int: at most 2^24)
   const int per = G / L;
-  const double total = (double)p.n_parts;
+  const uint32_t total = (uint32_t)p.n_parts;
   double bd = -INFINITY;
   int bi = INT_MAX;
   for (int r0 = t; r0 < p.n_parts; r0 += kLThreads) {
     int c[kLayoutMaxDevices];
 #pragma unroll
     for (int l = 0; l < kLayoutMaxDevices; ++l) c[l] = l < L ? per : 0;
-    double r = (double)r0, mc = total, score = 0.0;
+    uint32_t r = (uint32_t)r0, mc = total;
+    double score = 0.0;
     for (int q = 0; q < G; ++q) {
-      const double n = (double)(G - q);
+      const ExactDiv dn = exact_div_by((uint32_t)(G - q));
       bool done = false;
 #pragma unroll
       for (int v = 0; v < kLayoutMaxDevices; ++v) {
         if (!done && c[v] > 0) {
           // completions with device v at position q: mc * c_v / n, an exact
-          // integer below 2^53, so fp64 holds every step exactly
-          const double sub = mc * (double)c[v] / n;
+          // integer (mc * c_v < 2^24 * 16 fits 32 bits)
+          const uint32_t sub = exact_div(mc * (uint32_t)c[v], dn);
           if (r < sub) {
             score += A[q * L + v];
             mc = sub;
@@ -576,14 +593,14 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
     int c[kLayoutMaxDevices];
 #pragma unroll
     for (int l = 0; l < kLayoutMaxDevices; ++l) c[l] = l < L ? per : 0;
-    double r = (double)bi, mc = total;
+    uint32_t r = (uint32_t)bi, mc = total;
     for (int q = 0; q < G; ++q) {
-      const double n = (double)(G - q);
+      const ExactDiv dn = exact_div_by((uint32_t)(G - q));
       bool done = false;
 #pragma unroll
       for (int v = 0; v < kLayoutMaxDevices; ++v) {
         if (!done && c[v] > 0) {
-          const double sub = mc * (double)c[v] / n;
+          const uint32_t sub = exact_div(mc * (uint32_t)c[v], dn);
           if (r < sub) {
             p.heads[(int64_t)layer * G + q] = v;
             mc = sub;
