@@ -201,3 +201,21 @@ def test_sweeps_raise_the_objective_and_stop():
     # the reported J is the objective of the returned layout
     J, _, _ = oracle.layout_objective(up, down, res["heads"], res["neurons"])
     assert abs(J - res["J"]) < 1e-12
+
+
+def test_exact_division_by_odd_inverse():
+    """The head step divides mc * c_v by n (1 <= n <= 16, the quotient an exact
+    integer below 2^28) in 32-bit integers: n's power of two is shifted out,
+    then the product is multiplied by the odd part's inverse mod 2^32, found by
+    four Newton-Hensel steps x <- x (2 - o x) from x = o.  Checked here for
+    every n and a range of quotients, including the largest."""
+    M = 1 << 32
+    for n in range(1, 17):
+        tz = (n & -n).bit_length() - 1
+        o = n >> tz
+        x = o
+        for _ in range(4):
+            x = (x * (2 - o * x)) % M
+        assert (o * x) % M == 1
+        for q in list(range(0, 4096)) + [(1 << 24) - 1, (1 << 28) // n - 1]:
+            assert (((q * n) >> tz) * x) % M == q
