@@ -463,6 +463,9 @@ __device__ inline uint32_t exact_div(uint32_t x, ExactDiv d) { return (x >> d.tz
 // partition is then scored by unranking its lexicographic rank (multiset
 // permutations of G/L copies of each device), the score being
 // sum_g A[g][h(g)] in increasing g; the best (ties: lowest rank) wins.
+// LMAX: a compile-time bound on L (4 for the usual shapes, else 8), so the
+// unrolled per-device steps carry no dead devices
+template <int LMAX>
 __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) {
   __shared__ double A[kHeadMaxGroups * kLayoutMaxDevices];
   __shared__ double Apart[kLWaves * kLayoutMaxDevices];   // per-wave partial sums
@@ -504,15 +507,15 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
   const int parts = G <= kLWaves / 2 ? kLWaves / G : 1;
   for (int wg = w; wg < G * parts; wg += kLWaves) {
     const int g = wg / parts, q = wg - g * parts;
-    double acc[kLayoutMaxDevices];
+    double acc[LMAX];
 #pragma unroll
-    for (int l = 0; l < kLayoutMaxDevices; ++l) acc[l] = 0.0;
+    for (int l = 0; l < LMAX; ++l) acc[l] = 0.0;
 #pragma unroll 4
     for (int k = q * 64 + lane; k < I; k += parts * 64) {
       const double v = (double)Su[(int64_t)g * I + k];
       const int dv = nu[k];
 #pragma unroll
-      for (int l = 0; l < kLayoutMaxDevices; ++l)
+      for (int l = 0; l < LMAX; ++l)
         if (l == dv) acc[l] += v;
     }
     if (has_prev) {
@@ -521,12 +524,12 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
         const double v = (double)Sd[(int64_t)k * G + g];
         const int dv = nu_prev[k];
 #pragma unroll
-        for (int l = 0; l < kLayoutMaxDevices; ++l)
+        for (int l = 0; l < LMAX; ++l)
           if (l == dv) acc[l] += v;
       }
     }
 #pragma unroll
-    for (int l = 0; l < kLayoutMaxDevices; ++l) {
+    for (int l = 0; l < LMAX; ++l) {
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc[l] += __shfl_xor(acc[l], o);
       if (lane == 0 && l < L) Apart[(g * parts + q) * L + l] = acc[l];
@@ -547,16 +550,16 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
   double bd = -INFINITY;
   int bi = INT_MAX;
   for (int r0 = t; r0 < p.n_parts; r0 += kLThreads) {
-    int c[kLayoutMaxDevices];
+    int c[LMAX];
 #pragma unroll
-    for (int l = 0; l < kLayoutMaxDevices; ++l) c[l] = l < L ? per : 0;
+    for (int l = 0; l < LMAX; ++l) c[l] = l < L ? per : 0;
     uint32_t r = (uint32_t)r0, mc = total;
     double score = 0.0;
     for (int q = 0; q < G; ++q) {
       const ExactDiv dn = exact_div_by((uint32_t)(G - q));
       bool done = false;
 #pragma unroll
-      for (int v = 0; v < kLayoutMaxDevices; ++v) {
+      for (int v = 0; v < LMAX; ++v) {
         if (!done && c[v] > 0) {
           // completions with device v at position q: mc * c_v / n, an exact
           // integer (mc * c_v < 2^24 * 16 fits 32 bits)
@@ -590,15 +593,15 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
         bi = red_i[i];
       }
     // unrank the winner into the head devices
-    int c[kLayoutMaxDevices];
+    int c[LMAX];
 #pragma unroll
-    for (int l = 0; l < kLayoutMaxDevices; ++l) c[l] = l < L ? per : 0;
+    for (int l = 0; l < LMAX; ++l) c[l] = l < L ? per : 0;
     uint32_t r = (uint32_t)bi, mc = total;
     for (int q = 0; q < G; ++q) {
       const ExactDiv dn = exact_div_by((uint32_t)(G - q));
       bool done = false;
 #pragma unroll
-      for (int v = 0; v < kLayoutMaxDevices; ++v) {
+      for (int v = 0; v < LMAX; ++v) {
         if (!done && c[v] > 0) {
           const uint32_t sub = exact_div(mc * (uint32_t)c[v], dn);
           if (r < sub) {
@@ -620,7 +623,10 @@ __global__ __launch_bounds__(kLThreads) void head_step_kernel(HeadStepParams p) 
 }  // namespace
 
 hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(head_step_kernel, dim3(p.N), dim3(kLThreads), 0, st, p);
+  if (p.L <= 4)
+    hipLaunchKernelGGL(head_step_kernel<4>, dim3(p.N), dim3(kLThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(head_step_kernel<kLayoutMaxDevices>, dim3(p.N), dim3(kLThreads), 0, st, p);
   return hipGetLastError();
 }
 
