@@ -576,20 +576,25 @@ int check_head_dims(const char* fn, int G, int L) {
   return HNA_OK;
 }
 
+// J, the neuron-step stats [N][4] and the head-step statuses [N] sit in one
+// block, so that a sweep reads them back with one copy
 struct SearchWorkspace {
-  size_t heads, neurons, stats, hscore, hstatus, frac_up, frac_down, J, total;
+  size_t heads, neurons, hscore, frac_up, frac_down, report, J, stats, hstatus, report_bytes, total;
 };
 SearchWorkspace search_workspace(int N, int G, int I) {
   SearchWorkspace w;
   size_t o = 0;
   w.heads = o;     o += align256((size_t)N * G * 4);
   w.neurons = o;   o += align256((size_t)N * I * 4);
-  w.stats = o;     o += align256((size_t)N * 16);
   w.hscore = o;    o += align256((size_t)N * 8);
-  w.hstatus = o;   o += align256((size_t)N * 4);
   w.frac_up = o;   o += align256((size_t)N * 8);
   w.frac_down = o; o += align256((size_t)N * 8);
-  w.J = o;         o += align256(8);
+  w.report = o;
+  w.J = o;
+  w.stats = w.J + 8;
+  w.hstatus = w.stats + (size_t)N * 16;
+  w.report_bytes = 8 + (size_t)N * 20;
+  o += align256(w.report_bytes);
   w.total = o;
   return w;
 }
@@ -828,7 +833,7 @@ int hna_layout_search(int32_t N, int32_t G, int32_t I, int32_t L, const float* S
 
   *n_sweeps = 0;
   double bestJ = 0.0;
-  std::vector<int32_t> hst(N), nst((size_t)N * 4);
+  std::vector<char> report(wl.report_bytes);
   for (int s = 0; s < max_sweeps; ++s) {
     // neuron step from the kept heads, head step from the new neurons, then J
     NeuronStepParams np{S_up_hat, S_down_hat, head_device, nu_new, st_new,
@@ -840,14 +845,14 @@ int hna_layout_search(int32_t N, int32_t G, int32_t I, int32_t L, const float* S
     if (e != hipSuccess) return hip_fail(e, fn);
     e = launch_layout_objective(S_up_hat, S_down_hat, h_new, nu_new, N, G, I, fu, fd, Jd, st);
     if (e != hipSuccess) return hip_fail(e, fn);
-    double J = 0.0;
-    if ((e = hipMemcpyAsync(&J, Jd, sizeof(double), hipMemcpyDeviceToHost, st)) != hipSuccess ||
-        (e = hipMemcpyAsync(nst.data(), st_new, nst.size() * 4, hipMemcpyDeviceToHost, st)) !=
-            hipSuccess ||
-        (e = hipMemcpyAsync(hst.data(), hstatus, hst.size() * 4, hipMemcpyDeviceToHost, st)) !=
-            hipSuccess ||
+    if ((e = hipMemcpyAsync(report.data(), ws + wl.report, wl.report_bytes, hipMemcpyDeviceToHost,
+                            st)) != hipSuccess ||
         (e = hipStreamSynchronize(st)) != hipSuccess)
       return hip_fail(e, fn);
+    double J;
+    std::memcpy(&J, report.data(), sizeof(double));
+    const int32_t* nst = reinterpret_cast<const int32_t*>(report.data() + (wl.stats - wl.report));
+    const int32_t* hst = reinterpret_cast<const int32_t*>(report.data() + (wl.hstatus - wl.report));
     for (int i = 0; i < N; ++i) {
       const int ns = nst[(size_t)i * 4];
       if (ns == HNA_LAYOUT_BAD_HEADS)
