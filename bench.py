@@ -10,7 +10,11 @@ Prints one JSON line.  `value` is calibration tokens/s of the whole step;
 `roofline` describes the hot kernel (algorithmic MFMA FLOPs per launch over
 its average duration measured with HIP events on the launch stream);
 `cpu_baseline` is the float64 oracle timed on this host on a bounded token
-sample of the same layer.
+sample of the same layer.  Unless --no-legs is given, the line also carries
+the other single-layer workloads (Danube3-500M-shaped and the large
+4096 x 14336 layer) measured the same way, the 28-layer Qwen3-0.6B-shaped
+stack end to end, the leave-one-out score and the layout-search calls.
+Progress lines go to stderr.
 """
 from __future__ import annotations
 
@@ -243,9 +247,122 @@ def loo_bench(hna, layer, P, grp, reps: int):
                          "frac": tf / peak, "traffic": None}}
 
 
-def build_inputs(config: int, T=None):
+def progress(msg: str):
+    """One progress line on stderr (the JSON record alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def time_layer(hna, layer, steps: int, warmup: int):
+    """Whole-pass step time (wall clock over `steps` steps, synchronised on both
+    sides) and the hot kernel's average duration (HIP events on the launch
+    stream around hna_affinity_up, which launches only that kernel) for one
+    layer resident in HBM."""
+    import torch
+    P = hna.pass_for_layer(layer)
+    grp = [int(x) for x in layer["group_of_head"].tolist()]
+    grp_n = [int(x) for x in layer["group_of_head_next"].tolist()]
+    T = layer["a"].shape[0]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        P.fold(layer)
+        if ev is not None:
+            ev[0].record(stream)
+        P.hot(layer, grp)
+        if ev is not None:
+            ev[1].record(stream)
+        P.add(layer, grp)
+        P.finalize(1.0 / T)
+        P.down(layer, grp_n)
+
+    for _ in range(warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hot_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return P, wall * 1e3 / steps, hot_ms
+
+
+def layer_figures(shape, ms_step: float, hot_ms: float):
+    """Throughput and the hot kernel's roofline for one layer workload."""
+    T, H, d, I = shape.T, shape.H, shape.d, shape.I
+    flops_hot = 4.0 * T * H * d * I                          # algorithmic, one launch
+    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops_hot / (hot_ms * 1e-3) / 1e12
+    esz = 2 if shape.dtype == "bf16" else 4
+    stream_bytes = T * (esz * (H * d + 2 * I) + 8)           # a, g, u, r, r_next read once
+    return {
+        "tokens_per_s": T / (ms_step * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic_for(f"{shape.name}:T={T}")},
+        "hot_kernel_ms": hot_ms,
+        "mfma_frac_whole_step": flops_hot / (ms_step * 1e-3) / 1e12 / peak,
+        "hot_stream_gbs": stream_bytes / (hot_ms * 1e-3) / 1e9,
+    }
+
+
+def layer_leg(hna, config: int, steps: int, warmup: int):
+    """Another single-layer workload, measured like the main line."""
+    import torch
     import synth
-    return synth.make_config_layer(config, T=T, device="cuda")
+    shape = synth.layer_shape(config)
+    layer = synth.make_config_layer(config, device="cuda")
+    torch.cuda.synchronize()
+    _, ms_step, hot_ms = time_layer(hna, layer, steps, warmup)
+    rec = {"workload": shape.name, "T": shape.T, "hidden": shape.hidden, "H": shape.H,
+           "G": shape.G, "d": shape.d, "I": shape.I, "ms_per_step": ms_step}
+    rec.update(layer_figures(shape, ms_step, hot_ms))
+    del layer
+    torch.cuda.empty_cache()
+    return rec
+
+
+def stack_leg(hna, reps: int, warmup: int, T=None):
+    """The 28-layer Qwen3-0.6B-shaped stack end to end: every layer resident in
+    HBM, one pass = fold, hot kernel, ADD and reduction for each layer plus the
+    down edge of each adjacent pair (head_neuron_affinity_amd.StackPass, the
+    weight work on a side stream ahead of the token passes).  Average pass
+    time over `reps` passes (HIP events on the main stream, which waits for
+    the side stream at the end of each pass); the same without the side
+    stream for comparison."""
+    import torch
+    import synth
+    shape = synth.layer_shape(3)
+    if T is not None:
+        shape = shape.with_tokens(T)
+    layers = [synth.make_config_layer(3, layer=i, T=T, device="cuda") for i in range(shape.layers)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    out = {"workload": shape.name, "layers": shape.layers, "T": shape.T}
+    for overlap in (True, False):
+        stack = hna.StackPass(layers, overlap=overlap)
+        for _ in range(warmup):
+            stack.run(layers)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            stack.run(layers)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        key = "ms_per_pass" if overlap else "ms_per_pass_one_stream"
+        out[key] = ms
+        if overlap:
+            flops = 4.0 * shape.T * shape.H * shape.d * shape.I * shape.layers
+            out["tokens_per_s"] = shape.T / (ms * 1e-3)
+            out["layer_tokens_per_s"] = shape.T * shape.layers / (ms * 1e-3)
+            out["mfma_frac_whole_pass"] = flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+        del stack
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -253,9 +370,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, help="workload: 1, 2, 3 (28-layer stack) or 4")
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 4],
+                    help="single-layer workload of the main line")
     ap.add_argument("--tokens", type=int, default=None, help="override T (not for reported numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="main line only (no stack, other layers, leave-one-out or layout legs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (counter scaling runs)")
     args = ap.parse_args()
@@ -275,73 +395,44 @@ def main():
     shape = synth.layer_shape(args.config)
     if args.tokens:
         shape = shape.with_tokens(args.tokens)
-    n_layers = shape.layers
-    layers = [synth.make_config_layer(args.config, layer=i, T=args.tokens, device="cuda",
-                                      with_x=(i == 0))
-              for i in range(n_layers)]
+    L0 = synth.make_config_layer(args.config, T=args.tokens, device="cuda",
+                                 with_x=not args.no_legs)
     torch.cuda.synchronize()
-    L0 = layers[0]
-    passes = [hna.pass_for_layer(L) for L in layers]
-    grps = [[int(x) for x in L["group_of_head"].tolist()] for L in layers]
-    grps_n = [[int(x) for x in L["group_of_head_next"].tolist()] for L in layers]
-    T = shape.T
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        for i, (L, P) in enumerate(zip(layers, passes)):
-            P.fold(L)
-            if ev is not None and i == 0:
-                ev[0].record(stream)
-            P.hot(L, grps[i])
-            if ev is not None and i == 0:
-                ev[1].record(stream)
-            P.add(L, grps[i])
-            P.finalize(1.0 / T)
-            if n_layers == 1 or i + 1 < n_layers:
-                P.down(L, grps_n[i])
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    hot_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
-
-    H, d, I = shape.H, shape.d, shape.I
-    flops_hot = 4.0 * T * H * d * I                          # algorithmic, one launch
-    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_FP32_TFLOPS
-    achieved = flops_hot / (hot_ms * 1e-3) / 1e12
-    esz = 2 if shape.dtype == "bf16" else 4
-    stream_bytes = T * (esz * (H * d + 2 * I) + 8)           # a, g, u, r, r_next read once
-    workload = f"{shape.name}:T={T}"
-    traffic = traffic_for(workload)
-    value = T * 1.0 / (ms_step * 1e-3) if n_layers == 1 else T / (ms_step * 1e-3)
+    progress(f"{shape.name}: inputs ready")
+    P0, ms_step, hot_ms = time_layer(hna, L0, args.steps, args.warmup)
+    progress(f"{shape.name}: {ms_step:.3f} ms per step, hot kernel {hot_ms:.3f} ms")
+    fig = layer_figures(shape, ms_step, hot_ms)
     rec = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC, "value": fig["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": shape.dtype, "data": "synthetic (seeded generator, inputs resident in HBM)",
-        "config": {"workload": shape.name, "T": T, "hidden": shape.hidden, "H": H, "G": shape.G,
-                   "d": d, "I": I, "layers": n_layers},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic},
-        "hot_kernel_ms": hot_ms,
-        "mfma_frac_whole_step": flops_hot * n_layers / (ms_step * 1e-3) / 1e12 / peak,
-        "hot_stream_gbs": stream_bytes / (hot_ms * 1e-3) / 1e9,
+        "config": {"workload": shape.name, "T": shape.T, "hidden": shape.hidden, "H": shape.H,
+                   "G": shape.G, "d": shape.d, "I": shape.I, "layers": 1},
+        "roofline": fig["roofline"],
+        "hot_kernel_ms": fig["hot_kernel_ms"],
+        "mfma_frac_whole_step": fig["mfma_frac_whole_step"],
+        "hot_stream_gbs": fig["hot_stream_gbs"],
     }
-    rec["loo"] = loo_bench(hna, L0, passes[0], grps[0], 5)
-    rec["objective"] = objective_bench(hna, 200)
-    rec["neuron_step"] = neuron_step_bench(hna, 20)
-    rec["layout_search"] = search_bench(hna, 50)
-    if not args.no_cpu_baseline and n_layers == 1:
+    if not args.no_legs:
+        grp = [int(x) for x in L0["group_of_head"].tolist()]
+        rec["loo"] = loo_bench(hna, L0, P0, grp, 5)
+        progress("leave-one-out done")
+        rec["objective"] = objective_bench(hna, 200)
+        rec["neuron_step"] = neuron_step_bench(hna, 20)
+        rec["layout_search"] = search_bench(hna, 50)
+        progress("layout search done")
+        legs = {}
+        for c in (2, 4):
+            if c != args.config:
+                legs[synth.layer_shape(c).name] = layer_leg(hna, c, 10, 2)
+                progress(f"{synth.layer_shape(c).name} done")
+        rec["other_layers"] = legs
+        rec["stack"] = stack_leg(hna, 3, 1, T=args.tokens)
+        progress("stack done")
+    if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(L0)
+        progress("cpu baseline done")
     print(json.dumps(rec), flush=True)
 
 

@@ -12,13 +12,14 @@ from ._binding import (HnaError, HNA_BF16, HNA_F32, HNA_ACCUMULATE, hna_dims, hn
                        last_error, unit_mass, layout_objective, neuron_step,
                        head_step, layout_search, DUAL_ITERS, loo_workspace_bytes,
                        affinity_loo)
-from .pipeline import AffinityPass, pass_for_layer, affinity_layer
+from .pipeline import AffinityPass, StackPass, pass_for_layer, affinity_layer
 
 __all__ = [
     "HnaError", "HNA_BF16", "HNA_F32", "HNA_ACCUMULATE", "hna_dims", "hna_down_dims", "make_dims",
     "lib", "LIB_PATH", "EXPORTED", "fold_up_weights", "down_col_sqnorm", "affinity_up", "affinity_add",
     "finalize_up", "down_weight_norms", "down_combine", "up_workspace_bytes",
     "down_workspace_bytes", "folded_bytes", "status_string", "last_error", "AffinityPass",
+    "StackPass",
     "pass_for_layer", "affinity_layer", "unit_mass", "layout_objective",
     "neuron_step", "head_step", "layout_search", "DUAL_ITERS", "loo_workspace_bytes",
     "affinity_loo",

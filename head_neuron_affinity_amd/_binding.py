@@ -157,6 +157,54 @@ def _need_cuda(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _torch_dtype(dims) -> torch.dtype:
+    return torch.bfloat16 if dims.dtype == HNA_BF16 else torch.float32
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype,
+            tokens: bool = False):
+    """Shape and dtype of an argument, checked before its pointer is handed
+    over (the C ABI sees addresses only, so a short or mistyped tensor would
+    otherwise be read past its end).  With `tokens` the leading (token) dim may
+    be longer than the call's T: the call reads the first T rows."""
+    if t is None:
+        return
+    want = tuple(int(x) for x in shape)
+    got = tuple(t.shape)
+    ok = (len(got) == len(want) and got[1:] == want[1:] and got[0] >= want[0]) if tokens \
+        else got == want
+    if not ok:
+        raise ValueError(f"{name}: shape {got}, expected {want}"
+                         + (" (leading dim at least)" if tokens else ""))
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _expect_bytes(t: torch.Tensor, name: str, nbytes: int):
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _up_inputs(dims: hna_dims, a=None, g=None, u=None, r=None, r_next=None, M=None):
+    dt = _torch_dtype(dims)
+    _expect(a, "a", (dims.T, dims.H, dims.d), dt, tokens=True)
+    _expect(g, "g", (dims.T, dims.I), dt, tokens=True)
+    _expect(u, "u", (dims.T, dims.I), dt, tokens=True)
+    _expect(r, "r", (dims.T,), torch.float32, tokens=True)
+    _expect(r_next, "r_next", (dims.T,), torch.float32, tokens=True)
+    if M is not None:
+        _expect_bytes(M, "M", folded_bytes(dims))
+
+
+def _weights(dims: hna_dims, W_o=None, gamma=None, W_gate=None, W_up=None, W_down=None):
+    dt = _torch_dtype(dims)
+    _expect(W_o, "W_o", (dims.hidden, dims.H * dims.d), dt)
+    _expect(gamma, "gamma", (dims.hidden,), torch.float32)
+    _expect(W_gate, "W_gate", (dims.I, dims.hidden), dt)
+    _expect(W_up, "W_up", (dims.I, dims.hidden), dt)
+    _expect(W_down, "W_down", (dims.hidden, dims.I), dt)
+
+
 # ------------------------------------------------------------------ calls
 def folded_bytes(dims: hna_dims) -> int:
     n = lib().hna_folded_bytes(ctypes.byref(dims))
@@ -169,6 +217,7 @@ def fold_up_weights(dims: hna_dims, W_o, gamma, W_gate, W_up, out: Optional[torc
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """M_h = W_o^(h)T diag(gamma) [W_gate; W_up]^T in the kernel's layout (opaque bytes)."""
     _need_cuda(W_o, gamma, W_gate, W_up)
+    _weights(dims, W_o=W_o, gamma=gamma, W_gate=W_gate, W_up=W_up)
     L = lib()
     nb = folded_bytes(dims)
     if out is None:
@@ -185,8 +234,10 @@ def fold_up_weights(dims: hna_dims, W_o, gamma, W_gate, W_up, out: Optional[torc
 
 def down_col_sqnorm(dims: hna_dims, W_down, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _need_cuda(W_down)
+    _weights(dims, W_down=W_down)
     if out is None:
         out = torch.empty(dims.I, dtype=torch.float32, device=W_down.device)
+    _expect(out, "out", (dims.I,), torch.float32)
     _check(lib().hna_down_col_sqnorm(ctypes.byref(dims), _ptr(W_down), _ptr(out),
                                      _stream(W_down.device)), "hna_down_col_sqnorm")
     return out
@@ -200,6 +251,7 @@ def affinity_up(dims: hna_dims, a, g, u, r, r_next, M, group_of_head,
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The hot pass; returns the workspace holding the partial sums."""
     _need_cuda(a, g, u, r, r_next, M)
+    _up_inputs(dims, a, g, u, r, r_next, M)
     L = lib()
     wsb = L.hna_up_workspace_bytes(ctypes.byref(dims))
     if workspace is None:
@@ -214,6 +266,7 @@ def affinity_up(dims: hna_dims, a, g, u, r, r_next, M, group_of_head,
 def affinity_add(dims: hna_dims, a, r, M, group_of_head, workspace: torch.Tensor) -> torch.Tensor:
     """The ADD score through per-head Gram matrices, into the same workspace."""
     _need_cuda(a, r, M, workspace)
+    _up_inputs(dims, a=a, r=r, M=M)
     _check(lib().hna_affinity_add(ctypes.byref(dims), _ptr(a), _ptr(r), _ptr(M),
                                   _map(group_of_head), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(a.device)),
@@ -231,6 +284,11 @@ def finalize_up(dims: hna_dims, wd_sq, workspace, scale: float, accumulate: bool
         S_add = torch.empty((dims.G, dims.I), dtype=torch.float32, device=dev)
     if c_down is None and want_c:
         c_down = torch.empty(dims.I, dtype=torch.float32, device=dev)
+    _need_cuda(S_fo, S_add, c_down)
+    _expect(wd_sq, "wd_sq", (dims.I,), torch.float32)
+    _expect(S_fo, "S_fo", (dims.G, dims.I), torch.float32)
+    _expect(S_add, "S_add", (dims.G, dims.I), torch.float32)
+    _expect(c_down, "c_down", (dims.I,), torch.float32)
     _check(lib().hna_finalize_up(ctypes.byref(dims), _ptr(wd_sq), float(scale),
                                  HNA_ACCUMULATE if accumulate else 0, _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _ptr(S_fo),
@@ -245,6 +303,12 @@ def down_workspace_bytes(ddims: hna_down_dims) -> int:
 def down_weight_norms(ddims: hna_down_dims, W_q, W_k, W_v, gamma_next, W_down, group_of_head_next,
                       out=None, workspace=None) -> torch.Tensor:
     _need_cuda(W_q, W_k, W_v, gamma_next, W_down)
+    dt = torch.bfloat16 if ddims.dtype == HNA_BF16 else torch.float32
+    _expect(W_q, "W_q", (ddims.H * ddims.d, ddims.hidden), dt)
+    _expect(W_k, "W_k", (ddims.G * ddims.d, ddims.hidden), dt)
+    _expect(W_v, "W_v", (ddims.G * ddims.d, ddims.hidden), dt)
+    _expect(gamma_next, "gamma_next", (ddims.hidden,), torch.float32)
+    _expect(W_down, "W_down", (ddims.hidden, ddims.I), dt)
     L = lib()
     dev = W_q.device
     if out is None:
@@ -263,6 +327,8 @@ def down_weight_norms(ddims: hna_down_dims, W_q, W_k, W_v, gamma_next, W_down, g
 def down_combine(c_down, n, out=None) -> torch.Tensor:
     _need_cuda(c_down, n)
     G, I = n.shape
+    _expect(c_down, "c_down", (I,), torch.float32)
+    _expect(n, "n", (G, I), torch.float32)
     if out is None:
         out = torch.empty((I, G), dtype=torch.float32, device=n.device)
     _check(lib().hna_down_combine(int(I), int(G), _ptr(c_down), _ptr(n), _ptr(out),
@@ -421,6 +487,9 @@ def affinity_loo(dims: hna_dims, a, g, u, x, W_o, gamma, W_gate, W_up, M, group_
     _need_cuda(a, g, u, x, W_o, gamma, W_gate, W_up, M)
     if x.dtype != torch.float32 or gamma.dtype != torch.float32:
         raise ValueError("x and gamma must be fp32")
+    _up_inputs(dims, a=a, g=g, u=u, M=M)
+    _weights(dims, W_o=W_o, gamma=gamma, W_gate=W_gate, W_up=W_up)
+    _expect(x, "x", (dims.T, dims.hidden), torch.float32, tokens=True)
     L = lib()
     dev = M.device
     if S_loo is None:

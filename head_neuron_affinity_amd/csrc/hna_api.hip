@@ -90,10 +90,24 @@ int check_dims(const char* fn, const hna_dims* dm) {
   if (rc) return rc;
   if (dm->T < 0) return fail(HNA_ERR_INVALID_ARG, "%s: T=%lld < 0", fn, (long long)dm->T);
   if (dm->I < 1) return fail(HNA_ERR_INVALID_ARG, "%s: I=%d < 1", fn, dm->I);
-  if (dm->T > ((int64_t)1 << 40))
-    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld too large", fn, (long long)dm->T);
-  if (dm->I > (1 << 22)) return fail(HNA_ERR_UNSUPPORTED, "%s: I=%d too large", fn, dm->I);
-  return check_heads(fn, dm->hidden, dm->H, dm->G, dm->d);
+  // Token counts are held in 32-bit tile counts by the kernels' geometry.
+  if (dm->T > (int64_t)INT32_MAX)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld > 2^31 - 1", fn, (long long)dm->T);
+  if (dm->I > (1 << 22)) return fail(HNA_ERR_UNSUPPORTED, "%s: I=%d > 2^22", fn, dm->I);
+  rc = check_heads(fn, dm->hidden, dm->H, dm->G, dm->d);
+  if (rc) return rc;
+  // the hot kernel's grid (computed in 64 bits): at most 2^24 workgroups, so
+  // that its 256-thread workgroups stay within 2^32 threads
+  const int64_t n_tt = (dm->T + kTileTokens - 1) / kTileTokens;
+  const int64_t n_chunks = (n_tt + kTilesPerChunk - 1) / kTilesPerChunk;
+  const int64_t n_cg = (n_chunks + kSuperChunks - 1) / kSuperChunks;
+  const int64_t n_kt = ((int64_t)round_up(dm->I, 32) + kTileNeurons - 1) / kTileNeurons;
+  const int64_t n_ktg = (n_kt + kSuperKt - 1) / kSuperKt;
+  const int64_t grid = (n_ktg * n_cg + 7) / 8 * 8 * 32;
+  if (grid > ((int64_t)1 << 24))
+    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld with I=%d needs %lld workgroups > 2^24", fn,
+                (long long)dm->T, dm->I, (long long)grid);
+  return HNA_OK;
 }
 
 int check_map(const char* fn, const int32_t* map, int H, int G) {

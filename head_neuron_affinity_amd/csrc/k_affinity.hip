@@ -10,7 +10,11 @@
 //     of the tile and all 128 tokens (4 blocks of 32 in the MFMA C layout);
 //   * once per token tile each lane computes the operating-point
 //     coefficients A = silu'(g) u / r and B = silu(g) / r of its 64 (t, k)
-//     pairs (registers) and the down-edge moment (alpha / r_next)^2;
+//     pairs (registers) and the down-edge moment (alpha / r_next)^2; on the
+//     bf16 path they are kept as packed fp16 pairs, scaled by a power of two
+//     s <= min r of the tile (so s / r <= 1 and they keep fp16's range for
+//     any rms), and the tile's sums are divided by s^2 when they leave the
+//     registers;
 //   * per head h (in KV-group order) the wave runs the contraction a_h . M_h
 //     on the matrix cores as two chain pairs (token blocks 0-1, then 2-3),
 //     2 x 2 x d/16 MFMAs 32x32x16 each into gate and up accumulators, giving
@@ -164,6 +168,7 @@ void affinity_up_kernel(const UpParams p) {
   __shared__ __attribute__((aligned(16))) float rraw[4 * kTileTokens];     // r, pad, r_next, pad
   extern __shared__ __attribute__((aligned(16))) float accl[];             // [G][128] FO sums
   __shared__ int8_t s_order[kMaxHeads], s_group[kMaxHeads];               // head tables
+  __shared__ float s_rmin[2];                                              // per-wave min r of a tile
 
   // workgroup -> (neuron tile, token chunk); consecutive ids alternate XCDs
   const int id = blockIdx.x;
@@ -294,6 +299,9 @@ void affinity_up_kernel(const UpParams p) {
 #pragma unroll
   for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
   float c_acc = 0.f;
+  // 1 / s^2 of the token tile whose sums fo_run holds (bf16 path: the tile's
+  // coefficients carry the factor s)
+  float inv_s2 = 1.f;
   const char* Mbytes = static_cast<const char*>(p.M);
   const uint32_t mlane = (uint32_t)l * 8u * EB;
   // The head's folded-weight fragments, all d-steps.  They are loaded with
@@ -333,7 +341,25 @@ void affinity_up_kernel(const UpParams p) {
       const int64_t t = (int64_t)(tt0 + ti) * kTileTokens + (tid & (kTileTokens - 1));
       const bool ok = t < NT && (tid < kTileTokens || p.want_c);
       const float rv = rraw[(tid < kTileTokens ? 0 : 2 * kTileTokens) + (tid & (kTileTokens - 1))];
-      tokinv[tid] = ok ? __builtin_amdgcn_rcpf(rv) : 0.f;
+      float sc = 1.f;
+      if constexpr (sizeof(E) == 2) {
+        // tile scale: the largest power of two s <= min r over the tile's
+        // tokens (waves 0 and 1 hold the 128 r values), exponent clamped so
+        // that 1 / s^2 stays a normal fp32 value
+        if (tid < kTileTokens) {
+          float m = ok ? rv : __builtin_inff();
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) m = fminf(m, __shfl_xor(m, o));
+          if (l == 0) s_rmin[w] = m;
+        }
+        __syncthreads();
+        const float rmin = fminf(s_rmin[0], s_rmin[1]);
+        int e = rmin > 0.f && rmin < __builtin_inff() ? __builtin_amdgcn_frexp_expf(rmin) - 1 : 0;
+        e = max(-60, min(60, e));
+        if (tid < kTileTokens) sc = __builtin_ldexpf(1.f, e);
+        inv_s2 = __builtin_ldexpf(1.f, -2 * e);
+      }
+      tokinv[tid] = ok ? __builtin_amdgcn_rcpf(rv) * sc : 0.f;
     }
     __syncthreads();
     int64_t tbase = (int64_t)(tt0 + ti) * kTileTokens;
@@ -408,7 +434,7 @@ void affinity_up_kernel(const UpParams p) {
   auto flush = [&](int grp) __attribute__((always_inline)) {
     float fo = (fo_run[0] + fo_run[1]) + (fo_run[2] + fo_run[3]);
     fo += __shfl_xor(fo, 32);
-    if (l < 32) accl[grp * kTileNeurons + nl] += fo;
+    if (l < 32) accl[grp * kTileNeurons + nl] += fo * inv_s2;
 #pragma unroll
     for (int tb = 0; tb < kTB; ++tb) fo_run[tb] = 0.f;
   };

@@ -115,3 +115,87 @@ def affinity_layer(layer: Dict[str, torch.Tensor], with_down: bool = True) -> Di
     """Run the whole pass on one layer dict (tensors on the GPU) and return the scores."""
     ap = pass_for_layer(layer, with_down=with_down)
     return ap.run(layer)
+
+
+class StackPass:
+    """The affinity pass over an N-layer stack (section 3, "Affinity scores").
+
+    Per layer i: the weight fold, ||w^d||^2, the hot pass (FO sums and the
+    down-edge token moment of layer i's neurons), ADD and the fixed-order
+    reduction into S_fo[i], S_add[i].  Per adjacent pair (i, i+1): the down
+    edge from layer i's neurons to layer i+1's KV groups, whose weight part
+    uses layer i+1's attention projections W_q, W_k, W_v and pre-norm gain
+    gamma'.  In a layer dict these sit under "W_q", "W_k", "W_v",
+    "gamma_next" and "group_of_head_next" of layer i (the weights that follow
+    layer i's FFN), with r_next the rms entering layer i+1's pre-norm.
+
+    The weight-only work (fold, ||w^d||^2, down-edge weight norms) of every
+    layer runs on a side stream that runs ahead of the token passes: layer
+    i's token pass waits only for layer i's weights, so the weight GEMMs of
+    later layers overlap the token passes of earlier ones.  Each layer owns
+    its buffers; results are S_fo, S_add [N, G, I] and S_down [N-1, I, G']
+    fp32 on the device.
+    """
+
+    def __init__(self, layers: Sequence[Dict[str, torch.Tensor]], overlap: bool = True):
+        n = len(layers)
+        if n < 1:
+            raise ValueError("a stack needs at least one layer")
+        self.n = n
+        self.passes = [pass_for_layer(L, with_down=(i + 1 < n)) for i, L in enumerate(layers)]
+        self.groups = [[int(x) for x in L["group_of_head"].tolist()] for L in layers]
+        self.groups_next = [[int(x) for x in L["group_of_head_next"].tolist()] if i + 1 < n else None
+                            for i, L in enumerate(layers)]
+        T = self.passes[0].T
+        if any(P.T != T for P in self.passes):
+            raise ValueError("every layer of a stack sees the same calibration tokens")
+        self.T = T
+        self.overlap = overlap
+        dev = self.passes[0].device
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self.ready = [torch.cuda.Event() for _ in range(n)] if overlap else None
+
+    def _weights(self, i, L):
+        P = self.passes[i]
+        P.fold(L)
+        if P.with_down:
+            B.down_weight_norms(P.ddims, L["W_q"], L["W_k"], L["W_v"], L["gamma_next"],
+                                L["W_down"], self.groups_next[i], out=P.n_down,
+                                workspace=P.down_ws)
+
+    def _tokens(self, i, L, scale):
+        P = self.passes[i]
+        P.hot(L, self.groups[i])
+        P.add(L, self.groups[i])
+        P.finalize(scale)
+        if P.with_down:
+            B.down_combine(P.c_down, P.n_down, out=P.S_down)
+
+    def run(self, layers: Sequence[Dict[str, torch.Tensor]], scale: Optional[float] = None):
+        """Enqueue the whole stack on torch's current stream (and the side
+        stream); returns nothing, the scores stay in each layer's buffers."""
+        if len(layers) != self.n:
+            raise ValueError("layer count differs from the one the stack was built for")
+        sc = 1.0 / max(self.T, 1) if scale is None else scale
+        main = torch.cuda.current_stream()
+        if self.overlap:
+            self.side.wait_stream(main)          # inputs and buffers are ready on main
+            with torch.cuda.stream(self.side):
+                for i, L in enumerate(layers):
+                    self._weights(i, L)
+                    self.ready[i].record(self.side)
+            for i, L in enumerate(layers):
+                main.wait_event(self.ready[i])
+                self._tokens(i, L, sc)
+            main.wait_stream(self.side)           # nothing left running on the side
+        else:
+            for i, L in enumerate(layers):
+                self._weights(i, L)
+                self._tokens(i, L, sc)
+
+    def scores(self):
+        """(S_fo [N, G, I], S_add [N, G, I], S_down [N-1, I, G']) stacked copies."""
+        S_fo = torch.stack([P.S_fo for P in self.passes])
+        S_add = torch.stack([P.S_add for P in self.passes])
+        S_down = (torch.stack([P.S_down for P in self.passes[:-1]]) if self.n > 1 else None)
+        return S_fo, S_add, S_down

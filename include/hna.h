@@ -42,8 +42,10 @@
  *     the caller.
  *
  * Supported shapes: H <= 128, 1 <= G <= H, H % G == 0, 0 <= group_of_head[h]
- * < G; d a multiple of 16 with d <= 128; hidden >= 1; I >= 1; T >= 0.
- * Others return HNA_ERR_UNSUPPORTED.
+ * < G; d a multiple of 16 with d <= 128; hidden a positive multiple of 8;
+ * 1 <= I <= 2^22; 0 <= T <= 2^31 - 1, and T and I such that the hot kernel
+ * needs at most 2^24 workgroups (about 2^31 tokens at I = 3072).  Others
+ * return HNA_ERR_UNSUPPORTED (HNA_ERR_INVALID_ARG for non-positive sizes).
  */
 #ifndef HNA_H
 #define HNA_H

@@ -18,6 +18,11 @@ fixed order):
   x0   ~ N(0, 1)                          residual before attention, [T, hidden]
   W_q ~ N(0, 1/hidden) [H*d, hidden], W_k, W_v ~ N(0, 1/hidden) [G*d, hidden]
   gamma_next = 1 + 0.1*N(0, 1)            next layer's attention pre-norm gain
+  (optional, drawn last) massive-activation tokens: each token is picked
+  with probability frac, and value is added to residual dimension dim of x0
+  on the picked tokens (the delimiter-token spikes of roughly 7000 in one
+  residual dimension described in section 5, "Where the affinity
+  concentrates"; the rms of such a token is about value / sqrt(hidden))
 
 Derived quantities (float64, from the values already rounded to the storage
 dtype, so that they are consistent with what the kernels see):
@@ -116,7 +121,8 @@ def _randn(gen: torch.Generator, shape, device) -> torch.Tensor:
 
 def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = True,
                token_chunk: int = 8192, return_resid: bool = False,
-               with_x: bool = False) -> Dict[str, torch.Tensor]:
+               with_x: bool = False,
+               massive: Optional[tuple] = None) -> Dict[str, torch.Tensor]:
     """Draw one synthetic layer.
 
     Returns a dict of tensors on ``device``.  Matrices use the (out, in)
@@ -128,6 +134,9 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
     With ``with_x`` the residual entering the FFN norm is returned as "x_in",
     rounded to float32 (float64 for "f64"): the input of the leave-one-out
     score, which renormalises the residual without a head.
+    ``massive`` = (frac, dim, value) adds massive-activation tokens (see the
+    module docstring); the draw comes after every other one, so the rest of
+    the layer is the same as without it.
     """
     device = torch.device(device)
     T, D, H, G, d, I = shape.T, shape.hidden, shape.H, shape.G, shape.d, shape.I
@@ -153,6 +162,10 @@ def make_layer(shape: LayerShape, seed: int, device="cpu", with_next: bool = Tru
         nxt["W_v"] = _round(_randn(gen, (G * d, D), device) / math.sqrt(D), st)
         gn = 1.0 + 0.1 * _randn(gen, (D,), device)
         nxt["gamma_next"] = _round(gn, "bf16" if st == "bf16" else st)
+    if massive is not None:
+        frac, mdim, mval = massive
+        picked = torch.rand((T,), generator=gen, dtype=torch.float64, device=device) < frac
+        x0[picked, int(mdim)] += float(mval)
 
     out_dt = _STORE[st]
     scal_dt = torch.float64 if st == "f64" else torch.float32

@@ -83,6 +83,9 @@ def call_up(hna, dm, a=FAKE, g=FAKE, u=FAKE, r=FAKE, rn=None, M=FAKE, grp=(0, 0,
     (dict(T=-1), -1),
     (dict(H=0), -1),
     (dict(H=256, G=2), -2),        # too many heads
+    (dict(T=2**31), -2),           # tokens beyond the kernels' 32-bit tile counts
+    (dict(T=2**31 - 1, I=1 << 22), -2),   # hot-kernel grid beyond 2^24 workgroups
+    (dict(I=(1 << 22) + 1), -2),   # too many neurons
 ])
 def test_bad_dims_rejected(kw, status):
     hna = _lib()
@@ -336,3 +339,31 @@ def test_error_text_is_thread_local():
     t.start()
     t.join()
     assert mine and seen == [""]
+
+
+def test_binding_checks_shapes_and_dtypes():
+    """The binding checks every tensor's shape and dtype against the dims
+    before handing its address to the library (no GPU needed: the checks run
+    on tensor metadata)."""
+    import torch
+    hna = _lib()
+    from head_neuron_affinity_amd import _binding as B
+    dm = dims(hna, T=10, hidden=64, H=4, G=2, d=16, I=40, dtype=1)
+    bf = torch.bfloat16
+    B._up_inputs(dm, a=torch.empty(10, 4, 16, dtype=bf), g=torch.empty(10, 40, dtype=bf),
+                 r=torch.empty(10))
+    B._up_inputs(dm, a=torch.empty(12, 4, 16, dtype=bf))      # longer token buffer: first T rows
+    with pytest.raises(ValueError, match="a: shape"):
+        B._up_inputs(dm, a=torch.empty(9, 4, 16, dtype=bf))   # too few tokens
+    with pytest.raises(ValueError, match="g: shape"):
+        B._up_inputs(dm, g=torch.empty(10, 41, dtype=bf))
+    with pytest.raises(ValueError, match="u: dtype"):
+        B._up_inputs(dm, u=torch.empty(10, 40, dtype=torch.float32))
+    with pytest.raises(ValueError, match="r: dtype"):
+        B._up_inputs(dm, r=torch.empty(10, dtype=bf))
+    with pytest.raises(ValueError, match="M:"):
+        B._up_inputs(dm, M=torch.empty(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="W_o: shape"):
+        B._weights(dm, W_o=torch.empty(64, 60, dtype=bf))
+    with pytest.raises(ValueError, match="W_down: dtype"):
+        B._weights(dm, W_down=torch.empty(64, 40, dtype=torch.float32))

@@ -1,0 +1,158 @@
+"""Parity of every hot-kernel instantiation and of the operating-point edge
+cases, through the C ABI, against the float64 oracle.
+
+The hot kernel is compiled once per (input dtype, d / 16, g/u staging): bf16
+stages the g and u tiles through LDS when I % 8 == 0 and reads them directly
+otherwise; fp32 always reads them directly.  Each instantiation is run here on
+a small layer whose token count spans several 1024-token chunks with a ragged
+last tile, and whose neuron count leaves a ragged last neuron tile.
+
+The edge cases follow the operating points that eq. (5) of section 3
+("Affinity scores") passes through: g = 0 (silu' = 1/2, silu = 0), u = 0 (only
+the silu term is left), |g| = 30 (silu' -> 1 or -> 0), a head whose output is
+zero, tokens whose rms is about 200-300 because one residual dimension holds a
+spike of about 7000 (section 5, "Where the affinity concentrates"), and token
+rms values far outside the usual range on either side.  The oracle takes g, u
+and r as given inputs, so each case is a valid input of the definition.
+
+Tolerances: fp32 inputs, max|dS| / max|S| <= 1e-4 per output matrix; bf16
+inputs with fp32 accumulation, relative Frobenius ||dS|| / ||S|| <= 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-4
+BF16_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def hna():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import head_neuron_affinity_amd as m
+    m.lib()
+    return m
+
+
+def dev(layer):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) and not k.startswith("group_of") else v)
+            for k, v in layer.items()}
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def max_rel(x, ref):
+    return float(np.max(np.abs(x - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def fro_rel(x, ref):
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def check_layer(hna, L, dtype):
+    out = hna.affinity_layer(dev(L))
+    torch.cuda.synchronize()
+    got = {k: f64(v) for k, v in out.items()}
+    ref = oracle.affinity_layer(L)
+    tol, metric = (FP32_TOL, max_rel) if dtype == "f32" else (BF16_TOL, fro_rel)
+    for key in ("S_fo", "S_add", "c_down", "n_down", "S_down"):
+        assert np.all(np.isfinite(got[key])), key
+        err = metric(got[key], ref[key])
+        print(f"  {key}: err={err:.3e}", flush=True)
+        assert err <= tol, f"{key}: {err:.3e} > {tol}"
+        assert np.all(got[key] >= 0), key
+
+
+# ------------------------------------------------- every kernel instantiation
+SWEEP = ([("bf16", d, I) for d in range(16, 129, 16) for I in (264, 261)]
+         + [("f32", d, 261) for d in range(16, 129, 16)])
+
+
+@pytest.mark.parametrize("dtype,d,I", SWEEP)
+def test_instantiation(hna, dtype, d, I):
+    """T = 2333 tokens: three 1024-token chunks, the last one ending in a
+    ragged 29-token tile; I = 264 (bf16 g/u through LDS, ragged neuron tile)
+    or 261 (direct g/u reads, I % 8 != 0)."""
+    T, hidden, H, G = 2333, 64, 4, 2
+    print(f"dtype={dtype} d={d} I={I} T={T}", flush=True)
+    sh = synth.LayerShape("sweep", T, hidden, H, G, d, I, dtype, 0.5)
+    check_layer(hna, synth.make_layer(sh, seed=1000 + d + I), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_head_single_neuron(hna, dtype):
+    """The smallest shapes: one head in one group, one neuron, 77 tokens."""
+    sh = synth.LayerShape("min", 77, 16, 1, 1, 16, 1, dtype, 0.5)
+    check_layer(hna, synth.make_layer(sh, seed=7), dtype)
+
+
+# ------------------------------------------------------ operating-point edges
+EDGE_SHAPE = dict(T=1100, hidden=1024, H=8, G=4, d=128, I=1024)
+
+
+def edge_layer(dtype, seed, massive=None):
+    s = EDGE_SHAPE
+    sh = synth.LayerShape("edge", s["T"], s["hidden"], s["H"], s["G"], s["d"], s["I"], dtype, 0.5)
+    return synth.make_layer(sh, seed=seed, massive=massive)
+
+
+def set_tokens(L, key, t0, t1, value):
+    x = L[key].clone()
+    x[t0:t1] = value
+    L[key] = x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_operating_points(hna, dtype):
+    """Blocks of tokens at g = 0, u = 0, g = +30, g = -30 and g = +-30 with
+    |u| = 30, and one head whose output is zero."""
+    print(f"dtype={dtype}: operating points", flush=True)
+    L = edge_layer(dtype, 21)
+    set_tokens(L, "g", 0, 130, 0.0)
+    set_tokens(L, "u", 130, 260, 0.0)
+    set_tokens(L, "g", 260, 390, 30.0)
+    set_tokens(L, "g", 390, 520, -30.0)
+    sign = torch.where(torch.arange(L["g"].shape[1]) % 2 == 0, 1.0, -1.0).to(L["g"].dtype)
+    set_tokens(L, "g", 520, 650, 30.0 * sign)
+    set_tokens(L, "u", 520, 650, -30.0 * sign)
+    a = L["a"].clone()
+    a[:, 3, :] = 0
+    L["a"] = a
+    check_layer(hna, L, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("frac", [1.0, 0.05])
+def test_edge_massive_activation_tokens(hna, dtype, frac):
+    """A residual spike of 7000 in one dimension on every token (frac = 1:
+    r is about 7000 / sqrt(1024) ~ 219 throughout, so every coefficient
+    silu'(g) u / r and silu(g) / r is ~200 times smaller than usual), or on 5%
+    of the tokens (the mix of a real calibration set)."""
+    print(f"dtype={dtype}: massive-activation tokens, fraction {frac}", flush=True)
+    L = edge_layer(dtype, 22, massive=(frac, 7, 7000.0))
+    r = L["r"].double()
+    if frac == 1.0:
+        assert float(r.min()) > 150.0
+    else:
+        assert float(r.max()) > 150.0 and float(r.min()) < 3.0
+    check_layer(hna, L, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("r_scale", [1e-4, 1e4])
+def test_edge_extreme_rms(hna, dtype, r_scale):
+    """Token rms scaled by 1e-4 (coefficients up to ~1e5) or by 1e4
+    (coefficients down to ~1e-9): both far outside half precision's range,
+    inside fp32's.  Only the up edge sees r; r_next is left as drawn."""
+    print(f"dtype={dtype}: r scaled by {r_scale}", flush=True)
+    L = edge_layer(dtype, 23)
+    L["r"] = (L["r"].double() * r_scale).to(L["r"].dtype)
+    check_layer(hna, L, dtype)
