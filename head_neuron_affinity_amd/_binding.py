@@ -40,7 +40,7 @@ EXPORTED = [
     "hna_down_workspace_bytes", "hna_down_weight_norms", "hna_down_combine", "hna_unit_mass",
     "hna_layout_objective", "hna_neuron_step", "hna_head_step",
     "hna_layout_search_workspace_bytes", "hna_layout_search", "hna_loo_workspace_bytes",
-    "hna_affinity_loo",
+    "hna_affinity_loo", "hna_static_scratch_bytes", "hna_affinity_up_static",
 ]
 
 
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         "hna_head_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
         "hna_layout_search_workspace_bytes": (sz, [i32, i32, i32]),
         "hna_loo_workspace_bytes": (sz, [dp]),
+        "hna_static_scratch_bytes": (sz, []),
+        "hna_affinity_up_static": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, ip, f32,
+                                                  ctypes.c_int, vp, vp, vp, vp]),
         "hna_affinity_loo": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, f32, vp, vp,
                                             sz, vp]),
         "hna_layout_search": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp,
@@ -503,3 +506,28 @@ def affinity_loo(dims: hna_dims, a, g, u, x, W_o, gamma, W_gate, W_up, M, group_
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(dev)), "hna_affinity_loo")
     return S_loo
+
+
+# ------------------------------------------------ allocation-free up pass
+def static_scratch_bytes() -> int:
+    return int(lib().hna_static_scratch_bytes())
+
+
+def affinity_up_static(dims: hna_dims, a, g, u, r, r_next, M, wd_sq, group_of_head, scale: float,
+                       S_fo: torch.Tensor, S_add: torch.Tensor, c_down: Optional[torch.Tensor] = None,
+                       accumulate: bool = False):
+    """hna_affinity_up + hna_affinity_add + hna_finalize_up in one call on the
+    library's fixed scratch array: no workspace, and nothing is allocated
+    here either (the caller passes every output)."""
+    _need_cuda(a, g, u, r, r_next, M, wd_sq, S_fo, S_add, c_down)
+    _up_inputs(dims, a, g, u, r, r_next, M)
+    _expect(wd_sq, "wd_sq", (dims.I,), torch.float32)
+    _expect(S_fo, "S_fo", (dims.G, dims.I), torch.float32)
+    _expect(S_add, "S_add", (dims.G, dims.I), torch.float32)
+    _expect(c_down, "c_down", (dims.I,), torch.float32)
+    _check(lib().hna_affinity_up_static(ctypes.byref(dims), _ptr(a), _ptr(g), _ptr(u), _ptr(r),
+                                        _ptr(r_next), _ptr(M), _ptr(wd_sq), _map(group_of_head),
+                                        float(scale), HNA_ACCUMULATE if accumulate else 0,
+                                        _ptr(S_fo), _ptr(S_add), _ptr(c_down), _stream(M.device)),
+           "hna_affinity_up_static")
+    return S_fo, S_add, c_down

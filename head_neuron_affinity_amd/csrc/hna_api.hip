@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -363,6 +364,79 @@ int hna_finalize_up(const hna_dims* dm, const float* wd_sq, float scale, int fla
                                    dm->G, dm->I, geo.I32, wd_sq, scale, flags & HNA_ACCUMULATE,
                                    S_fo, S_add, c_down, st),
                 st, fn);
+}
+
+// ------------------------------------------------ allocation-free up pass
+// Scratch of hna_affinity_up_static: a fixed array in device memory, one copy
+// per GPU the library runs on, held until the process ends.  Host code never
+// names the array itself (its host-side name is not a device address): the
+// address comes from hipGetSymbolAddress once per device and is kept below.
+}  // extern "C"
+
+namespace {
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxScratchDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that
+// device, with that device current).
+int static_scratch(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices with a scratch copy", fn,
+                dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (!ptr) return fail(HNA_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HNA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t hna_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int hna_affinity_up_static(const hna_dims* dm, const void* a, const void* g, const void* u,
+                           const float* r, const float* r_next, const void* M, const float* wd_sq,
+                           const int32_t* group_of_head, float scale, int flags, float* S_fo,
+                           float* S_add, float* c_down, void* stream) {
+  const char* fn = "hna_affinity_up_static";
+  int rc = check_dims(fn, dm);
+  if (rc) return rc;
+  rc = check_map(fn, group_of_head, dm->H, dm->G);
+  if (rc) return rc;
+  if (flags & ~HNA_ACCUMULATE) return fail(HNA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+  if (!r_next != !c_down)
+    return fail(HNA_ERR_INVALID_ARG, "%s: r_next and c_down must both be given or both be NULL", fn);
+  const size_t need = up_ws_bytes(dm);
+  if (need > kStaticScratchBytes)
+    return fail(HNA_ERR_WORKSPACE,
+                "%s: T=%lld needs %zu bytes of scratch, more than the fixed %zu: pass fewer "
+                "tokens per call (HNA_ACCUMULATE adds the calls up)",
+                fn, (long long)dm->T, need, kStaticScratchBytes);
+  void* ws = nullptr;
+  rc = static_scratch(fn, &ws);
+  if (rc) return rc;
+  // The same three steps as hna_affinity_up, hna_affinity_add and
+  // hna_finalize_up, on the scratch instead of a caller's workspace.  Every
+  // region they read is written first in the same call, so nothing needs
+  // clearing.
+  rc = hna_affinity_up(dm, a, g, u, r, r_next, M, group_of_head, ws, kStaticScratchBytes, stream);
+  if (rc) return rc;
+  rc = hna_affinity_add(dm, a, r, M, group_of_head, ws, kStaticScratchBytes, stream);
+  if (rc) return rc;
+  return hna_finalize_up(dm, wd_sq, scale, flags, ws, kStaticScratchBytes, S_fo, S_add, c_down,
+                         stream);
 }
 
 size_t hna_down_workspace_bytes(const hna_down_dims* dm) {

@@ -180,6 +180,33 @@ int hna_finalize_up(const hna_dims* dims, const float* wd_sq, float scale, int f
                     const void* workspace, size_t workspace_bytes,
                     float* S_fo, float* S_add, float* c_down, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the three
+ * calls above in one, hna_affinity_up + hna_affinity_add + hna_finalize_up
+ * with the same arguments and results, whose partial sums live in a fixed
+ * scratch array of hna_static_scratch_bytes() (64 MiB) compiled into the
+ * library instead of a caller's workspace.  Nothing is allocated: each GPU
+ * the library runs on holds its own copy of the array from the first call on
+ * it until the process ends (its address is looked up once per device, with
+ * that device current).
+ *   Outputs: S_fo, S_add [G, I] and, when r_next is given, c_down [I]
+ *   (r_next and c_down are both given or both NULL); flags and scale as for
+ *   hna_finalize_up (HNA_ACCUMULATE adds token chunks up).
+ * Calls that need more scratch than the array holds (about 100 MB for
+ * 131,072 tokens of a 32-head, 14,336-neuron layer) return
+ * HNA_ERR_WORKSPACE: split the tokens over calls with HNA_ACCUMULATE.  Every
+ * call on one GPU uses that GPU's one array and leaves its contents behind;
+ * each call writes every region it reads before reading it, so no clearing
+ * is needed.  Calls on one GPU that overlap (concurrent streams, or threads
+ * without ordering) race on the array: order them on one stream.
+ */
+size_t hna_static_scratch_bytes(void);
+int hna_affinity_up_static(const hna_dims* dims, const void* a, const void* g, const void* u,
+                           const float* r, const float* r_next, const void* M, const float* wd_sq,
+                           const int32_t* group_of_head, float scale, int flags, float* S_fo,
+                           float* S_add, float* c_down, void* stream);
+
 /* -------------------------------------------------------------- down edge */
 
 /* Bytes of workspace hna_down_weight_norms needs. */
