@@ -200,6 +200,9 @@ int hna_fold_up_weights(const hna_dims* dm, const void* W_o, const float* gamma,
   p.d = dm->d;
   p.KB = p.N / 32;
   p.S = dm->d / 16;
+  if (dm->dtype == HNA_BF16) {
+    return finish(launch_mm_bf16(p, kEpiFold, 2, st), st, fn);
+  }
   dim3 grid((p.N + 127) / 128, (Hd + 127) / 128, 2);
   return finish(launch_gemm(p, dm->dtype, kEpiFold, grid, st), st, fn);
 }
@@ -489,7 +492,12 @@ int hna_down_weight_norms(const hna_down_dims* dm, const void* W_q, const void* 
   p.G_next = dm->G;
   p.d_next = dm->d;
   const int nseg = dm->H + 2 * dm->G;
-  e = launch_gemm(p, dm->dtype, kEpiSegSq, dim3((dm->I + 127) / 128, nseg, 1), st);
+  if (dm->dtype == HNA_BF16) {
+    // segments of W_q (one per query head), then of W_k and W_v (one per group)
+    e = launch_mm_bf16(p, kEpiSegSq, nseg, st);
+  } else {
+    e = launch_gemm(p, dm->dtype, kEpiSegSq, dim3((dm->I + 127) / 128, nseg, 1), st);
+  }
   if (e != hipSuccess) return hip_fail(e, fn);
   // segments of group g': its query heads (ascending), then its k rows, then its v rows
   int16_t seg_list[3 * kMaxHeads];

@@ -190,11 +190,13 @@ hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st);
 // c contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a
 // row-major X [K, Mrows].  Epilogues: write the folded layout, or sum C^2 over
 // the n of a segment.
-enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1 };
+// The plain store writes C[m, n] (fp32 or the input dtype) at C + m * ldc + n,
+// or at C + n * ldc + m when transposed.
+enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1, kEpiStore = 2 };
 
 struct GemmParams {
   const void* X;       // Xs [Mrows, K]
-  const void* Y[3];    // fold: Y[0] = W_gate, Y[1] = W_up; segsq: W_q, W_k, W_v
+  const void* Y[3];    // fold: Y[0] = W_gate, Y[1] = W_up; segsq: W_q, W_k, W_v; store: Y[0]
   int64_t ldx, ldy;
   int Mrows, N, K;     // fold: N = I32 (rows of Y beyond Nvalid are zero)
   int Nvalid;
@@ -204,7 +206,20 @@ struct GemmParams {
   // segment-square output
   float* seg_part;     // [n_seg][Mrows]
   int H_next, G_next, d_next;
+  // plain-store output; grid.y indexes batches (X, Y and C advance by bx, by,
+  // bc elements) or, when k_split > 0, chunks of k_split along K (C advances
+  // by bc, one fp32 part per chunk)
+  void* C;
+  int64_t ldc, bx, by, bc;
+  int k_split;
+  int trans;           // store C transposed
+  int out_bf16;        // store in bf16 (fp32 otherwise)
 };
+// The bf16 GEMM (k_mm.hip): grid y runs over gate / up (fold, ny = 2), the
+// H' + 2 G' segments of W_q, W_k, W_v (segment square), or batches / K chunks
+// of Y[0] (store).  X, Y rows 16-byte aligned (ldx, ldy multiples of 8), K and
+// k_split multiples of 8.
+hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st);
 
 
 // The leave-one-out score through its split T1 + 2 T2 + T3 (see k_loo.hip).

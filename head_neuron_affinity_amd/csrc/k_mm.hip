@@ -1,0 +1,316 @@
+// bf16 "NT" GEMM on the matrix cores for the weight products of the affinity
+// pass and of the leave-one-out score: C[m, n] = sum_k X[m, k] Y[n, k], X and Y
+// row-major with k contiguous, fp32 accumulation.  Three epilogues:
+//   * fold (section 3, "Affinity scores": M_h = W_o^(h)T diag(gamma) W^T): C is
+//     written in the fragment order of the folded weights;
+//   * segment square (the down edge's ||b_gk||^2): C^2 summed over the rows n
+//     of one W_q / W_k / W_v segment, b never stored;
+//   * plain store, fp32 or bf16, C or its transpose, per batch or per K chunk.
+// Workgroup tile BM x BN x 64 on WGM x WGN waves, each wave (BM/WGM) x
+// (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
+// The fold runs 256 x 256 tiles on 8 waves (two per SIMD, so one wave's
+// MFMAs overlap the other's LDS reads and barrier waits); the segment square
+// and the plain store run 128 x 128 (or 128 x 256) tiles on 4 waves, two
+// workgroups per CU.  Both operand tiles arrive in LDS by asynchronous
+// 16-byte buffer -> LDS copies into a ring of NST stages: the copies of K
+// step k + NST - 1 are issued before the MFMAs of step k.  LDS rows of 64
+// elements (128 bytes) hold their 16-byte chunks XOR-swizzled by the row's
+// low 3 bits, so a fragment read (32 rows, one chunk) touches each bank slot
+// once per 8 rows.  Rows past M or N and elements past K read zeros (buffer
+// range check, chunk masking); K must be a multiple of 8.  Workgroup ids map
+// tiles XCD by XCD, in groups of 4 tile rows, so the workgroups that share an
+// XCD's L2 at one time share operand panels.
+#include "hna_internal.h"
+#include "hna_hot.h"
+
+namespace hna {
+namespace {
+
+using namespace hot;
+
+constexpr int BK = 64;                  // K per stage (one 128-byte LDS row)
+
+
+// Asynchronous 16-byte buffer -> LDS copy with a scalar offset soff added to
+// the address (voff is what the range check covers); lane l writes LDS
+// m0 + 16 l.  The resource is passed as its four descriptor words.
+__device__ inline void dma16s(u32x4 rs, uint32_t voff, uint32_t soff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+
+// Raw buffer descriptor words (32-bit data format, no swizzle, stride 0) over
+// [base, base + bytes), built from values the compiler may not see as uniform
+// (they are): each word goes through readfirstlane, so the descriptor lives
+// in scalar registers.
+__device__ inline u32x4 uniform_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu;
+  d.z = __builtin_amdgcn_readfirstlane(bytes);
+  d.w = 0x00020000u;
+  return d;
+}
+
+template <int BM, int BN, int WGM, int WGN, int NST, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParams p) {
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  constexpr int NW = WGM * WGN;               // waves, WGM x WGN
+  constexpr int WM = BM / WGM, WN = BN / WGN; // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 tiles per wave
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * 128;           // bytes per stage
+  constexpr int NCP = ROWS / (8 * NW);        // copies per thread per stage
+  constexpr int NCX = BM / (8 * NW);          // of which X rows
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy rounds cover whole rows");
+  static_assert(EPI != kEpiSegSq || (BN == 128 && BM <= 64 * NW), "a segment is one tile column");
+
+  static_assert((NST - 2) * NCP <= 63, "copies in flight must fit the wait counter");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STAGE];
+  __shared__ float red[WGN][BM];
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WGN, wn = w % WGN;
+
+  // ---- tile of this workgroup ----
+  const int N = EPI == kEpiSegSq ? p.d_next : p.N;
+  const int ntm = (p.Mrows + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  const int ntiles = ntm * ntn;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  // tiles in groups of GM tile rows, column by column within a group: the
+  // workgroups an XCD runs at once cover a few rows and columns of tiles
+  constexpr int GM = 4;
+  const int gsize = GM * ntn;
+  const int g0 = (t / gsize) * GM, gm = min(GM, ntm - g0), tg = t - (g0 / GM) * gsize;
+  const int tm = g0 + tg % gm, tn = tg / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.y;
+
+  // Y: the gate (z = 0) or up (z = 1) matrix (fold); for the segment square
+  // segment z of W_q (z < H'), W_k, then W_v (d' rows each); batch or K chunk
+  // z (store)
+  const __bf16* X = static_cast<const __bf16*>(p.X);
+  const __bf16* Y;
+  int Nrows;
+  int kbeg = 0, kend = p.K;
+  if constexpr (EPI == kEpiFold) {
+    Y = static_cast<const __bf16*>(z ? p.Y[1] : p.Y[0]);
+    Nrows = p.Nvalid;
+  } else if constexpr (EPI == kEpiSegSq) {
+    const int c = z < p.H_next ? 0 : (z < p.H_next + p.G_next ? 1 : 2);
+    const int zs = z - (c == 0 ? 0 : (c == 1 ? p.H_next : p.H_next + p.G_next));
+    Y = static_cast<const __bf16*>(c == 0 ? p.Y[0] : (c == 1 ? p.Y[1] : p.Y[2])) +
+        (int64_t)zs * p.d_next * p.ldy;
+    Nrows = p.d_next;
+  } else {
+    Y = static_cast<const __bf16*>(p.Y[0]);
+    Nrows = p.N;
+    if (p.k_split > 0) {
+      kbeg = z * p.k_split;
+      kend = min(p.K, kbeg + p.k_split);
+    } else {
+      X += (int64_t)z * p.bx;
+      Y += (int64_t)z * p.by;
+    }
+  }
+  // resources over the rows from m0 / n0 on (rows past the end read zeros)
+  const uint32_t lim = 0x7ffff000u;
+  const int64_t xb = (int64_t)max(0, p.Mrows - m0) * p.ldx * 2;
+  const int64_t yb = (int64_t)max(0, Nrows - n0) * p.ldy * 2;
+  const uint32_t xbytes = xb > (int64_t)lim ? lim : (uint32_t)xb;
+  const uint32_t ybytes = yb > (int64_t)lim ? lim : (uint32_t)yb;
+  const u32x4 rx = uniform_rsrc(X + (int64_t)m0 * p.ldx, xbytes);
+  const u32x4 ry = uniform_rsrc(Y + (int64_t)n0 * p.ldy, ybytes);
+
+  // ---- copies: copy i of wave w fills rows 8 (4 i + w) .. + 7 of the stage
+  // (X rows first, then Y rows); lane l: row + l / 8, slot l % 8 holding
+  // chunk (l % 8) ^ (row & 7) ----
+  uint32_t voff[NCP];
+  int kc[NCP];   // element offset of the lane's chunk within the stage
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int r = 8 * (NW * i + w) + (l >> 3);
+    const int c = (l & 7) ^ (r & 7);
+    kc[i] = 8 * c;
+    voff[i] = i < NCX ? (uint32_t)((int64_t)r * p.ldx * 2 + 16 * c)
+                      : (uint32_t)((int64_t)(r - BM) * p.ldy * 2 + 16 * c);
+  }
+  const uint32_t lds0 = lds_addr(lds) + (uint32_t)w * 1024u;
+  auto issue = [&](int k0, int buf) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + (uint32_t)(buf * STAGE);
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
+    const bool tail = k0 + BK > kend;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const uint32_t v = tail && k0 + kc[i] >= kend ? kOutOfRange : voff[i];
+      dma16s(i < NCX ? rx : ry, v, soff, base + (uint32_t)(i * NW * 1024));
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < nk) issue(kbeg + st * BK, st);
+  for (int kt = 0; kt < nk; ++kt) {
+    // step kt has landed once at most the copies of the steps after it that
+    // are in flight remain (copies complete in issue order); the barrier
+    // makes it visible to every wave and ends every wave's reads of step
+    // kt - 1, whose stage the next copies overwrite
+    const int ahead = min(NST - 2, nk - 1 - kt);
+    if (NST >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * NCP));
+    else if (NST >= 3 && ahead >= 1) __builtin_amdgcn_s_waitcnt(vm_wait(NCP));
+    else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __syncthreads();
+    if (kt + NST - 1 < nk) issue(kbeg + (kt + NST - 1) * BK, (kt + NST - 1) % NST);
+    const unsigned char* sb = lds + (kt % NST) * STAGE;
+    constexpr int NKS = BK / 16;
+    auto rd = [&](int ks, uint4 (&fa)[TM][1], uint4 (&fb)[TN][1]) __attribute__((always_inline)) {
+      const int col = 2 * ks + (l >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 32 + (l & 31);
+        fa[i][0] = *reinterpret_cast<const uint4*>(sb + r * 128 + ((col ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = BM + wn * WN + j * 32 + (l & 31);
+        fb[j][0] = *reinterpret_cast<const uint4*>(sb + r * 128 + ((col ^ (r & 7)) << 4));
+      }
+    };
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 af[TM][1], bfr[TN][1];
+      rd(ks, af, bfr);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mma(acc[i][j], af[i], bfr[j]);
+    }
+  }
+
+  // ---- epilogues: lane l holds column (l & 31) and rows
+  // 8 (v / 4) + 4 (l / 32) + (v % 4) of each 32x32 tile ----
+  if constexpr (EPI == kEpiFold) {
+    // lanes l and l ^ 32 swap halves so that each lane owns two whole groups
+    // of 8 rows (8 consecutive j of one neuron: one 16-byte piece of the
+    // folded layout)
+    const int upl = l >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        uint32_t mine[4][2];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          mine[a][0] = f32_to_bf16_bits(acc[i][j][4 * a]) | (f32_to_bf16_bits(acc[i][j][4 * a + 1]) << 16);
+          mine[a][1] = f32_to_bf16_bits(acc[i][j][4 * a + 2]) | (f32_to_bf16_bits(acc[i][j][4 * a + 3]) << 16);
+        }
+        const int n = n0 + wn * WN + j * 32 + (l & 31);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int ka = 2 * b + upl;
+          uint32_t lo_w[2], hi_w[2];
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const uint32_t send = upl ? mine[2 * b][v] : mine[2 * b + 1][v];
+            const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+            const uint32_t keep = upl ? mine[2 * b + 1][v] : mine[2 * b][v];
+            lo_w[v] = upl ? recv : keep;
+            hi_w[v] = upl ? keep : recv;
+          }
+          const int m = m0 + wm * WM + i * 32 + 8 * ka;
+          if (m < p.Mrows && n < p.N) {
+            const int h = m / p.d, jj = m - h * p.d;
+            const int64_t o = folded_index(h, jj, n, z, p.KB, p.S);
+            *reinterpret_cast<uint4*>(static_cast<__bf16*>(p.M) + o) =
+                make_uint4(lo_w[0], lo_w[1], hi_w[0], hi_w[1]);
+          }
+        }
+      }
+  } else if constexpr (EPI == kEpiSegSq) {
+    // sum of squares over this segment's rows n (the tile's columns)
+    float sq[TM][16];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) s2 = fmaf(acc[i][j][v], acc[i][j][v], s2);
+        sq[i][v] = s2;
+      }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sq[i][v] += __shfl_xor(sq[i][v], off);
+    if ((l & 31) == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          red[wn][wm * WM + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = sq[i][v];
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < p.Mrows) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < WGN; ++q) t += red[q][tid];
+      p.seg_part[(int64_t)z * p.Mrows + m0 + tid] = t;
+    }
+  } else {
+    char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + (l & 31);
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int mb = m0 + wm * WM + i * 32 + 8 * a + 4 * (l >> 5);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = mb + e;
+            if (m >= p.Mrows) continue;
+            const float v = acc[i][j][4 * a + e];
+            const int64_t o = p.trans ? (int64_t)n * p.ldc + m : (int64_t)m * p.ldc + n;
+            if (p.out_bf16) reinterpret_cast<uint16_t*>(Cb)[o] = (uint16_t)f32_to_bf16_bits(v);
+            else reinterpret_cast<float*>(Cb)[o] = v;
+          }
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NST, int EPI>
+void launch_t(const GemmParams& p, int ny, hipStream_t st) {
+  const int N = EPI == kEpiSegSq ? p.d_next : p.N;
+  const int ntiles = ((p.Mrows + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const dim3 grid(8 * ((ntiles + 7) / 8), ny);
+  hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, WGM, WGN, NST, EPI>), grid, dim3(64 * WGM * WGN), 0, st, p);
+}
+
+}  // namespace
+
+hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
+  if (ny == 0 || p.Mrows == 0) return hipSuccess;
+  if (epilogue == kEpiSegSq) launch_t<128, 128, 2, 2, 2, kEpiSegSq>(p, ny, st);
+  else if (epilogue == kEpiFold) launch_t<256, 256, 4, 2, 2, kEpiFold>(p, ny, st);
+  else if (p.N <= 128) launch_t<128, 128, 2, 2, 2, kEpiStore>(p, ny, st);
+  else launch_t<128, 256, 2, 2, 2, kEpiStore>(p, ny, st);
+  return hipGetLastError();
+}
+
+}  // namespace hna
