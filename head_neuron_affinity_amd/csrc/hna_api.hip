@@ -184,7 +184,8 @@ int hna_fold_up_weights(const hna_dims* dm, const void* W_o, const float* gamma,
     return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need_ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int Hd = dm->H * dm->d;
-  hipError_t e = launch_scale_transpose(W_o, gamma, workspace, dm->hidden, Hd, dm->dtype, st);
+  hipError_t e = launch_scale_transpose(W_o, gamma, workspace, dm->hidden, Hd, dm->hidden,
+                                        dm->dtype, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   GemmParams p{};
   p.X = workspace;
@@ -200,11 +201,8 @@ int hna_fold_up_weights(const hna_dims* dm, const void* W_o, const float* gamma,
   p.d = dm->d;
   p.KB = p.N / 32;
   p.S = dm->d / 16;
-  if (dm->dtype == HNA_BF16) {
-    return finish(launch_mm_bf16(p, kEpiFold, 2, st), st, fn);
-  }
-  dim3 grid((p.N + 127) / 128, (Hd + 127) / 128, 2);
-  return finish(launch_gemm(p, dm->dtype, kEpiFold, grid, st), st, fn);
+  e = dm->dtype == HNA_BF16 ? launch_mm_bf16(p, kEpiFold, 2, st) : launch_gemm_f32(p, kEpiFold, 2, st);
+  return finish(e, st, fn);
 }
 
 int hna_down_col_sqnorm(const hna_dims* dm, const void* W_down, float* wd_sq, void* stream) {
@@ -473,7 +471,8 @@ int hna_down_weight_norms(const hna_down_dims* dm, const void* W_q, const void* 
   if (workspace_bytes < need)
     return fail(HNA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_scale_transpose(W_down, gamma_next, workspace, dm->hidden, dm->I, dm->dtype, st);
+  hipError_t e = launch_scale_transpose(W_down, gamma_next, workspace, dm->hidden, dm->I,
+                                        dm->hidden, dm->dtype, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   float* seg_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + down_ws_transposed(dm));
   GemmParams p{};
@@ -492,12 +491,9 @@ int hna_down_weight_norms(const hna_down_dims* dm, const void* W_q, const void* 
   p.G_next = dm->G;
   p.d_next = dm->d;
   const int nseg = dm->H + 2 * dm->G;
-  if (dm->dtype == HNA_BF16) {
-    // segments of W_q (one per query head), then of W_k and W_v (one per group)
-    e = launch_mm_bf16(p, kEpiSegSq, nseg, st);
-  } else {
-    e = launch_gemm(p, dm->dtype, kEpiSegSq, dim3((dm->I + 127) / 128, nseg, 1), st);
-  }
+  // segments of W_q (one per query head), then of W_k and W_v (one per group)
+  e = dm->dtype == HNA_BF16 ? launch_mm_bf16(p, kEpiSegSq, nseg, st)
+                            : launch_gemm_f32(p, kEpiSegSq, nseg, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   // segments of group g': its query heads (ascending), then its k rows, then its v rows
   int16_t seg_list[3 * kMaxHeads];
@@ -606,35 +602,37 @@ int hna_neuron_step(int32_t N, int32_t G, int32_t I, int32_t L, const float* S_u
 namespace {
 
 struct LooWorkspace {
-  size_t xx, xl, ZA, U, Q, coef, R, Rs, Y, t1, t1r, gram_part, gram, t3, t3_part, blas, total;
+  size_t xx, xl, xT, WoT, Z, ZAT, U, Q, coef, R, Rs, Y, t1, t1r, gram_part, gram, t3, t3_part,
+      total;
   int n_tc;
 };
-constexpr size_t kBlasWorkspace = 64u << 20;   // handed to rocBLAS for its GEMMs
 LooWorkspace loo_workspace(const hna_dims* dm) {
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
   const size_t es = esize_of(dm->dtype);
-  const size_t thd = (size_t)dm->T * dm->H * dm->d;
+  const size_t HD = (size_t)dm->H * dm->d, D = (size_t)dm->hidden;
+  const size_t thd = (size_t)dm->T * HD;
+  const size_t tp = (size_t)loo_tokens_padded(dm->T);
   LooWorkspace w;
   w.n_tc = t1_chunks(dm->T);
   size_t o = 0;
   w.xx = o;        o += align256((size_t)dm->T * sizeof(float));
-  w.xl = o;        o += dm->dtype == HNA_BF16 ? align256((size_t)dm->T * dm->hidden * 2) : 0;
-  w.ZA = o;        o += align256(thd * es);   // x W_o, then a scaled by alpha beta
+  w.xl = o;        o += dm->dtype == HNA_BF16 ? align256((size_t)dm->T * D * 2) : 0;
+  w.xT = o;        o += align256(D * tp * es);      // x^T, padded tokens
+  w.WoT = o;       o += align256(HD * D * es);      // W_o^T
+  w.Z = o;         o += align256(thd * es);         // x W_o (then a scaled, unfused path)
+  w.ZAT = o;       o += align256(HD * tp * es);     // (alpha beta / r) a, transposed
   w.U = o;         o += loo_coef_fused(dm->d, dm->dtype) ? 0 : align256(thd * es);
-  w.Q = o;         o += align256((size_t)dm->H * dm->d * dm->d * es);
+  w.Q = o;         o += align256(HD * dm->d * es);
   w.coef = o;      o += align256((size_t)dm->T * dm->H * 2 * sizeof(float));
-  const int64_t r_split = loo_r_split(dm->T);
-  const int r_parts = (int)r_split + (dm->T % r_split ? 1 : 0);
-  w.R = o;         o += align256((size_t)r_parts * dm->H * dm->d * dm->hidden * sizeof(float));
-  w.Rs = o;        o += align256((size_t)dm->H * dm->d * dm->hidden * es);
-  w.Y = o;         o += align256((size_t)2 * dm->H * dm->d * dm->I * sizeof(float));
+  w.R = o;         o += align256((size_t)loo_r_parts(dm->T) * HD * D * sizeof(float));
+  w.Rs = o;        o += align256(HD * D * es);
+  w.Y = o;         o += align256((size_t)2 * HD * dm->I * sizeof(float));
   w.t1 = o;        o += align256((size_t)w.n_tc * dm->H * dm->I * sizeof(float));
   w.t1r = o;       o += align256((size_t)dm->H * dm->I * sizeof(double));
   w.gram_part = o; o += geo.gram_part_bytes;
   w.gram = o;      o += geo.gram_bytes;
   w.t3 = o;        o += geo.add_bytes;
   w.t3_part = o;   o += geo.add_part_bytes;
-  w.blas = o;      o += kBlasWorkspace;
   w.total = o;
   return w;
 }
@@ -733,8 +731,12 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   if (rc) return rc;
   rc = check_map(fn, group_of_head, dm->H, dm->G);
   if (rc) return rc;
-  if ((int64_t)dm->T > INT32_MAX)
-    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld exceeds 2^31 - 1", fn, (long long)dm->T);
+  // the token GEMM reads 256-row tiles of the transposed operands (rows of
+  // T padded tokens) through 32-bit buffer offsets
+  constexpr int64_t kLooMaxTokens = 4000000;
+  if ((int64_t)dm->T > kLooMaxTokens)
+    return fail(HNA_ERR_UNSUPPORTED, "%s: T=%lld exceeds %lld tokens per call", fn,
+                (long long)dm->T, (long long)kLooMaxTokens);
   REQUIRE_PTR(M);
   REQUIRE_PTR(S_loo);
   REQUIRE_PTR(workspace);
@@ -756,7 +758,10 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   char* ws = static_cast<char*>(workspace);
   float* xx = reinterpret_cast<float*>(ws + wl.xx);
   void* xl = ws + wl.xl;
-  void* ZA = ws + wl.ZA;
+  void* xT = ws + wl.xT;
+  void* WoT = ws + wl.WoT;
+  void* Z = ws + wl.Z;
+  void* ZAT = ws + wl.ZAT;
   void* U = ws + wl.U;
   void* Q = ws + wl.Q;
   float2* coef = reinterpret_cast<float2*>(ws + wl.coef);
@@ -764,9 +769,9 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   float* R = reinterpret_cast<float*>(ws + wl.R);
   void* Rs = ws + wl.Rs;
   float* t1 = reinterpret_cast<float*>(ws + wl.t1);
-  void* bws = ws + wl.blas;
   const UpGeometry geo = up_geometry(dm->T, dm->H, dm->G, dm->d, dm->I, dm->dtype);
   const int HD = dm->H * dm->d, dt = dm->dtype, T = (int)dm->T, d = dm->d, D = dm->hidden;
+  const int Tp = (int)loo_tokens_padded(dm->T);
   const bool bf = dt == HNA_BF16;
 
   // heads in KV-group order (shared by the quadratic forms and the combine)
@@ -783,54 +788,70 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
   }
   qp.group_start[dm->G] = cp.group_start[dm->G] = (int16_t)n;
 
+  // C[m, n] = sum_k X[m, k] Yo[n, k], stored at C + n * ldc + m, over ny batch
+  // entries (X, Yo, C advance by bx, by, bc) or K chunks of k_split; C in the
+  // input dtype or fp32
+  auto gemm = [&](const void* X, int ldx, const void* Yo, int ldy, int Mr, int N, int K, void* C,
+                  int ldc, bool c_in_dtype, int ny, int64_t bx, int64_t by, int64_t bc,
+                  int k_split) {
+    GemmParams p{};
+    p.X = X;
+    p.Y[0] = Yo;
+    p.ldx = ldx;
+    p.ldy = ldy;
+    p.Mrows = Mr;
+    p.N = N;
+    p.Nvalid = N;
+    p.K = K;
+    p.C = C;
+    p.ldc = ldc;
+    p.bx = bx;
+    p.by = by;
+    p.bc = bc;
+    p.k_split = k_split;
+    p.out_bf16 = bf && c_in_dtype;
+    return bf ? launch_mm_bf16(p, kEpiStore, ny, st) : launch_gemm_f32(p, kEpiStore, ny, st);
+  };
+
   hipError_t e;
-  int bs = 0;
   if (dm->T > 0) {
-    // 1. |x|^2 (and x in bf16 for the GEMM); the moments x . o_h and |o_h|^2
-    //    through Z = x W_o, Q_h = W_o^(h)T W_o^(h), U_h = Q_h a_h (column-major
-    //    views: W_o is HD x hidden, x is hidden x T, a and Z and U are HD x T)
+    // 1. |x|^2 (and x in bf16); the transposed operands W_o^T [HD][hidden] and
+    //    x^T [hidden][Tp]; the moments x . o_h and |o_h|^2 through Z = x W_o
+    //    [T][HD], Q_h = W_o^(h)T W_o^(h) [d][d] and U_h = a_h Q_h [T][HD]
     if ((e = launch_x_prep(x, dm->T, D, xx, bf ? xl : nullptr, st)) != hipSuccess)
       return hip_fail(e, fn);
     const void* xg = bf ? xl : static_cast<const void*>(x);
     const bool fused = loo_coef_fused(d, dt);
-    if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, false, HD, T, D, W_o, dt, HD, 0, xg, dt, D,
-                        0, ZA, dt, HD, 0, 1)) != 0 ||
-        (bs = blas_gemm(st, bws, kBlasWorkspace, false, true, d, d, D, W_o, dt, HD, d, W_o, dt, HD,
-                        d, Q, dt, d, (int64_t)d * d, dm->H)) != 0 ||
-        (!fused && (bs = blas_gemm(st, bws, kBlasWorkspace, false, false, d, T, d, Q, dt, d,
-                                   (int64_t)d * d, a, dt, HD, d, U, dt, HD, d, dm->H)) != 0))
-      return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
+    if ((e = launch_scale_transpose(W_o, nullptr, WoT, D, HD, D, dt, st)) != hipSuccess ||
+        (e = launch_scale_transpose(xg, nullptr, xT, T, D, Tp, dt, st)) != hipSuccess ||
+        (e = gemm(WoT, D, xg, D, HD, T, D, Z, HD, true, 1, 0, 0, 0, 0)) != hipSuccess ||
+        (e = gemm(WoT, D, WoT, D, d, d, D, Q, d, true, dm->H, (int64_t)d * D, (int64_t)d * D,
+                  (int64_t)d * d, 0)) != hipSuccess ||
+        (!fused && (e = gemm(Q, d, a, HD, d, T, d, U, HD, true, dm->H, (int64_t)d * d, d, d,
+                             0)) != hipSuccess))
+      return hip_fail(e, fn);
     // 2. T2: Y^g = (alpha beta a)^T g and Y^u likewise.  With g_t = W_g (gamma x_t) / r_t,
     //    Y^g = R diag(gamma) W_g^T where R = ((alpha beta / r) a)^T x: the scaled
-    //    head outputs are written over Z, R is one GEMM over the tokens
-    //    (HD x hidden), and Y^g, Y^u are two GEMMs over hidden
+    //    head outputs, transposed (ZAT), and x^T make R one GEMM over the tokens
+    //    (HD x hidden, in K chunks), and Y^g, Y^u are two GEMMs over hidden
     if (fused) {
-      if ((e = launch_loo_coef_fused(a, ZA, Q, xx, dm->T, dm->H, d, D, coef, st)) != hipSuccess)
+      if ((e = launch_loo_coef_fused(a, Z, ZAT, Q, xx, dm->T, dm->H, d, D, coef, st)) != hipSuccess)
         return hip_fail(e, fn);
-    } else if ((e = launch_loo_coef(a, ZA, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess ||
-               (e = launch_scale_a(a, coef, xx, dm->T, dm->H, d, D, ZA, dt, st)) != hipSuccess) {
+    } else if ((e = launch_loo_coef(a, Z, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess ||
+               (e = launch_scale_a(a, coef, xx, dm->T, dm->H, d, D, Z, dt, st)) != hipSuccess ||
+               (e = launch_scale_transpose(Z, nullptr, ZAT, T, HD, Tp, dt, st)) != hipSuccess) {
       return hip_fail(e, fn);
     }
-    // R in token chunks (strided batch), the remainder as one more part
-    const int rs = loo_r_split(dm->T);
-    const int tk = T / rs, rem = T - rs * tk;
-    const int64_t hdD = (int64_t)HD * D;
-    const size_t esz = esize_of(dt);
-    if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, D, tk, ZA, dt, HD,
-                        (int64_t)tk * HD, xg, dt, D, (int64_t)tk * D, R, 0, HD, hdD, rs)) != 0 ||
-        (rem > 0 &&
-         (bs = blas_gemm(st, bws, kBlasWorkspace, false, true, HD, D, rem,
-                         static_cast<const char*>(ZA) + (size_t)rs * tk * HD * esz, dt, HD, 0,
-                         static_cast<const char*>(xg) + (size_t)rs * tk * D * esz, dt, D, 0,
-                         R + rs * hdD, 0, HD, 0, 1)) != 0))
-      return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
-    if ((e = launch_scale_cols(R, rs + (rem > 0 ? 1 : 0), gamma, HD, D, Rs, dt, st)) != hipSuccess)
+    const int r_parts = loo_r_parts(dm->T);
+    if ((e = gemm(xT, Tp, ZAT, Tp, D, HD, Tp, R, D, false, r_parts, 0, 0, (int64_t)HD * D,
+                  loo_r_chunk(dm->T))) != hipSuccess ||
+        (e = launch_scale_cols(R, r_parts, gamma, HD, D, Rs, dt, st)) != hipSuccess)
       return hip_fail(e, fn);
+    // Y^g [I][HD] = W_g Rs^T: row k is sum_c W_g[k][c] Rs[j][c]
     for (int gu = 0; gu < 2; ++gu)
-      if ((bs = blas_gemm(st, bws, kBlasWorkspace, false, false, HD, dm->I, D, Rs, dt, HD, 0,
-                          gu ? W_up : W_gate, dt, D, 0, Y + (int64_t)gu * HD * dm->I, 0, HD, 0,
-                          1)) != 0)
-        return fail(HNA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", fn, bs);
+      if ((e = gemm(Rs, D, gu ? W_up : W_gate, D, HD, dm->I, D, Y + (int64_t)gu * HD * dm->I, HD,
+                    false, 1, 0, 0, 0, 0)) != hipSuccess)
+        return hip_fail(e, fn);
     // 3. T1
     if ((e = launch_t1(g, u, coef, dm->T, dm->H, dm->I, t1, dm->dtype, st)) != hipSuccess ||
         (e = launch_t1_reduce(t1, wl.n_tc, (int64_t)dm->H * dm->I,

@@ -185,13 +185,12 @@ struct HeadStepParams {
 };
 hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st);
 
-// ------------------------------------------------------ scaled NT GEMM (MFMA)
-// C[m, n] = sum_c Xs[m, c] * Y[n, c]; Xs [Mrows, K] and Y [N, K] row-major with
-// c contiguous.  launch_scale_transpose makes Xs[m, c] = s[c] * X[c, m] from a
-// row-major X [K, Mrows].  Epilogues: write the folded layout, or sum C^2 over
-// the n of a segment.
-// The plain store writes C[m, n] (fp32 or the input dtype) at C + m * ldc + n,
-// or at C + n * ldc + m when transposed.
+// --------------------------------------------------------- NT GEMM (MFMA)
+// C[m, n] = sum_c X[m, c] * Y[n, c]; X [Mrows, K] and Y [N, K] row-major with
+// c contiguous.  launch_scale_transpose makes X[m, c] = s[c] * W[c, m] from a
+// row-major W [K, Mrows].  Epilogues: write the folded layout, sum C^2 over
+// the n of a segment, or store C[m, n] (fp32, or bf16 from the bf16 kernel)
+// at C + n * ldc + m (C transposed: m contiguous, ldc and m0 multiples of 4).
 enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1, kEpiStore = 2 };
 
 struct GemmParams {
@@ -212,7 +211,6 @@ struct GemmParams {
   void* C;
   int64_t ldc, bx, by, bc;
   int k_split;
-  int trans;           // store C transposed
   int out_bf16;        // store in bf16 (fp32 otherwise)
 };
 // The bf16 GEMM (k_mm.hip): grid y runs over gate / up (fold, ny = 2), the
@@ -239,35 +237,36 @@ hipError_t launch_x_prep(const float* x, int64_t T, int D, float* xx, void* xl, 
 hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const float* xx, int64_t T,
                            int H, int d, int D, float2* coef, int dtype, hipStream_t st);
 // bf16 with d a multiple of 32 up to 128: the moments (|o_h|^2 on the matrix
-// cores from Q_h = W_o^(h)T W_o^(h)), alpha and beta, and alpha beta a written
-// over Z (ZA holds Z = x W_o on entry), in one kernel
+// cores from Q_h = W_o^(h)T W_o^(h)), alpha and beta, and (alpha beta / r) a
+// written transposed, ZAT [H d][Tp] (Z = x W_o is read), in one kernel
 bool loo_coef_fused(int d, int dtype);
-hipError_t launch_loo_coef_fused(const void* a, void* ZA, const void* Q, const float* xx, int64_t T,
-                                 int H, int d, int D, float2* coef, hipStream_t st);
+hipError_t launch_loo_coef_fused(const void* a, const void* Z, void* ZAT, const void* Q,
+                                 const float* xx, int64_t T, int H, int d, int D, float2* coef,
+                                 hipStream_t st);
 hipError_t launch_scale_a(const void* a, const float2* coef, const float* xx, int64_t T, int H,
                           int d, int D, void* As, int dtype, hipStream_t st);
-// R = ((alpha beta / r) a)^T x over the tokens is split into this many equal
-// token chunks (a batched GEMM, so that its few output tiles still fill the
-// chip), plus one part for the remainder when T is not a multiple
-int loo_r_split(int64_t T);
+// Tokens padded to a multiple of 8 (the K length of the token GEMM)
+int64_t loo_tokens_padded(int64_t T);
+// R = ((alpha beta / r) a)^T x over the tokens runs in K chunks of this many
+// padded tokens (a multiple of 64), one fp32 part per chunk, so that its few
+// output tiles still fill the chip
+int loo_r_chunk(int64_t T);
+int loo_r_parts(int64_t T);
 // Rs = (sum of `parts` parts of R) diag(gamma) in the input dtype, each part
-// column-major [HD x D] fp32
+// row-major [HD][D] fp32
 hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int HD, int D,
                              void* Rs, int dtype, hipStream_t st);
 int t1_chunks(int64_t T);
 hipError_t launch_t1(const void* g, const void* u, const float2* coef, int64_t T, int H, int I,
                      float* t1, int dtype, hipStream_t st);
 hipError_t launch_loo_combine(const LooCombineParams& p, int dtype, hipStream_t st);
-// C = op(A) op(B) per batch entry, column-major, fp32 accumulation, by rocBLAS;
-// types 0 = fp32, 1 = bf16.  Returns the rocBLAS status (0 = success, -1 = no
-// device).
-int blas_gemm(hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb, int m, int n, int k,
-              const void* A, int at, int lda, int64_t sa, const void* B, int bt, int ldb,
-              int64_t sb, void* C, int ct, int ldc, int64_t sc, int batch);
-
-hipError_t launch_scale_transpose(const void* X, const float* s, void* Xs, int K, int Mrows,
-                                  int dtype, hipStream_t st);
-hipError_t launch_gemm(const GemmParams& p, int dtype, int epilogue, dim3 grid,
-                       hipStream_t st);
+// out[c, r] = s[r] in[r, c] (s null: no scaling) for in [rows, cols]
+// row-major; out rows have length ldo >= rows (ldo a multiple of 8), the
+// entries past rows are written as zeros
+hipError_t launch_scale_transpose(const void* in, const float* s, void* out, int rows, int cols,
+                                  int ldo, int dtype, hipStream_t st);
+// The fp32 GEMM (k_gemm.hip): ny = gate / up (fold), segments (segment square)
+// or batches / K chunks (store); K and k_split multiples of 4
+hipError_t launch_gemm_f32(const GemmParams& p, int epilogue, int ny, hipStream_t st);
 
 }  // namespace hna

@@ -13,20 +13,21 @@
 //        g_t = W_g (gamma * x_t) / r_t exactly (g is the pre-activation of x), so
 //        Y^g_h = R_h diag(gamma) W_g^T with R_h = sum_t (alpha beta / r_t) a_th x_t^T:
 //        one token GEMM of width hidden shared by gate and up, then two small
-//        weight GEMMs (rocBLAS), instead of two token GEMMs of width I
+//        weight GEMMs, instead of two token GEMMs of width I
 //   T3 = m^T C_h m,  C_h = sum_t beta_th^2 a_th a_th^T   (the Gram and quadratic-
 //        form kernels of the ADD score, weighted per token and head)
 // r_h^2 = (|x|^2 - 2 x . o_h + |o_h|^2) / hidden needs |x|^2 (x_prep_kernel)
 // and two moments per (token, head): x . o_h = (x W_o)_h . a_h and
 // |o_h|^2 = a_h . (Q_h a_h) with Q_h = W_o^(h)T W_o^(h), from three more plain
-// GEMMs (x W_o, the Q_h, Q_h a_h; rocBLAS) and the dots in loo_coef_kernel.  All
+// GEMMs (x W_o, the Q_h, Q_h a_h) and the dots in loo_coef_kernel.  Every GEMM
+// runs on this library's own MFMA kernels (k_mm.hip for bf16, k_gemm.hip for
+// fp32), which take both operands k-contiguous: the token product R reads
+// transposed copies of x and of the scaled a, padded to a multiple of 8
+// tokens with zeros.  All
 // three terms are non-cancelling in practice (T3 dominates; T2 is a fraction of
 // it), so rounding a * alpha beta / r and R_h diag(gamma) to bf16 for the GEMMs
 // costs far less than the bf16 tolerance.
-#include <rocblas/rocblas.h>
-
 #include <cmath>
-#include <mutex>
 
 #include "hna_internal.h"
 
@@ -179,16 +180,18 @@ __device__ inline float bf16_at(const uint4& v, int e) {
 // 32 (mt / 2) + 8 (m / 4) + 4 (mt % 2) + m % 4, which puts every entry of V
 // that a lane receives on a feature whose a value the lane already holds.
 // x . o_h = Z . a is dotted over the same features; two exchanges across the
-// wave's quarters complete both sums.  Z is overwritten, in place, by
-// (alpha beta / r) a (rounded to bf16).
+// wave's quarters complete both sums.
+// (alpha beta / r) a, rounded to bf16, is written transposed: ZAT[h d + j][t]
+// for t < Tp (zeros for the padding tokens T .. Tp - 1).
 constexpr int kCoefBlocksPerHead = 128;
 
 template <int ND>
 __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __restrict__ a,
-                                                            __bf16* ZA,
+                                                            const __bf16* __restrict__ Z,
+                                                            __bf16* __restrict__ ZAT,
                                                             const __bf16* __restrict__ Q,
                                                             const float* __restrict__ xx,
-                                                            int64_t T, int H, int D,
+                                                            int64_t T, int64_t Tp, int H, int D,
                                                             float2* __restrict__ coef) {
   constexpr int d = 32 * ND, QS = d + 8;  // LDS row stride, elements
   __shared__ __attribute__((aligned(16))) uint16_t qs[d * QS];
@@ -201,7 +204,8 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
   __syncthreads();
   const int lane = threadIdx.x & 63, qq = lane >> 4, tl = lane & 15;
   const uint16_t* ap = reinterpret_cast<const uint16_t*>(a);
-  uint16_t* zp = reinterpret_cast<uint16_t*>(ZA);
+  const uint16_t* zp = reinterpret_cast<const uint16_t*>(Z);
+  uint16_t* ztp = reinterpret_cast<uint16_t*>(ZAT) + (int64_t)h * d * Tp;
   const int64_t n_tiles = (T + 15) / 16;
   const int64_t step = (int64_t)gridDim.x * 4;
   int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -224,7 +228,6 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
     if (tile + step < n_tiles) fetch(tile + step);  // the next tile loads under this one's work
     const int64_t t = tile * 16 + tl;
     const bool ok = t < T;
-    const int64_t base = ((ok ? t : 0) * H + h) * d + 8 * qq;
     // re-read the Q_h fragments from LDS on every tile rather than holding all
     // of them in registers across the loop (an opaque offset stops the hoist)
     int qoff = (8 * (tl >> 2) + (tl & 3)) * QS + 8 * qq;
@@ -252,48 +255,53 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
     oo += __shfl_xor(oo, 16);
     xo += __shfl_xor(xo, 32);
     oo += __shfl_xor(oo, 32);
-    if (!ok) continue;
-    const double x2 = (double)xx[t];
-    const double den = x2 - 2.0 * (double)xo + (double)oo;
-    float2 c = make_float2(0.f, 0.f);
-    if (den > 0.0 && x2 > 0.0) {
-      c.x = (float)(1.0 - sqrt(x2 / den));
-      c.y = (float)sqrt((double)D / den);
+    float w = 0.f;
+    if (ok) {
+      const double x2 = (double)xx[t];
+      const double den = x2 - 2.0 * (double)xo + (double)oo;
+      float2 c = make_float2(0.f, 0.f);
+      if (den > 0.0 && x2 > 0.0) {
+        c.x = (float)(1.0 - sqrt(x2 / den));
+        c.y = (float)sqrt((double)D / den);
+      }
+      if (qq == 0) coef[t * H + h] = c;
+      w = c.x * c.y * inv_rms((float)x2, D);
     }
-    if (qq == 0) coef[t * H + h] = c;
-    const float w = c.x * c.y * inv_rms((float)x2, D);
+    if (t >= Tp) continue;
+    // feature 32 ks + 8 qq + e of token t; the 16 lanes of a quarter write 16
+    // consecutive tokens of one row
 #pragma unroll
-    for (int ks = 0; ks < ND; ++ks) {
-      const uint4 v = a_cur[ks];
-      *reinterpret_cast<uint4*>(zp + base + 32 * ks) =
-          make_uint4(pack_bf16x2(bf16_at(v, 0) * w, bf16_at(v, 1) * w),
-                     pack_bf16x2(bf16_at(v, 2) * w, bf16_at(v, 3) * w),
-                     pack_bf16x2(bf16_at(v, 4) * w, bf16_at(v, 5) * w),
-                     pack_bf16x2(bf16_at(v, 6) * w, bf16_at(v, 7) * w));
-    }
+    for (int ks = 0; ks < ND; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        ztp[(int64_t)(32 * ks + 8 * qq + e) * Tp + t] =
+            (uint16_t)f32_to_bf16_bits(bf16_at(a_cur[ks], e) * w);
   }
 }
 
 // Rs = (sum of the token-chunk parts of R) diag(gamma) in the input dtype: each
-// part is column-major [HD x hidden] fp32 (column c, the hidden index, is
-// scaled by gamma[c]); the parts are added in order; 4 entries per thread
+// part is row-major [HD][hidden] fp32 (column c, the hidden index, is scaled by
+// gamma[c]); the parts are added in order; 4 entries per thread
 template <typename E>
 __global__ __launch_bounds__(256) void scale_cols_kernel(const float* __restrict__ R, int parts,
-                                                         const float* __restrict__ gamma, int HD,
+                                                         const float* __restrict__ gamma, int D,
                                                          int64_t n, E* __restrict__ Rs) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;   // n and HD are multiples of 16
+  if (i >= n) return;   // n and D are multiples of 8
   float4 v = *reinterpret_cast<const float4*>(R + i);
   for (int q = 1; q < parts; ++q) {
     const float4 w = *reinterpret_cast<const float4*>(R + (int64_t)q * n + i);
     v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
   }
-  const float gm = gamma[i / HD];
+  const int c = (int)(i % D);
+  v.x *= gamma[c];
+  v.y *= gamma[c + 1];
+  v.z *= gamma[c + 2];
+  v.w *= gamma[c + 3];
   if constexpr (sizeof(E) == 2) {
-    *reinterpret_cast<uint2*>(Rs + i) = make_uint2(pack_bf16x2(v.x * gm, v.y * gm),
-                                                   pack_bf16x2(v.z * gm, v.w * gm));
+    *reinterpret_cast<uint2*>(Rs + i) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
   } else {
-    *reinterpret_cast<float4*>(Rs + i) = make_float4(v.x * gm, v.y * gm, v.z * gm, v.w * gm);
+    *reinterpret_cast<float4*>(Rs + i) = v;
   }
 }
 
@@ -512,9 +520,19 @@ hipError_t launch_scale_a(const void* a, const float2* coef, const float* xx, in
   return hipGetLastError();
 }
 
-int loo_r_split(int64_t T) {
-  const int64_t s = T / 4096;
-  return (int)(s < 1 ? 1 : (s > 8 ? 8 : s));
+int64_t loo_tokens_padded(int64_t T) { return (T + 7) / 8 * 8; }
+
+int loo_r_chunk(int64_t T) {
+  const int64_t tp = loo_tokens_padded(T);
+  int64_t s = T / 4096;
+  s = s < 1 ? 1 : (s > 8 ? 8 : s);
+  const int64_t kc = ((tp + s - 1) / s + 63) / 64 * 64;
+  return (int)(kc < 64 ? 64 : kc);
+}
+
+int loo_r_parts(int64_t T) {
+  const int64_t tp = loo_tokens_padded(T), kc = loo_r_chunk(T);
+  return (int)((tp + kc - 1) / kc);
 }
 
 hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int HD, int D,
@@ -523,30 +541,33 @@ hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int 
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n / 4 + 255) / 256));
   if (dtype == 1)
-    hipLaunchKernelGGL(scale_cols_kernel<__bf16>, grid, dim3(256), 0, st, R, parts, gamma, HD, n,
+    hipLaunchKernelGGL(scale_cols_kernel<__bf16>, grid, dim3(256), 0, st, R, parts, gamma, D, n,
                        static_cast<__bf16*>(Rs));
   else
-    hipLaunchKernelGGL(scale_cols_kernel<float>, grid, dim3(256), 0, st, R, parts, gamma, HD, n,
+    hipLaunchKernelGGL(scale_cols_kernel<float>, grid, dim3(256), 0, st, R, parts, gamma, D, n,
                        static_cast<float*>(Rs));
   return hipGetLastError();
 }
 
 bool loo_coef_fused(int d, int dtype) { return dtype == 1 && d % 32 == 0 && d >= 32 && d <= 128; }
 
-hipError_t launch_loo_coef_fused(const void* a, void* ZA, const void* Q, const float* xx, int64_t T,
-                                 int H, int d, int D, float2* coef, hipStream_t st) {
+hipError_t launch_loo_coef_fused(const void* a, const void* Z, void* ZAT, const void* Q,
+                                 const float* xx, int64_t T, int H, int d, int D, float2* coef,
+                                 hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int64_t n_tiles = (T + 15) / 16;
   const int64_t bx = (n_tiles + 3) / 4;
+  const int64_t Tp = loo_tokens_padded(T);
   const dim3 grid((unsigned)(bx < kCoefBlocksPerHead ? bx : kCoefBlocksPerHead), (unsigned)H);
   const auto* ab = static_cast<const __bf16*>(a);
-  auto* zb = static_cast<__bf16*>(ZA);
+  const auto* zb = static_cast<const __bf16*>(Z);
+  auto* zt = static_cast<__bf16*>(ZAT);
   const auto* qb = static_cast<const __bf16*>(Q);
   switch (d / 32) {
-    case 1: hipLaunchKernelGGL(loo_coef_mfma_kernel<1>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
-    case 2: hipLaunchKernelGGL(loo_coef_mfma_kernel<2>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
-    case 3: hipLaunchKernelGGL(loo_coef_mfma_kernel<3>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
-    case 4: hipLaunchKernelGGL(loo_coef_mfma_kernel<4>, grid, dim3(256), 0, st, ab, zb, qb, xx, T, H, D, coef); break;
+    case 1: hipLaunchKernelGGL(loo_coef_mfma_kernel<1>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 2: hipLaunchKernelGGL(loo_coef_mfma_kernel<2>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 3: hipLaunchKernelGGL(loo_coef_mfma_kernel<3>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 4: hipLaunchKernelGGL(loo_coef_mfma_kernel<4>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -586,42 +607,6 @@ hipError_t launch_loo_combine(const LooCombineParams& p, int dtype, hipStream_t 
   if (dtype == 1) hipLaunchKernelGGL(loo_combine_kernel<__bf16>, grid, dim3(64), 0, st, p);
   else hipLaunchKernelGGL(loo_combine_kernel<float>, grid, dim3(64), 0, st, p);
   return hipGetLastError();
-}
-
-// ---- plain GEMMs by rocBLAS (column-major, fp32 accumulation); one handle per
-// device, created at the first call, used under a lock so that concurrent
-// callers do not share its stream and workspace settings
-namespace {
-std::mutex g_blas_mu;
-rocblas_handle g_blas[64] = {};
-rocblas_datatype blas_type(int t) { return t == 1 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r; }
-}  // namespace
-
-int blas_gemm(hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb, int m, int n, int k,
-              const void* A, int at, int lda, int64_t sa, const void* B, int bt, int ldb,
-              int64_t sb, void* C, int ct, int ldc, int64_t sc, int batch) {
-  if (m == 0 || n == 0 || batch == 0) return 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  std::lock_guard<std::mutex> lock(g_blas_mu);
-  if (!g_blas[dev]) {
-    const rocblas_status cs = rocblas_create_handle(&g_blas[dev]);
-    if (cs != rocblas_status_success) {
-      g_blas[dev] = nullptr;
-      return (int)cs;
-    }
-  }
-  rocblas_handle hb = g_blas[dev];
-  rocblas_status bs = rocblas_set_stream(hb, st);
-  if (bs == rocblas_status_success) bs = rocblas_set_workspace(hb, ws, ws_bytes);
-  const float one = 1.0f, zero = 0.0f;
-  if (bs == rocblas_status_success)
-    bs = rocblas_gemm_strided_batched_ex(
-        hb, ta ? rocblas_operation_transpose : rocblas_operation_none,
-        tb ? rocblas_operation_transpose : rocblas_operation_none, m, n, k, &one, A,
-        blas_type(at), lda, sa, B, blas_type(bt), ldb, sb, &zero, C, blas_type(ct), ldc, sc, C,
-        blas_type(ct), ldc, sc, batch, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return (int)bs;
 }
 
 }  // namespace hna

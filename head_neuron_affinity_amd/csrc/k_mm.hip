@@ -5,7 +5,8 @@
 //     written in the fragment order of the folded weights;
 //   * segment square (the down edge's ||b_gk||^2): C^2 summed over the rows n
 //     of one W_q / W_k / W_v segment, b never stored;
-//   * plain store, fp32 or bf16, C or its transpose, per batch or per K chunk.
+//   * plain store of C transposed (C[m, n] at n * ldc + m, m contiguous),
+//     fp32 or bf16, per batch entry or per K chunk.
 // Workgroup tile BM x BN x 64 on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
 // The fold runs 256 x 256 tiles on 8 waves (two per SIMD, so one wave's
@@ -29,6 +30,7 @@ namespace {
 using namespace hot;
 
 constexpr int BK = 64;                  // K per stage (one 128-byte LDS row)
+constexpr uint32_t kMaxResourceBytes = 0x7ffff000u;   // below the out-of-range offset
 
 
 // Asynchronous 16-byte buffer -> LDS copy with a scalar offset soff added to
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
     }
   }
   // resources over the rows from m0 / n0 on (rows past the end read zeros)
-  const uint32_t lim = 0x7ffff000u;
+  const uint32_t lim = kMaxResourceBytes;
   const int64_t xb = (int64_t)max(0, p.Mrows - m0) * p.ldx * 2;
   const int64_t yb = (int64_t)max(0, Nrows - n0) * p.ldy * 2;
   const uint32_t xbytes = xb > (int64_t)lim ? lim : (uint32_t)xb;
@@ -270,6 +272,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
       p.seg_part[(int64_t)z * p.Mrows + m0 + tid] = t;
     }
   } else {
+    // C[m, n] at n * ldc + m: a lane's 4 consecutive rows m (e = 0..3) are one
+    // 8-byte (bf16) or 16-byte (fp32) store
     char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -280,14 +284,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int mb = m0 + wm * WM + i * 32 + 8 * a + 4 * (l >> 5);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = mb + e;
-            if (m >= p.Mrows) continue;
-            const float v = acc[i][j][4 * a + e];
-            const int64_t o = p.trans ? (int64_t)n * p.ldc + m : (int64_t)m * p.ldc + n;
-            if (p.out_bf16) reinterpret_cast<uint16_t*>(Cb)[o] = (uint16_t)f32_to_bf16_bits(v);
-            else reinterpret_cast<float*>(Cb)[o] = v;
+          if (mb >= p.Mrows) continue;
+          const int64_t o = (int64_t)n * p.ldc + mb;
+          const float v0 = acc[i][j][4 * a], v1 = acc[i][j][4 * a + 1];
+          const float v2 = acc[i][j][4 * a + 2], v3 = acc[i][j][4 * a + 3];
+          if (mb + 4 <= p.Mrows) {
+            if (p.out_bf16)
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Cb) + o) =
+                  make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                             f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+            else
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Cb) + o) = make_float4(v0, v1, v2, v3);
+          } else {
+            const float v[4] = {v0, v1, v2, v3};
+            for (int e = 0; e < p.Mrows - mb; ++e) {
+              if (p.out_bf16) reinterpret_cast<uint16_t*>(Cb)[o + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+              else reinterpret_cast<float*>(Cb)[o + e] = v[e];
+            }
           }
         }
       }
@@ -295,22 +308,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
 }
 
 template <int BM, int BN, int WGM, int WGN, int NST, int EPI>
-void launch_t(const GemmParams& p, int ny, hipStream_t st) {
+hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
+  // a tile's rows must lie within the 32-bit range of its buffer resource
+  if ((int64_t)BM * p.ldx * 2 > kMaxResourceBytes || (int64_t)BN * p.ldy * 2 > kMaxResourceBytes)
+    return hipErrorInvalidValue;
   const int N = EPI == kEpiSegSq ? p.d_next : p.N;
   const int ntiles = ((p.Mrows + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid(8 * ((ntiles + 7) / 8), ny);
   hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, WGM, WGN, NST, EPI>), grid, dim3(64 * WGM * WGN), 0, st, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
-  if (epilogue == kEpiSegSq) launch_t<128, 128, 2, 2, 2, kEpiSegSq>(p, ny, st);
-  else if (epilogue == kEpiFold) launch_t<256, 256, 4, 2, 2, kEpiFold>(p, ny, st);
-  else if (p.N <= 128) launch_t<128, 128, 2, 2, 2, kEpiStore>(p, ny, st);
-  else launch_t<128, 256, 2, 2, 2, kEpiStore>(p, ny, st);
-  return hipGetLastError();
+  if (epilogue == kEpiSegSq) return launch_t<128, 128, 2, 2, 2, kEpiSegSq>(p, ny, st);
+  if (epilogue == kEpiFold) return launch_t<256, 256, 4, 2, 2, kEpiFold>(p, ny, st);
+  if (p.N == 0) return hipSuccess;
+  // 256 x 256 tiles when both sides fill them and there is a tile per CU
+  if (p.Mrows >= 256 && p.N >= 256 &&
+      (int64_t)((p.Mrows + 255) / 256) * ((p.N + 255) / 256) * ny >= 256)
+    return launch_t<256, 256, 4, 2, 2, kEpiStore>(p, ny, st);
+  return launch_t<128, 128, 2, 2, 2, kEpiStore>(p, ny, st);
 }
 
 }  // namespace hna

@@ -23,9 +23,9 @@
  *     they are float32.  gamma, gamma_next, r, r_next, wd_sq and every output
  *     are float32 in both cases.  Accumulation is float32.
  *   - Every tensor pointer is a device pointer owned by the caller; the
- *     library allocates no memory and keeps no state between calls (except
- *     the rocBLAS handle of hna_affinity_loo, see there).  Scratch space is
- *     the caller's workspace.  group maps are host arrays, read
+ *     library allocates no memory and keeps no state between calls (the
+ *     allocation-free entry point's static device array aside, see there).
+ *     Scratch space is the caller's workspace.  group maps are host arrays, read
  *     during the call only.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and runs asynchronously; nothing synchronises the host except
@@ -37,7 +37,7 @@
  *     Launch failures return HNA_ERR_HIP.  Nothing prints, aborts or throws.
  *   - Device pointers must be 16-byte aligned (HNA_ERR_ALIGNMENT otherwise).
  *   - The library is reentrant; its only global mutable state is the
- *     thread-local error text and hna_affinity_loo's rocBLAS handles.  Calls
+ *     thread-local error text (and that static array).  Calls
  *     that share a workspace or an output must be ordered on one stream by
  *     the caller.
  *
@@ -256,15 +256,11 @@ size_t hna_loo_workspace_bytes(const hna_dims* dims);
  *     given must be its pre-activations, g = W_gate (gamma * x / rms(x)))
  *   S_loo fp32 [G, I] output (written, also for T = 0: zeros)
  * A token whose residual vanishes without head h (r_h = 0) contributes
- * nothing for that head.  Limits: those of hna_affinity_up and T < 2^31.
- * Deterministic (fixed-order sums in the library's own kernels; the plain
- * GEMMs run through rocBLAS).
- * rocBLAS: this call runs four plain GEMMs (five for fp32 inputs or a head
- * dim that is not 32, 64, 96 or 128) through one rocBLAS handle per
- * device, created at the first call on that device and kept until the
- * process ends (calls are serialised on it); rocBLAS's workspace is a slice
- * of the caller's workspace.  This is the library's only state besides the
- * thread-local error text.
+ * nothing for that head.  Limits: those of hna_affinity_up and T <= 4,000,000
+ * per call (HNA_ERR_UNSUPPORTED above: the token GEMM addresses 256-row tiles
+ * of the transposed operands through 32-bit offsets).  Deterministic: every
+ * sum, the plain GEMMs included, runs in a fixed order in the library's own
+ * kernels (no BLAS library is used).
  */
 int hna_affinity_loo(const hna_dims* dims, const void* a, const void* g, const void* u,
                      const float* x, const void* W_o, const float* gamma, const void* W_gate,

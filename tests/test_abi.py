@@ -314,6 +314,7 @@ def test_loo_validates():
         return loo(ctypes.byref(d), a, F, F, x, F, gamma, Wg, Wu, M, g, 1.0, S, ws, wsb, None)
 
     assert call(d=dims(hna, d=20)) == -2            # head dim not a multiple of 16
+    assert call(d=dims(hna, T=4_000_001)) == -2     # past the token limit of one call
     assert call(M=None) == -1
     assert call(S=vp(MIS)) == -3
     assert call(wsb=need - 1) == -4

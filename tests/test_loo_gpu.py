@@ -61,11 +61,14 @@ def check(got, ref, tol, metric):
     (synth.LayerShape("mid-bf16", 2048, 256, 8, 4, 64, 384, "bf16", 0.5), BF16_TOL, "fro"),
     # head dim 32 and a token count off the 32-token tile
     (synth.LayerShape("d32-ragged-bf16", 999, 128, 4, 2, 32, 200, "bf16", 0.5), BF16_TOL, "fro"),
-    # token counts that split the cross term's token GEMM into equal chunks
-    # plus a one-token remainder part (2 x 4097 + 1 and 3 x 4096 + 1)
+    # token counts off the 8-token padding of the token GEMM's transposed
+    # operands and off its K chunks (2 and 3 chunks, the last one short)
     (synth.LayerShape("split-remainder-bf16", 8195, 128, 4, 2, 32, 200, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("split-remainder-fp32", 12289, 64, 4, 2, 16, 128, "f32", 0.5), FP32_TOL, "max"),
     (synth.LayerShape("d128-bf16", 512, 512, 16, 8, 128, 256, "bf16", 0.5), BF16_TOL, "fro"),
+    # fewer tokens than one 8-token pad group (one K step of 64, mostly zeros)
+    (synth.LayerShape("five-tokens-bf16", 5, 128, 4, 2, 32, 64, "bf16", 0.5), BF16_TOL, "fro"),
+    (synth.LayerShape("three-tokens-fp32", 3, 64, 4, 2, 16, 64, "f32", 0.5), FP32_TOL, "max"),
     # the Danube3-500M layer shape (head dim 96), fewer tokens and neurons
     (synth.LayerShape("danube-shape-bf16", 1024, 1536, 16, 8, 96, 512, "bf16", 0.5), BF16_TOL, "fro"),
 ])
