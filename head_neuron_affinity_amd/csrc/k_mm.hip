@@ -15,9 +15,9 @@
 // workgroups per CU.  Both operand tiles arrive in LDS by asynchronous
 // 16-byte buffer -> LDS copies into a ring of NST stages: the copies of K
 // step k + NST - 1 are issued before the MFMAs of step k.  LDS rows of 64
-// elements (128 bytes) hold their 16-byte chunks XOR-swizzled by the row's
-// low 3 bits, so a fragment read (32 rows, one chunk) touches each bank slot
-// once per 8 rows.  Rows past M or N and elements past K read zeros (buffer
+// elements (128 bytes) hold their 16-byte chunks XOR-swizzled by the row index,
+// so the 16 rows that a fragment read (32 rows, one chunk) serves at once hit
+// 16 distinct bank slots (no LDS bank conflicts, by the counters).  Rows past M or N and elements past K read zeros (buffer
 // range check, chunk masking); K must be a multiple of 8.  Workgroup ids map
 // tiles XCD by XCD, in groups of 4 tile rows, so the workgroups that share an
 // XCD's L2 at one time share operand panels.
@@ -29,7 +29,6 @@ namespace {
 
 using namespace hot;
 
-constexpr int BK = 64;                  // K per stage (one 128-byte LDS row)
 constexpr uint32_t kMaxResourceBytes = 0x7ffff000u;   // below the out-of-range offset
 
 
@@ -55,17 +54,43 @@ __device__ inline u32x4 uniform_rsrc(const void* base, uint32_t bytes) {
   return d;
 }
 
-template <int BM, int BN, int WGM, int WGN, int NST, int EPI>
+// XOR applied to the 16-byte chunk index in row r of a stage whose rows hold
+// CPR chunks: any 8 consecutive rows put one chunk column in 8 distinct
+// 16-byte slots of the 128-byte lines they span
+#ifndef MM_BIG
+#define MM_BIG 256, 256, 64, 4, 2, 2
+#endif
+#ifndef MM_SMALL
+#define MM_SMALL 128, 128, 64, 2, 2, 2
+#endif
+#ifndef MM_SEG
+#define MM_SEG 128, 128, 64, 2, 2, 2, kEpiSegSq
+#endif
+
+template <int CPR>
+__device__ inline int swz(int r) {
+  // 128-byte rows: a 64-bank LDS serves 16 lanes (16 rows) of a 16-byte read
+  // at once, so every 16 rows must also cover 16 distinct slots of the
+  // 256-byte lines they span
+  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+  return (r / (8 / CPR)) % CPR;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParams p) {
+  static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
   static_assert(NST >= 2 && NST <= 4, "two to four stages");
   constexpr int NW = WGM * WGN;               // waves, WGM x WGN
   constexpr int WM = BM / WGM, WN = BN / WGN; // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 tiles per wave
   constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * 128;           // bytes per stage
-  constexpr int NCP = ROWS / (8 * NW);        // copies per thread per stage
-  constexpr int NCX = BM / (8 * NW);          // of which X rows
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy rounds cover whole rows");
+  constexpr int ROWB = 2 * BK;                // bytes per LDS row
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows one wave's copy fills
+  constexpr int STAGE = ROWS * ROWB;          // bytes per stage
+  constexpr int NCP = ROWS / (RPI * NW);      // copies per thread per stage
+  constexpr int NCX = BM / (RPI * NW);        // of which X rows
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "copy rounds cover whole rows");
   static_assert(EPI != kEpiSegSq || (BN == 128 && BM <= 64 * NW), "a segment is one tile column");
 
   static_assert((NST - 2) * NCP <= 63, "copies in flight must fit the wait counter");
@@ -135,8 +160,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   int kc[NCP];   // element offset of the lane's chunk within the stage
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
-    const int r = 8 * (NW * i + w) + (l >> 3);
-    const int c = (l & 7) ^ (r & 7);
+    const int r = RPI * (NW * i + w) + l / CPR;
+    const int c = (l % CPR) ^ swz<CPR>(r);
     kc[i] = 8 * c;
     voff[i] = i < NCX ? (uint32_t)((int64_t)r * p.ldx * 2 + 16 * c)
                       : (uint32_t)((int64_t)(r - BM) * p.ldy * 2 + 16 * c);
@@ -181,12 +206,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WM + i * 32 + (l & 31);
-        fa[i][0] = *reinterpret_cast<const uint4*>(sb + r * 128 + ((col ^ (r & 7)) << 4));
+        fa[i][0] = *reinterpret_cast<const uint4*>(sb + r * ROWB + ((col ^ swz<CPR>(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = BM + wn * WN + j * 32 + (l & 31);
-        fb[j][0] = *reinterpret_cast<const uint4*>(sb + r * 128 + ((col ^ (r & 7)) << 4));
+        fb[j][0] = *reinterpret_cast<const uint4*>(sb + r * ROWB + ((col ^ swz<CPR>(r)) << 4));
       }
     };
 #pragma unroll
@@ -307,7 +332,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NST, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
 hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
   // a tile's rows must lie within the 32-bit range of its buffer resource
   if ((int64_t)BM * p.ldx * 2 > kMaxResourceBytes || (int64_t)BN * p.ldy * 2 > kMaxResourceBytes)
@@ -315,7 +340,7 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
   const int N = EPI == kEpiSegSq ? p.d_next : p.N;
   const int ntiles = ((p.Mrows + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid(8 * ((ntiles + 7) / 8), ny);
-  hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, WGM, WGN, NST, EPI>), grid, dim3(64 * WGM * WGN), 0, st, p);
+  hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, BK, WGM, WGN, NST, EPI>), grid, dim3(64 * WGM * WGN), 0, st, p);
   return hipGetLastError();
 }
 
@@ -323,14 +348,14 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
 
 hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
-  if (epilogue == kEpiSegSq) return launch_t<128, 128, 2, 2, 2, kEpiSegSq>(p, ny, st);
-  if (epilogue == kEpiFold) return launch_t<256, 256, 4, 2, 2, kEpiFold>(p, ny, st);
+  if (epilogue == kEpiSegSq) return launch_t<MM_SEG>(p, ny, st);
+  if (epilogue == kEpiFold) return launch_t<MM_BIG, kEpiFold>(p, ny, st);
   if (p.N == 0) return hipSuccess;
   // 256 x 256 tiles when both sides fill them and there is a tile per CU
   if (p.Mrows >= 256 && p.N >= 256 &&
       (int64_t)((p.Mrows + 255) / 256) * ((p.N + 255) / 256) * ny >= 256)
-    return launch_t<256, 256, 4, 2, 2, kEpiStore>(p, ny, st);
-  return launch_t<128, 128, 2, 2, 2, kEpiStore>(p, ny, st);
+    return launch_t<MM_BIG, kEpiStore>(p, ny, st);
+  return launch_t<MM_SMALL, kEpiStore>(p, ny, st);
 }
 
 }  // namespace hna
