@@ -7,20 +7,21 @@
 //     of one W_q / W_k / W_v segment, b never stored;
 //   * plain store of C transposed (C[m, n] at n * ldc + m, m contiguous),
 //     fp32 or bf16, per batch entry or per K chunk.
-// Workgroup tile BM x BN x 64 on WGM x WGN waves, each wave (BM/WGM) x
+// Workgroup tile BM x BN x BK on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
-// The fold runs 256 x 256 tiles on 8 waves (two per SIMD, so one wave's
-// MFMAs overlap the other's LDS reads and barrier waits); the segment square
-// and the plain store run 128 x 128 (or 128 x 256) tiles on 4 waves, two
-// workgroups per CU.  Both operand tiles arrive in LDS by asynchronous
-// 16-byte buffer -> LDS copies into a ring of NST stages: the copies of K
-// step k + NST - 1 are issued before the MFMAs of step k.  LDS rows of 64
-// elements (128 bytes) hold their 16-byte chunks XOR-swizzled by the row index,
-// so the 16 rows that a fragment read (32 rows, one chunk) serves at once hit
-// 16 distinct bank slots (no LDS bank conflicts, by the counters).  Rows past M or N and elements past K read zeros (buffer
-// range check, chunk masking); K must be a multiple of 8.  Workgroup ids map
-// tiles XCD by XCD, in groups of 4 tile rows, so the workgroups that share an
-// XCD's L2 at one time share operand panels.
+// The fold and the large stores run 256 x 256 tiles on 8 waves (two per SIMD,
+// so one wave's MFMAs overlap the other's LDS reads and barrier waits); the
+// segment square and the small stores run 128 x 128 tiles on 4 waves, two
+// workgroups per CU.  Both operand tiles arrive in LDS by asynchronous 16-byte
+// buffer -> LDS copies into a ring of NST stages: the copies of K step
+// k + NST - 1 are issued before the MFMAs of step k (BK = 64 with two stages
+// measured faster than BK = 32 with three or four).  LDS rows of 64 elements
+// (128 bytes) hold their 16-byte chunks XOR-swizzled by the row index, so the
+// 16 rows that a fragment read serves at once hit 16 distinct bank slots (the
+// bank-conflict counter reads 0).  Rows past M or N and elements past K read
+// zeros (buffer range check, chunk masking); K must be a multiple of 8.
+// Workgroup ids map tiles XCD by XCD, in groups of 4 tile rows, so the
+// workgroups that share an XCD's L2 at one time share operand panels.
 #include "hna_internal.h"
 #include "hna_hot.h"
 
