@@ -15,7 +15,9 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhna.so")
+# HNA_LIB_PATH selects another build of the same library (the sanitizer
+# build of the host-validation test); the default is the in-tree libhna.so
+LIB_PATH = os.environ.get("HNA_LIB_PATH") or os.path.join(_PKG, "libhna.so")
 
 HNA_OK = 0
 HNA_ERR_INVALID_ARG = -1
