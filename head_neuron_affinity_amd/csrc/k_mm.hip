@@ -9,10 +9,10 @@
 //     fp32 or bf16, per batch entry or per K chunk.
 // Workgroup tile BM x BN x BK on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
-// The fold and the large stores run 256 x 256 tiles on 8 waves (two per SIMD,
-// so one wave's MFMAs overlap the other's LDS reads and barrier waits); the
-// segment square and the small stores run 128 x 128 tiles on 4 waves, two
-// workgroups per CU.  Both operand tiles arrive in LDS by asynchronous 16-byte
+// The fold and the large stores run 256 x 256 tiles on 8 waves in ping-pong:
+// the two waves of a SIMD alternate between an MFMA phase and a memory phase
+// (LDS fragment reads, copies), barrier to barrier; the segment square and
+// the small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.  Both operand tiles arrive in LDS by asynchronous 16-byte
 // buffer -> LDS copies into a ring of NST stages: the copies of K step
 // k + NST - 1 are issued before the MFMAs of step k (BK = 64 with two stages
 // measured faster than BK = 32 with three or four).  LDS rows of 64 elements
@@ -58,15 +58,6 @@ __device__ inline u32x4 uniform_rsrc(const void* base, uint32_t bytes) {
 // XOR applied to the 16-byte chunk index in row r of a stage whose rows hold
 // CPR chunks: any 8 consecutive rows put one chunk column in 8 distinct
 // 16-byte slots of the 128-byte lines they span
-#ifndef MM_BIG
-#define MM_BIG 256, 256, 64, 4, 2, 2
-#endif
-#ifndef MM_SMALL
-#define MM_SMALL 128, 128, 64, 2, 2, 2
-#endif
-#ifndef MM_SEG
-#define MM_SEG 128, 128, 64, 2, 2, 2, kEpiSegSq
-#endif
 
 template <int CPR>
 __device__ inline int swz(int r) {
@@ -77,9 +68,10 @@ __device__ inline int swz(int r) {
   return (r / (8 / CPR)) % CPR;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI, bool PP>
 __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParams p) {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static_assert(!PP || (WGM * WGN == 8 && NST == 2), "ping-pong: 8 waves, two stages");
   static_assert(NST >= 2 && NST <= 4, "two to four stages");
   constexpr int NW = WGM * WGN;               // waves, WGM x WGN
   constexpr int WM = BM / WGM, WN = BN / WGN; // wave tile
@@ -154,75 +146,156 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   const u32x4 rx = uniform_rsrc(X + (int64_t)m0 * p.ldx, xbytes);
   const u32x4 ry = uniform_rsrc(Y + (int64_t)n0 * p.ldy, ybytes);
 
-  // ---- copies: copy i of wave w fills rows 8 (4 i + w) .. + 7 of the stage
-  // (X rows first, then Y rows); lane l: row + l / 8, slot l % 8 holding
-  // chunk (l % 8) ^ (row & 7) ----
-  uint32_t voff[NCP];
-  int kc[NCP];   // element offset of the lane's chunk within the stage
-#pragma unroll
-  for (int i = 0; i < NCP; ++i) {
-    const int r = RPI * (NW * i + w) + l / CPR;
-    const int c = (l % CPR) ^ swz<CPR>(r);
-    kc[i] = 8 * c;
-    voff[i] = i < NCX ? (uint32_t)((int64_t)r * p.ldx * 2 + 16 * c)
-                      : (uint32_t)((int64_t)(r - BM) * p.ldy * 2 + 16 * c);
-  }
-  const uint32_t lds0 = lds_addr(lds) + (uint32_t)w * 1024u;
-  auto issue = [&](int k0, int buf) __attribute__((always_inline)) {
-    const uint32_t base = lds0 + (uint32_t)(buf * STAGE);
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
-    const bool tail = k0 + BK > kend;
-#pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      const uint32_t v = tail && k0 + kc[i] >= kend ? kOutOfRange : voff[i];
-      dma16s(i < NCX ? rx : ry, v, soff, base + (uint32_t)(i * NW * 1024));
-    }
-  };
-
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  constexpr int NKS = BK / 16;
+  // fragment reads of K sub-step ks of the stage at sb
+  auto rd = [&](const unsigned char* sb, int ks, uint4 (&fa)[TM][1], uint4 (&fb)[TN][1])
+      __attribute__((always_inline)) {
+    const int col = 2 * ks + (l >> 5);
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st)
-    if (st < nk) issue(kbeg + st * BK, st);
-  for (int kt = 0; kt < nk; ++kt) {
-    // step kt has landed once at most the copies of the steps after it that
-    // are in flight remain (copies complete in issue order); the barrier
-    // makes it visible to every wave and ends every wave's reads of step
-    // kt - 1, whose stage the next copies overwrite
-    const int ahead = min(NST - 2, nk - 1 - kt);
-    if (NST >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * NCP));
-    else if (NST >= 3 && ahead >= 1) __builtin_amdgcn_s_waitcnt(vm_wait(NCP));
-    else __builtin_amdgcn_s_waitcnt(vm_wait(0));
-    __syncthreads();
-    if (kt + NST - 1 < nk) issue(kbeg + (kt + NST - 1) * BK, (kt + NST - 1) % NST);
-    const unsigned char* sb = lds + (kt % NST) * STAGE;
-    constexpr int NKS = BK / 16;
-    auto rd = [&](int ks, uint4 (&fa)[TM][1], uint4 (&fb)[TN][1]) __attribute__((always_inline)) {
-      const int col = 2 * ks + (l >> 5);
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + i * 32 + (l & 31);
+      fa[i][0] = *reinterpret_cast<const uint4*>(sb + r * ROWB + ((col ^ swz<CPR>(r)) << 4));
+    }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + (l & 31);
-        fa[i][0] = *reinterpret_cast<const uint4*>(sb + r * ROWB + ((col ^ swz<CPR>(r)) << 4));
-      }
+    for (int j = 0; j < TN; ++j) {
+      const int r = BM + wn * WN + j * 32 + (l & 31);
+      fb[j][0] = *reinterpret_cast<const uint4*>(sb + r * ROWB + ((col ^ swz<CPR>(r)) << 4));
+    }
+  };
+
+  if constexpr (PP) {
+    // ---- ping-pong: waves 0-3 (group A, one per SIMD) and 4-7 (group B)
+    // alternate between a memory phase (LDS fragment reads of a whole K step
+    // into registers; group A also issues every copy of the next stage) and
+    // an MFMA phase, separated by workgroup barriers: while one wave of a
+    // SIMD runs its MFMAs the other reads.  Group B starts one phase late.
+    // Barrier sequence, phase by phase (A | B):
+    //   copy stage 0, wait | -            barrier 1
+    //   mem(0)             | -            barrier 2
+    //   mfma(0), wait      | mem(0)       barrier 3
+    //   mem(1)             | mfma(0)      barrier 4 ...
+    //   mfma(k), wait      | mem(k)       barrier 2k + 3
+    //   -                  | mfma(nk - 1) barrier 2 nk + 2
+    // so both groups pass 2 nk + 2 barriers.  Group A's copies of stage k + 1
+    // (issued in mem(k)) overwrite the buffer of stage k - 1, whose last reads
+    // (B's mem(k - 1)) ended at barrier 2k + 1; A waits for them at the end
+    // of mfma(k), so they are visible from barrier 2k + 3 on, before either
+    // group reads them.  Each memory phase waits for its own LDS reads before
+    // its barrier.
+    constexpr int NWC = 4;                          // copying waves
+    constexpr int NCPA = ROWS / (RPI * NWC);        // copies per group-A thread
+    constexpr int NCXA = BM / (RPI * NWC);
+    static_assert(BM % (RPI * NWC) == 0 && BN % (RPI * NWC) == 0, "copy rounds cover whole rows");
+    const bool grp_a = w < NWC;
+    const int wa = w & (NWC - 1);
+    // copy i of A-wave wa fills rows RPI (4 i + wa) .. + RPI - 1; the lane's
+    // chunk is the same for every i (rows 32 apart share their swizzle)
+    const int r0 = RPI * wa + l / CPR;
+    const int c0 = (l % CPR) ^ swz<CPR>(r0);
+    const int kc0 = 8 * c0;
+    const uint32_t vx0 = (uint32_t)((int64_t)r0 * p.ldx * 2 + 16 * c0);
+    const uint32_t vy0 = (uint32_t)((int64_t)r0 * p.ldy * 2 + 16 * c0);
+    const uint32_t sx = __builtin_amdgcn_readfirstlane((uint32_t)(RPI * NWC * p.ldx * 2));
+    const uint32_t sy = __builtin_amdgcn_readfirstlane((uint32_t)(RPI * NWC * p.ldy * 2));
+    const uint32_t lds0 = lds_addr(lds) + (uint32_t)wa * 1024u;
+    auto issue = [&](int k0, int buf) __attribute__((always_inline)) {
+      const uint32_t base = lds0 + (uint32_t)(buf * STAGE);
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
+      const bool drop = k0 + BK > kend && k0 + kc0 >= kend;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = BM + wn * WN + j * 32 + (l & 31);
-        fb[j][0] = *reinterpret_cast<const uint4*>(sb + r * ROWB + ((col ^ swz<CPR>(r)) << 4));
+      for (int i = 0; i < NCPA; ++i) {
+        const uint32_t v = drop ? kOutOfRange
+                                : (i < NCXA ? vx0 + (uint32_t)i * sx : vy0 + (uint32_t)(i - NCXA) * sy);
+        dma16s(i < NCXA ? rx : ry, v, soff, base + (uint32_t)(i * NWC * 1024));
       }
     };
+    auto barrier = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (grp_a) {
+      if (nk > 0) issue(kbeg, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    barrier();                       // 1
+    if (!grp_a) barrier();           // 2 (group B's idle phase)
+    for (int kt = 0; kt < nk; ++kt) {
+      const unsigned char* sb = lds + (kt & 1) * STAGE;
+      // memory phase
+      if (grp_a && kt + 1 < nk) issue(kbeg + (kt + 1) * BK, (kt + 1) & 1);
+      uint4 af[NKS][TM][1], bfr[NKS][TN][1];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 af[TM][1], bfr[TN][1];
-      rd(ks, af, bfr);
+      for (int ks = 0; ks < NKS; ++ks) rd(sb, ks, af[ks], bfr[ks]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier();
+      // MFMA phase
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) mma(acc[i][j], af[i], bfr[j]);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mma(acc[i][j], af[ks][i], bfr[ks][j]);
+      if (grp_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      barrier();
+    }
+    if (grp_a) barrier();            // group A's last barrier (B's last mfma)
+  } else {
+    // ---- copies: copy i of wave w fills rows 8 (4 i + w) .. + 7 of the stage
+    // (X rows first, then Y rows); lane l: row + l / 8, slot l % 8 holding
+    // chunk (l % 8) ^ (row & 7) ----
+    uint32_t voff[NCP];
+    int kc[NCP];   // element offset of the lane's chunk within the stage
+  #pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int r = RPI * (NW * i + w) + l / CPR;
+      const int c = (l % CPR) ^ swz<CPR>(r);
+      kc[i] = 8 * c;
+      voff[i] = i < NCX ? (uint32_t)((int64_t)r * p.ldx * 2 + 16 * c)
+                        : (uint32_t)((int64_t)(r - BM) * p.ldy * 2 + 16 * c);
+    }
+    const uint32_t lds0 = lds_addr(lds) + (uint32_t)w * 1024u;
+    auto issue = [&](int k0, int buf) __attribute__((always_inline)) {
+      const uint32_t base = lds0 + (uint32_t)(buf * STAGE);
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
+      const bool tail = k0 + BK > kend;
+  #pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        const uint32_t v = tail && k0 + kc[i] >= kend ? kOutOfRange : voff[i];
+        dma16s(i < NCX ? rx : ry, v, soff, base + (uint32_t)(i * NW * 1024));
+      }
+    };
+
+  #pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+      if (st < nk) issue(kbeg + st * BK, st);
+    for (int kt = 0; kt < nk; ++kt) {
+      // step kt has landed once at most the copies of the steps after it that
+      // are in flight remain (copies complete in issue order); the barrier
+      // makes it visible to every wave and ends every wave's reads of step
+      // kt - 1, whose stage the next copies overwrite
+      const int ahead = min(NST - 2, nk - 1 - kt);
+      if (NST >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * NCP));
+      else if (NST >= 3 && ahead >= 1) __builtin_amdgcn_s_waitcnt(vm_wait(NCP));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+      __syncthreads();
+      if (kt + NST - 1 < nk) issue(kbeg + (kt + NST - 1) * BK, (kt + NST - 1) % NST);
+      const unsigned char* sb = lds + (kt % NST) * STAGE;
+  #pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint4 af[TM][1], bfr[TN][1];
+        rd(sb, ks, af, bfr);
+  #pragma unroll
+        for (int i = 0; i < TM; ++i)
+  #pragma unroll
+          for (int j = 0; j < TN; ++j) mma(acc[i][j], af[i], bfr[j]);
+      }
     }
   }
 
@@ -333,7 +406,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI, bool PP = false>
 hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
   // a tile's rows must lie within the 32-bit range of its buffer resource
   if ((int64_t)BM * p.ldx * 2 > kMaxResourceBytes || (int64_t)BN * p.ldy * 2 > kMaxResourceBytes)
@@ -341,7 +414,7 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
   const int N = EPI == kEpiSegSq ? p.d_next : p.N;
   const int ntiles = ((p.Mrows + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid(8 * ((ntiles + 7) / 8), ny);
-  hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, BK, WGM, WGN, NST, EPI>), grid, dim3(64 * WGM * WGN), 0, st, p);
+  hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, BK, WGM, WGN, NST, EPI, PP>), grid, dim3(64 * WGM * WGN), 0, st, p);
   return hipGetLastError();
 }
 
@@ -349,14 +422,14 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
 
 hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
-  if (epilogue == kEpiSegSq) return launch_t<MM_SEG>(p, ny, st);
-  if (epilogue == kEpiFold) return launch_t<MM_BIG, kEpiFold>(p, ny, st);
+  if (epilogue == kEpiSegSq) return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
+  if (epilogue == kEpiFold) return launch_t<256, 256, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
   if (p.N == 0) return hipSuccess;
   // 256 x 256 tiles when both sides fill them and there is a tile per CU
   if (p.Mrows >= 256 && p.N >= 256 &&
       (int64_t)((p.Mrows + 255) / 256) * ((p.N + 255) / 256) * ny >= 256)
-    return launch_t<MM_BIG, kEpiStore>(p, ny, st);
-  return launch_t<MM_SMALL, kEpiStore>(p, ny, st);
+    return launch_t<256, 256, 64, 4, 2, 2, kEpiStore, true>(p, ny, st);
+  return launch_t<128, 128, 64, 2, 2, 2, kEpiStore>(p, ny, st);
 }
 
 }  // namespace hna
