@@ -815,15 +815,14 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
 
   hipError_t e;
   if (dm->T > 0) {
-    // 1. |x|^2 (and x in bf16); the transposed operands W_o^T [HD][hidden] and
-    //    x^T [hidden][Tp]; the moments x . o_h and |o_h|^2 through Z = x W_o
-    //    [T][HD], Q_h = W_o^(h)T W_o^(h) [d][d] and U_h = a_h Q_h [T][HD]
-    if ((e = launch_x_prep(x, dm->T, D, xx, bf ? xl : nullptr, st)) != hipSuccess)
+    // 1. |x|^2, x in bf16 and x^T [hidden][Tp] in one pass; W_o^T [HD][hidden];
+    //    the moments x . o_h and |o_h|^2 through Z = x W_o [T][HD],
+    //    Q_h = W_o^(h)T W_o^(h) [d][d] and U_h = a_h Q_h [T][HD]
+    if ((e = launch_x_prep(x, dm->T, D, Tp, xx, bf ? xl : nullptr, xT, dt, st)) != hipSuccess)
       return hip_fail(e, fn);
     const void* xg = bf ? xl : static_cast<const void*>(x);
     const bool fused = loo_coef_fused(d, dt);
     if ((e = launch_scale_transpose(W_o, nullptr, WoT, D, HD, D, dt, st)) != hipSuccess ||
-        (e = launch_scale_transpose(xg, nullptr, xT, T, D, Tp, dt, st)) != hipSuccess ||
         (e = gemm(WoT, D, xg, D, HD, T, D, Z, HD, true, 1, 0, 0, 0, 0)) != hipSuccess ||
         (e = gemm(WoT, D, WoT, D, d, d, D, Q, d, true, dm->H, (int64_t)d * D, (int64_t)d * D,
                   (int64_t)d * d, 0)) != hipSuccess ||

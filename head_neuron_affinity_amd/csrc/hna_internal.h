@@ -233,7 +233,10 @@ struct LooCombineParams {
   int16_t group_start[kMaxHeads + 1];
 };
 hipError_t launch_t1_reduce(const float* t1, int n_tc, int64_t HI, double* t1r, hipStream_t st);
-hipError_t launch_x_prep(const float* x, int64_t T, int D, float* xx, void* xl, hipStream_t st);
+// |x|^2, x in bf16 (xl, when not null) and x transposed into [D][Tp] (GEMM
+// dtype, zero padding tokens) in one pass
+hipError_t launch_x_prep(const float* x, int64_t T, int D, int64_t Tp, float* xx, void* xl,
+                         void* xT, int dtype, hipStream_t st);
 hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const float* xx, int64_t T,
                            int H, int d, int D, float2* coef, int dtype, hipStream_t st);
 // bf16 with d a multiple of 32 up to 128: the moments (|o_h|^2 on the matrix

@@ -36,36 +36,79 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kXRows = 4;  // rows of x per 256-thread block (one wave each)
+// One pass over x: |x_t|^2, x rounded to bf16 (when xl is given: the x W_o
+// GEMM's operand) and x transposed, xT [D][Tp] in the GEMM dtype (the token
+// GEMM's operand; tokens T .. Tp - 1 are zeros).  A workgroup takes 64 tokens
+// and walks their rows in 64-feature tiles through LDS; thread (rr, cc) holds
+// columns 4 cc .. 4 cc + 3 of rows rr, rr + 16, rr + 32, rr + 48 and their
+// partial squares, which a fixed butterfly over the row's 16 threads adds at
+// the end.  D is a multiple of 8.
+constexpr int kXT = 64;
 
-// |x_t|^2 (one wave per row, fixed order) and, when xl is given, x rounded to
-// bf16 for the x W_o GEMM
+template <typename E>
 __global__ __launch_bounds__(256) void x_prep_kernel(const float* __restrict__ x, int64_t T, int D,
-                                                     float* __restrict__ xx,
-                                                     uint16_t* __restrict__ xl) {
-  const int l = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kXRows + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = x + t * D;
-  float s = 0.f;
-  if ((D & 3) == 0) {
-    for (int n = 4 * l; n < D; n += 256) {
-      const float4 v = *reinterpret_cast<const float4*>(row + n);
-      s = fmaf(v.x, v.x, s);
-      s = fmaf(v.y, v.y, s);
-      s = fmaf(v.z, v.z, s);
-      s = fmaf(v.w, v.w, s);
-      if (xl) *reinterpret_cast<uint2*>(xl + t * D + n) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+                                                     int64_t Tp, float* __restrict__ xx,
+                                                     uint16_t* __restrict__ xl,
+                                                     E* __restrict__ xT) {
+  __shared__ float tile[kXT][kXT + 1];
+  const int tid = threadIdx.x, cc = tid & 15, rr = tid >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kXT;
+  float sq[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int EPC = 16 / sizeof(E);   // elements per 16-byte store of xT
+  constexpr int CPF = kXT / EPC;        // stores per feature row of the tile
+  for (int f0 = 0; f0 < D; f0 += kXT) {
+    const int f = f0 + 4 * cc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rr + 16 * i;
+      const int64_t t = t0 + r;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < T && f < D) {
+        v = *reinterpret_cast<const float4*>(x + t * D + f);
+        if (xl)
+          *reinterpret_cast<uint2*>(xl + t * D + f) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      }
+      sq[i] = fmaf(v.x, v.x, sq[i]);
+      sq[i] = fmaf(v.y, v.y, sq[i]);
+      sq[i] = fmaf(v.z, v.z, sq[i]);
+      sq[i] = fmaf(v.w, v.w, sq[i]);
+      tile[r][4 * cc] = v.x;
+      tile[r][4 * cc + 1] = v.y;
+      tile[r][4 * cc + 2] = v.z;
+      tile[r][4 * cc + 3] = v.w;
     }
-  } else {
-    for (int n = l; n < D; n += 64) {
-      s = fmaf(row[n], row[n], s);
-      if (xl) xl[t * D + n] = (uint16_t)f32_to_bf16_bits(row[n]);
+    __syncthreads();
+    for (int q = tid; q < kXT * CPF; q += 256) {
+      const int fr = q / CPF, tc = (q % CPF) * EPC;
+      const int fg = f0 + fr;
+      const int64_t tt = t0 + tc;
+      if (fg < D && tt < Tp) {   // Tp and tt are multiples of EPC
+        E* o = xT + (int64_t)fg * Tp + tt;
+        if constexpr (sizeof(E) == 2) {
+          *reinterpret_cast<uint4*>(o) = make_uint4(
+              pack_bf16x2(tile[tc][fr], tile[tc + 1][fr]), pack_bf16x2(tile[tc + 2][fr], tile[tc + 3][fr]),
+              pack_bf16x2(tile[tc + 4][fr], tile[tc + 5][fr]), pack_bf16x2(tile[tc + 6][fr], tile[tc + 7][fr]));
+        } else {
+          *reinterpret_cast<float4*>(o) =
+              make_float4(tile[tc][fr], tile[tc + 1][fr], tile[tc + 2][fr], tile[tc + 3][fr]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // the 16 threads of row set rr are 16 consecutive lanes of one wave
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sq[i] += __shfl_xor(sq[i], o);
+  if (cc == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + rr + 16 * i;
+      if (t < T) xx[t] = sq[i];
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (l == 0) xx[t] = s;
 }
 
 __device__ inline void load8(const __bf16* p, float (&v)[8]) {
@@ -479,11 +522,16 @@ __global__ __launch_bounds__(64) void loo_combine_kernel(const LooCombineParams 
 
 }  // namespace
 
-hipError_t launch_x_prep(const float* x, int64_t T, int D, float* xx, void* xl, hipStream_t st) {
+hipError_t launch_x_prep(const float* x, int64_t T, int D, int64_t Tp, float* xx, void* xl,
+                         void* xT, int dtype, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const int64_t blocks = (T + kXRows - 1) / kXRows;
-  hipLaunchKernelGGL(x_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, T, D, xx,
-                     static_cast<uint16_t*>(xl));
+  const dim3 grid((unsigned)((Tp + kXT - 1) / kXT));
+  if (dtype == 1)
+    hipLaunchKernelGGL(x_prep_kernel<__bf16>, grid, dim3(256), 0, st, x, T, D, Tp, xx,
+                       static_cast<uint16_t*>(xl), static_cast<__bf16*>(xT));
+  else
+    hipLaunchKernelGGL(x_prep_kernel<float>, grid, dim3(256), 0, st, x, T, D, Tp, xx,
+                       static_cast<uint16_t*>(xl), static_cast<float*>(xT));
   return hipGetLastError();
 }
 
