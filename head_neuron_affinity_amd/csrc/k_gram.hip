@@ -8,17 +8,19 @@
 //   sum_t (p_h . w^g_k)^2 = m_hk^T C_h m_hk,   C_h = sum_t a_th a_th^T / r_t^2.
 // The identity is exact (linearity of the sum), so ADD needs one d x d Gram
 // matrix per head instead of a per-(token, head, neuron) square:
-//   gram_kernel   C_h over a token chunk, on the matrix cores, staged through
-//                 LDS transposed (token index contiguous) so that both MFMA
-//                 operands read 16-byte fragments;
+//   gram_kernel   C_h = sum_t (a_th / r_t)(a_th / r_t)^T over a token chunk,
+//                 on the matrix cores: a / r is staged once through LDS,
+//                 transposed (token index contiguous), and serves as both MFMA
+//                 operands (16-byte fragments);
 //   gram_reduce   fixed-order sum over the token chunks;
 //   quad_kernel   Y = C_h M_h(:, block) on the matrix cores, then
 //                 add[g][k] = sum_{h in g} sum_{gate, up} m_hk . Y(:, k).
-// bf16 path: a itself is exact; the scaled operand a / r^2 is rounded to bf16
-// once (an unbiased relative error <= 2^-9 per product, averaged over the
-// token sum), and the reduced fp32 Gram entries are split into two bf16 terms
-// (hi + lo) for the quadratic forms, a relative error near 2^-16 there.  f32
-// path: fp32 MFMA throughout.
+// bf16 path: a / r is rounded to bf16 once (an unbiased relative error <= 2^-9
+// per element, <= 2^-8 per product, averaged over the token sum), and the
+// reduced fp32 Gram entries are split into two bf16 terms (hi + lo) for the
+// quadratic forms, a relative error near 2^-16 there.  f32 path: fp32 MFMA
+// throughout.  A weight w_th per (token, head) in place of 1 / r_t^2 (the
+// leave-one-out score's beta^2) scales by sqrt(w) = beta the same way.
 #include "hna_internal.h"
 
 namespace hna {
@@ -29,12 +31,10 @@ constexpr int kGThreads = 256;
 template <typename E> struct GramLds;
 template <> struct GramLds<__bf16> {
   static constexpr int kPitch = kGramStage + 8;   // elements; 144-byte rows
-  static constexpr int kBufs = 2;                 // a, a / r^2 (rounded to bf16)
   static constexpr int kQ = 1;
 };
 template <> struct GramLds<float> {
   static constexpr int kPitch = kGramStage + 4;   // 272-byte rows
-  static constexpr int kBufs = 2;                 // a, a / r^2
   static constexpr int kQ = 2;
 };
 
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
   using L = GramLds<E>;
   constexpr int TP = L::kPitch;
   constexpr int Q = L::kQ;
-  __shared__ __attribute__((aligned(16))) E xs[L::kBufs][128 * TP];
+  __shared__ __attribute__((aligned(16))) E xs[128 * TP];   // a / r, transposed
 
   const int h = blockIdx.x % p.H;
   const int gc = blockIdx.x / p.H;
@@ -77,9 +77,7 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
   const int64_t H = p.H;
 
   // rows d .. d32-1 stay zero
-  for (int x = tid; x < (d32 - d) * TP; x += kGThreads)
-#pragma unroll
-    for (int b = 0; b < L::kBufs; ++b) xs[b][d * TP + x] = E(0.f);
+  for (int x = tid; x < (d32 - d) * TP; x += kGThreads) xs[d * TP + x] = E(0.f);
 
   f32x16 acc[4];
 #pragma unroll
@@ -131,84 +129,64 @@ __global__ __launch_bounds__(kGThreads) void gram_kernel(const GramParams p) {
     // (ok is refilled by the load of stage ts + 2 kGramStage below)
     __syncthreads();   // the previous stage has been read
     if (has_item) {
-      // tokens outside the chunk get weight 0: each product pairs a value with
-      // a weighted value, so their (finite, row t_begin) values add nothing
+      // tokens outside the chunk get weight 0 (their finite values, from row
+      // t_begin, then add nothing)
 #pragma unroll
       for (int j = 0; j < 4; ++j) rr[j] = ((ok >> j) & 1) ? rr[j] : 0.f;
-      float x[4][8];
-      float wt[4];
+      float sw[4];   // sqrt of the weight: 1 / r_t, or beta_th
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j)
         // hardware reciprocal (about 1 ulp): the product is rounded to bf16
         // on the bf16 path, and 1 ulp is far inside the fp32 tolerance
-        const float inv = rr[j] != 0.f ? __builtin_amdgcn_rcpf(rr[j] * rr[j]) : 0.f;
-        wt[j] = weighted ? rr[j] * rr[j] : inv;
-        if constexpr (sizeof(E) == 2) {
-          const uint32_t wv[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[j][2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
-            x[j][2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
-          }
-        } else {
-          const uint32_t wv[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
-                                  raw[j][NV - 1].x, raw[j][NV - 1].y, raw[j][NV - 1].z,
-                                  raw[j][NV - 1].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[j][e] = __uint_as_float(wv[e]);
-        }
-      }
+        sw[j] = weighted ? rr[j] : (rr[j] != 0.f ? __builtin_amdgcn_rcpf(rr[j]) : 0.f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int base = (8 * fo + e) * TP + 4 * tq;
-        if constexpr (sizeof(E) == 2) {
-          // feature e of tokens 0..3: the raw bf16 halves, repacked (exact)
-          const uint32_t w0 = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-          uint32_t r[4];
+        float y[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t wv[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
-            r[j] = wv[e >> 1];
+        for (int j = 0; j < 4; ++j) {
+          float xv;
+          if constexpr (sizeof(E) == 2) {
+            const uint32_t wv = e < 2 ? raw[j][0].x : e < 4 ? raw[j][0].y : e < 6 ? raw[j][0].z : raw[j][0].w;
+            xv = (e & 1) ? __uint_as_float(wv & 0xffff0000u) : __uint_as_float(wv << 16);
+          } else {
+            const uint32_t wv[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
+                                    raw[j][NV - 1].x, raw[j][NV - 1].y, raw[j][NV - 1].z,
+                                    raw[j][NV - 1].w};
+            xv = __uint_as_float(wv[e]);
           }
-          const uint32_t x01 = __builtin_amdgcn_perm(r[1], r[0], w0);
-          const uint32_t x23 = __builtin_amdgcn_perm(r[3], r[2], w0);
-          float y[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = x[j][e] * wt[j];
-          *reinterpret_cast<uint2*>(&xs[0][base]) = make_uint2(x01, x23);
-          *reinterpret_cast<uint2*>(&xs[1][base]) =
-              make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-        } else {
-          *reinterpret_cast<float4*>(&xs[0][base]) = make_float4(x[0][e], x[1][e], x[2][e], x[3][e]);
-          *reinterpret_cast<float4*>(&xs[1][base]) = make_float4(
-              x[0][e] * wt[0], x[1][e] * wt[1], x[2][e] * wt[2], x[3][e] * wt[3]);
+          y[j] = xv * sw[j];
         }
+        if constexpr (sizeof(E) == 2)
+          *reinterpret_cast<uint2*>(&xs[base]) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        else
+          *reinterpret_cast<float4*>(&xs[base]) = make_float4(y[0], y[1], y[2], y[3]);
       }
     }
     __syncthreads();
     load_item(raw, rr, ok, ts + 2 * kGramStage);   // past the chunk: masked off
-    // C[i][j] += sum_t x[i][t] * (x[j][t] / r_t^2): A rows i, B rows j
+    // C[i][j] += sum_t (x[i][t] / r_t) (x[j][t] / r_t): A rows i, B rows j
 #pragma unroll
     for (int q = 0; q < kGramStage / 16; ++q) {
       const int col = 16 * q + 8 * (l >> 5);
       uint4 af[2][Q], bh[2][Q];
       // the fragments of the wave's row tiles (A) and column tiles (B)
-      auto frag = [&](uint4 (&f)[Q], int buf, int tile) __attribute__((always_inline)) {
+      auto frag = [&](uint4 (&f)[Q], int tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int qq = 0; qq < Q; ++qq)
-          f[qq] = *reinterpret_cast<const uint4*>(&xs[buf][(tile * 32 + (l & 31)) * TP + col] +
+          f[qq] = *reinterpret_cast<const uint4*>(&xs[(tile * 32 + (l & 31)) * TP + col] +
                                                   qq * (16 / sizeof(E)));
       };
       if constexpr (NT >= 3) {
         const int it0 = 2 * (w >> 1), jt0 = 2 * (w & 1);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          if (it0 + x < NT) frag(af[x], 0, it0 + x);
-          if (jt0 + x < NT) frag(bh[x], 1, jt0 + x);
+          if (it0 + x < NT) frag(af[x], it0 + x);
+          if (jt0 + x < NT) frag(bh[x], jt0 + x);
         }
       } else if (w < NT * NT) {
-        frag(af[0], 0, w / NT);
-        frag(bh[0], 1, w % NT);
+        frag(af[0], w / NT);
+        frag(bh[0], w % NT);
       }
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
