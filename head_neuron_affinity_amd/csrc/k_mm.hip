@@ -12,14 +12,15 @@
 // The fold and the large stores run 256 x 256 tiles on 8 waves in ping-pong:
 // the two waves of a SIMD alternate between an MFMA phase and a memory phase
 // (LDS fragment reads, copies), barrier to barrier; the segment square and
-// the small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.  Both operand tiles arrive in LDS by asynchronous 16-byte
-// buffer -> LDS copies into a ring of NST stages: the copies of K step
-// k + NST - 1 are issued before the MFMAs of step k (BK = 64 with two stages
-// measured faster than BK = 32 with three or four).  LDS rows of 64 elements
-// (128 bytes) hold their 16-byte chunks XOR-swizzled by the row index, so the
-// 16 rows that a fragment read serves at once hit 16 distinct bank slots (the
-// bank-conflict counter reads 0).  Rows past M or N and elements past K read
-// zeros (buffer range check, chunk masking); K must be a multiple of 8.
+// the small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.
+// Both operand tiles arrive in LDS by asynchronous 16-byte buffer -> LDS
+// copies into a ring of NST stages: the copies of K step k + NST - 1 are
+// issued before the MFMAs of step k (BK = 64 with two stages measured faster
+// than BK = 32 with three or four).  LDS rows of 64 elements (128 bytes) hold
+// their 16-byte chunks XOR-swizzled by the row index, so the 16 rows that a
+// fragment read serves at once hit 16 distinct bank slots (the bank-conflict
+// counter reads 0).  Rows past M or N and elements past K read zeros (buffer
+// range check, chunk masking); K must be a multiple of 8.
 // Workgroup ids map tiles XCD by XCD, in groups of 4 tile rows, so the
 // workgroups that share an XCD's L2 at one time share operand panels.
 #include "hna_internal.h"
