@@ -10,7 +10,9 @@ Prints one JSON line.  `value` is calibration tokens/s of the whole step;
 `roofline` describes the hot kernel (algorithmic MFMA FLOPs per launch over
 its average duration measured with HIP events on the launch stream);
 `cpu_baseline` is the float64 oracle timed on this host on a bounded token
-sample of the same layer.  Unless --no-legs is given, the line also carries
+sample of the same layer; `mfma_loop` is the matrix cores' sustained bf16
+rate on random operands (hna_mfma_rate_probe), the second reference for the
+hot kernel's MFMA rate besides the published peak.  Unless --no-legs is given, the line also carries
 the other single-layer workloads (Danube3-500M-shaped and the large
 4096 x 14336 layer) measured the same way, the 28-layer Qwen3-0.6B-shaped
 stack end to end, the leave-one-out score and the layout-search calls.
@@ -289,6 +291,33 @@ def time_layer(hna, layer, steps: int, warmup: int):
     return P, wall * 1e3 / steps, hot_ms
 
 
+def mfma_loop_bench(hna, hot_tflops: float, n_wg: int = 512, rounds: int = 10000, reps: int = 5):
+    """The matrix cores' sustained bf16 rate on this device: hna_mfma_rate_probe
+    (back-to-back 32x32x16 MFMAs, four independent accumulators per wave, two
+    waves per SIMD, random operands so that power and clock are those of real
+    data; about as long as one hot-kernel launch), timed with HIP events on the
+    launch stream.  The hot kernel's MFMA rate is also reported as a fraction
+    of it."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(20260)
+    seed = torch.randn(n_wg * 256 * 64, device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        hna.mfma_rate_probe(seed, n_wg, rounds, out=out)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        hna.mfma_rate_probe(seed, n_wg, rounds, out=out)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = n_wg * 4 * rounds * 4 * 32768 / (ms * 1e-3) / 1e12
+    return {"achieved": tf, "unit": "TFLOP/s", "frac_of_published_peak": tf / PEAK_BF16_TFLOPS,
+            "hot_kernel_frac_of_loop": hot_tflops / tf, "ms_per_call": ms,
+            "workgroups": n_wg, "waves_per_simd": 2, "rounds": rounds, "operands": "random bf16"}
+
+
 def layer_figures(shape, ms_step: float, hot_ms: float):
     """Throughput and the hot kernel's roofline for one layer workload."""
     T, H, d, I = shape.T, shape.H, shape.d, shape.I
@@ -414,6 +443,9 @@ def main():
         "mfma_frac_whole_step": fig["mfma_frac_whole_step"],
         "hot_stream_gbs": fig["hot_stream_gbs"],
     }
+    if shape.dtype == "bf16":
+        rec["mfma_loop"] = mfma_loop_bench(hna, fig["roofline"]["achieved"])
+        progress("matrix-core rate probe done")
     if not args.no_legs:
         grp = [int(x) for x in L0["group_of_head"].tolist()]
         rec["loo"] = loo_bench(hna, L0, P0, grp, 5)

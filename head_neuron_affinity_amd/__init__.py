@@ -11,7 +11,8 @@ from ._binding import (HnaError, HNA_BF16, HNA_F32, HNA_ACCUMULATE, hna_dims, hn
                        up_workspace_bytes, down_workspace_bytes, folded_bytes, status_string,
                        last_error, unit_mass, layout_objective, neuron_step,
                        head_step, layout_search, DUAL_ITERS, loo_workspace_bytes,
-                       affinity_loo, static_scratch_bytes, affinity_up_static)
+                       affinity_loo, static_scratch_bytes, affinity_up_static,
+                       mfma_rate_probe)
 from .pipeline import AffinityPass, StackPass, pass_for_layer, affinity_layer
 
 __all__ = [
@@ -22,5 +23,5 @@ __all__ = [
     "StackPass",
     "pass_for_layer", "affinity_layer", "unit_mass", "layout_objective",
     "neuron_step", "head_step", "layout_search", "DUAL_ITERS", "loo_workspace_bytes",
-    "affinity_loo", "static_scratch_bytes", "affinity_up_static",
+    "affinity_loo", "static_scratch_bytes", "affinity_up_static", "mfma_rate_probe",
 ]

@@ -43,6 +43,7 @@ EXPORTED = [
     "hna_layout_objective", "hna_neuron_step", "hna_head_step",
     "hna_layout_search_workspace_bytes", "hna_layout_search", "hna_loo_workspace_bytes",
     "hna_affinity_loo", "hna_static_scratch_bytes", "hna_affinity_up_static",
+    "hna_mfma_rate_probe",
 ]
 
 
@@ -105,6 +106,7 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_int, vp, vp, vp, vp]),
         "hna_affinity_loo": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, f32, vp, vp,
                                             sz, vp]),
+        "hna_mfma_rate_probe": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "hna_layout_search": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                                               ctypes.POINTER(ctypes.c_double), ip, vp, sz, vp]),
     }
@@ -342,6 +344,23 @@ def down_combine(c_down, n, out=None) -> torch.Tensor:
 
 
 # ------------------------------------------------------- layout objective
+def mfma_rate_probe(seed: torch.Tensor, n_workgroups: int, iters: int,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run the matrix-core rate probe (hna_mfma_rate_probe): `seed` holds
+    n_workgroups * 256 * 128 bytes of bf16 operands; returns the per-thread
+    checksums (fp32, n_workgroups * 256)."""
+    _need_cuda(seed)
+    n = int(n_workgroups) * 256
+    if seed.numel() * seed.element_size() < n * 128:
+        raise ValueError(f"seed: {seed.numel() * seed.element_size()} bytes, needs {n * 128}")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=seed.device)
+    _expect(out, "out", (n,), torch.float32)
+    _check(lib().hna_mfma_rate_probe(int(n_workgroups), int(iters), _ptr(seed), _ptr(out),
+                                     _stream(seed.device)), "hna_mfma_rate_probe")
+    return out
+
+
 def unit_mass(S: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Each matrix S[m] (fp32, last two dims) divided by its own sum; 0 if the sum is 0."""
     _need_cuda(S)

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libhna.so")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 
 SOURCES = ["hna_api.hip", "k_affinity.hip", "k_gram.hip", "k_gemm.hip", "k_mm.hip",
-           "k_small.hip", "k_objective.hip", "k_layout.hip", "k_loo.hip"]
+           "k_small.hip", "k_objective.hip", "k_layout.hip", "k_loo.hip", "k_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

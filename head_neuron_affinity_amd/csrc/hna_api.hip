@@ -537,6 +537,19 @@ int hna_unit_mass(const float* S, int64_t count, int32_t n_matrices, float* out,
   return finish(launch_unit_mass(S, count, n_matrices, out, st), st, fn);
 }
 
+int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, const void* seed, float* out,
+                        void* stream) {
+  const char* fn = "hna_mfma_rate_probe";
+  if (n_workgroups < 1 || n_workgroups > 65536)
+    return fail(HNA_ERR_INVALID_ARG, "%s: n_workgroups=%d outside [1, 65536]", fn, n_workgroups);
+  if (iters < 1 || iters > 1000000)
+    return fail(HNA_ERR_INVALID_ARG, "%s: iters=%d outside [1, 1000000]", fn, iters);
+  REQUIRE_PTR(seed);
+  REQUIRE_PTR(out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(launch_mfma_rate(seed, n_workgroups, iters, out, st), st, fn);
+}
+
 int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, const float* S_down,
                          const int32_t* head_device, const int32_t* neuron_device,
                          double* frac_up, double* frac_down, double* J, void* stream) {

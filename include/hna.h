@@ -402,6 +402,24 @@ int hna_layout_search(int32_t N, int32_t G, int32_t I, int32_t L, const float* S
                       int32_t* neuron_stats, double* J_history, int32_t* n_sweeps,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ measurement */
+
+/*
+ * Sustained bf16 matrix-core rate (a measurement aid, not a step of the
+ * method; it reads the dense rate the affinity kernel's MFMA throughput is
+ * compared with).  n_workgroups workgroups of 256 threads each run `iters`
+ * rounds of four independent 32x32x16 bf16 MFMAs (v_mfma_f32_32x32x16_bf16)
+ * per wave: n_workgroups * 4 * iters * 4 * 32768 FLOP in all.  Thread t of
+ * the grid loads its four operand pairs from seed[8 t .. 8 t + 7] (16-byte
+ * items of bf16: seed holds n_workgroups * 256 * 128 bytes; random values
+ * give the power draw, and the clock, of real data) and writes the sum of its
+ * accumulators to out[t] (n_workgroups * 256 floats).  Both buffers are
+ * caller-owned device memory, 16-byte aligned.  Limits: 1 <= n_workgroups <=
+ * 65536 and 1 <= iters <= 1,000,000, else HNA_ERR_INVALID_ARG.
+ */
+int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, const void* seed, float* out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -327,6 +327,22 @@ def test_loo_validates():
     assert L.hna_loo_workspace_bytes(None) == 0
 
 
+def test_mfma_rate_probe_validates():
+    hna = _lib()
+    L = hna.lib()
+    vp = ctypes.c_void_p
+    F = vp(FAKE)
+    probe = L.hna_mfma_rate_probe
+    assert probe(0, 10, F, F, None) == -1            # no workgroups
+    assert probe(65537, 10, F, F, None) == -1        # past the grid limit
+    assert probe(8, 0, F, F, None) == -1             # no rounds
+    assert "iters" in L.hna_last_error().decode()
+    assert probe(8, 1_000_001, F, F, None) == -1     # past the round limit
+    assert probe(8, 10, None, F, None) == -1
+    assert probe(8, 10, F, vp(MIS), None) == -3
+    assert "out" in L.hna_last_error().decode()
+
+
 def test_error_text_is_thread_local():
     hna = _lib()
     call_up(hna, dims(hna, d=20))
