@@ -9,7 +9,8 @@
 //     fp32 or bf16, per batch entry or per K chunk.
 // Workgroup tile BM x BN x BK on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
-// The fold and the large stores run 256 x 256 tiles on 8 waves in ping-pong:
+// The fold (256 x 256, or 256 x 192 where that fills the CUs better) and the
+// large stores run 256-row tiles on 8 waves in ping-pong:
 // the two waves of a SIMD alternate between an MFMA phase and a memory phase
 // (LDS fragment reads, copies), barrier to barrier; the segment square and
 // the small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.
@@ -421,10 +422,24 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
 
 }  // namespace
 
+// rounds of `slots` concurrent workgroups (one per CU) times the work of one
+// tile (its column count, at equal rows and K): the cost of a tiling
+static int64_t tiling_cost(int64_t tiles, int slots, int cols) { return (tiles + slots - 1) / slots * cols; }
+
 hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
+  const int64_t ntm256 = (p.Mrows + 255) / 256;
+  // one segment per tile column (192-row ping-pong tiles measured 17-36%
+  // slower than these)
   if (epilogue == kEpiSegSq) return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
-  if (epilogue == kEpiFold) return launch_t<256, 256, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
+  if (epilogue == kEpiFold) {
+    // 256 x 192 tiles where they fill the CUs with less work per CU (the
+    // Qwen3-0.6B-shaped fold: 256 tiles instead of 192 on 256 CUs)
+    const int64_t c256 = tiling_cost(ntm256 * ((p.N + 255) / 256) * ny, 256, 256);
+    const int64_t c192 = tiling_cost(ntm256 * ((p.N + 191) / 192) * ny, 256, 192);
+    if (c192 < c256) return launch_t<256, 192, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
+    return launch_t<256, 256, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
+  }
   if (p.N == 0) return hipSuccess;
   // 256 x 256 tiles when both sides fill them and there is a tile per CU
   if (p.Mrows >= 256 && p.N >= 256 &&
