@@ -373,9 +373,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
       p.seg_part[(int64_t)z * p.Mrows + m0 + tid] = t;
     }
   } else {
+    char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
+    if constexpr (PP && WM == 64 && WN % 64 == 0) {
+      // bf16 output of the 256 x 256 kernel: each wave stages its 64-row
+      // block through LDS, 64 columns at a time (the operand stages are idle
+      // once every wave has passed the loop's last barrier), so that eight
+      // lanes write one column's 64 consecutive rows (128 bytes) with 16-byte
+      // stores instead of 64 scattered 8-byte pieces per instruction
+      if (p.out_bf16 && p.ldc % 8 == 0 && p.bc % 8 == 0) {
+        constexpr int PITCH = 144;   // bytes per staged column: 128 + 16
+        static_assert(NW * 64 * PITCH <= NST * STAGE, "staging fits the operand stages");
+        __syncthreads();
+        unsigned char* stg = lds + w * 64 * PITCH;
+        uint16_t* Cs = reinterpret_cast<uint16_t*>(Cb);
+#pragma unroll
+        for (int jh = 0; jh < WN / 64; ++jh) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int a = 0; a < 4; ++a) {
+                const f32x16& c = acc[i][2 * jh + jj];
+                const int nn = jj * 32 + (l & 31), mm = i * 32 + 8 * a + 4 * (l >> 5);
+                *reinterpret_cast<uint2*>(stg + nn * PITCH + mm * 2) =
+                    make_uint2(f32_to_bf16_bits(c[4 * a]) | (f32_to_bf16_bits(c[4 * a + 1]) << 16),
+                               f32_to_bf16_bits(c[4 * a + 2]) | (f32_to_bf16_bits(c[4 * a + 3]) << 16));
+              }
+          // a wave's LDS operations run in order; the wait and the clobber
+          // keep the compiler's order too
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int c = l + 64 * k, nn = c >> 3, q = c & 7;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + nn * PITCH + q * 16);
+            const int n = n0 + wn * WN + jh * 64 + nn;
+            const int m = m0 + wm * WM + 8 * q;
+            if (n >= p.N || m >= p.Mrows) continue;
+            const int64_t o = (int64_t)n * p.ldc + m;
+            if (m + 8 <= p.Mrows) {
+              *reinterpret_cast<uint4*>(Cs + o) = v;
+            } else {
+              const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+              for (int e = 0; e < p.Mrows - m; ++e) Cs[o + e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        return;
+      }
+    }
     // C[m, n] at n * ldc + m: a lane's 4 consecutive rows m (e = 0..3) are one
     // 8-byte (bf16) or 16-byte (fp32) store
-    char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
