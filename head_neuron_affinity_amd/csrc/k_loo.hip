@@ -225,7 +225,10 @@ __device__ inline float bf16_at(const uint4& v, int e) {
 // x . o_h = Z . a is dotted over the same features; two exchanges across the
 // wave's quarters complete both sums.
 // (alpha beta / r) a, rounded to bf16, is written transposed: ZAT[h d + j][t]
-// for t < Tp (zeros for the padding tokens T .. Tp - 1).
+// for t < Tp (zeros for the padding tokens T .. Tp - 1).  The workgroup's four
+// waves take four adjacent 16-token tiles; their values are staged through
+// LDS, feature-major, so that each ZAT row receives its 64 tokens as one
+// 128-byte run of 16-byte stores.
 constexpr int kCoefBlocksPerHead = 128;
 
 template <int ND>
@@ -237,7 +240,11 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
                                                             int64_t T, int64_t Tp, int H, int D,
                                                             float2* __restrict__ coef) {
   constexpr int d = 32 * ND, QS = d + 8;  // LDS row stride, elements
+  constexpr int ZS = 64 + 8;              // staged ZAT row: 64 tokens + pad
   __shared__ __attribute__((aligned(16))) uint16_t qs[d * QS];
+  // the workgroup's 64 tokens of (alpha beta / r) a, feature-major, so that
+  // ZAT rows go out as 128-byte runs
+  __shared__ __attribute__((aligned(16))) uint16_t zst[d * ZS];
   const int h = blockIdx.y;
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(Q) + (int64_t)h * d * d;
   for (int i = threadIdx.x; i < d * d / 8; i += 256) {
@@ -251,7 +258,12 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
   uint16_t* ztp = reinterpret_cast<uint16_t*>(ZAT) + (int64_t)h * d * Tp;
   const int64_t n_tiles = (T + 15) / 16;
   const int64_t step = (int64_t)gridDim.x * 4;
-  int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // blocks of 64 tokens, the 4 waves' tiles side by side; the trip count is
+  // the workgroup's, so every wave reaches every barrier (a tile past the
+  // last reads and stages zeros, and nothing of it is stored)
+  const int64_t n_blk = (n_tiles + 3) / 4;
+  const int wave = threadIdx.x >> 6;
+  int64_t tile = (int64_t)blockIdx.x * 4 + wave;
   uint4 ar[ND], zr[ND];
   auto fetch = [&](int64_t tt) {
     const int64_t t = tt * 16 + tl;
@@ -264,11 +276,11 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
     }
   };
   fetch(tile);
-  for (; tile < n_tiles; tile += step) {
+  for (int64_t blk = blockIdx.x; blk < n_blk; blk += gridDim.x, tile += step) {
     uint4 a_cur[ND], z_cur[ND];
 #pragma unroll
     for (int ks = 0; ks < ND; ++ks) { a_cur[ks] = ar[ks]; z_cur[ks] = zr[ks]; }
-    if (tile + step < n_tiles) fetch(tile + step);  // the next tile loads under this one's work
+    fetch(tile + step);  // the next tile loads under this one's work (zeros past the last)
     const int64_t t = tile * 16 + tl;
     const bool ok = t < T;
     // re-read the Q_h fragments from LDS on every tile rather than holding all
@@ -310,15 +322,23 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
       if (qq == 0) coef[t * H + h] = c;
       w = c.x * c.y * inv_rms((float)x2, D);
     }
-    if (t >= Tp) continue;
-    // feature 32 ks + 8 qq + e of token t; the 16 lanes of a quarter write 16
-    // consecutive tokens of one row
+    // feature 32 ks + 8 qq + e of token t into column 16 wave + tl
 #pragma unroll
     for (int ks = 0; ks < ND; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        ztp[(int64_t)(32 * ks + 8 * qq + e) * Tp + t] =
+        zst[(32 * ks + 8 * qq + e) * ZS + 16 * wave + tl] =
             (uint16_t)f32_to_bf16_bits(bf16_at(a_cur[ks], e) * w);
+    __syncthreads();
+    // row f's 64 tokens as eight 16-byte pieces (tokens past Tp not stored)
+    const int64_t t_blk = blk * 64;
+#pragma unroll
+    for (int k = 0; k < d / 32; ++k) {
+      const int c = threadIdx.x + 256 * k, f = c >> 3, q = c & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(zst + f * ZS + 8 * q);
+      if (t_blk + 8 * q < Tp) *reinterpret_cast<uint4*>(ztp + (int64_t)f * Tp + t_blk + 8 * q) = v;
+    }
+    __syncthreads();
   }
 }
 

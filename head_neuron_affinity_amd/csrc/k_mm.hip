@@ -375,7 +375,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   } else {
     char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
     if constexpr (PP && WM == 64 && WN % 64 == 0) {
-      // bf16 output of the 256 x 256 kernel: each wave stages its 64-row
+      // output of the 256 x 256 kernel, bf16: each wave stages its 64-row
       // block through LDS, 64 columns at a time (the operand stages are idle
       // once every wave has passed the loop's last barrier), so that eight
       // lanes write one column's 64 consecutive rows (128 bytes) with 16-byte
@@ -416,6 +416,46 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
             } else {
               const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
               for (int e = 0; e < p.Mrows - m; ++e) Cs[o + e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        return;
+      }
+      // fp32 output (the token-chunk parts of R): the same through LDS, 32
+      // columns at a time, sixteen lanes writing one column's 64 rows (256
+      // bytes)
+      if (!p.out_bf16 && p.ldc % 4 == 0 && p.bc % 4 == 0) {
+        constexpr int PITCH = 272;   // bytes per staged column: 256 + 16
+        static_assert(NW * 32 * PITCH <= NST * STAGE, "staging fits the operand stages");
+        __syncthreads();
+        unsigned char* stg = lds + w * 32 * PITCH;
+        float* Cf = reinterpret_cast<float*>(Cb);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const f32x16& c = acc[i][j];
+              const int nn = l & 31, mm = i * 32 + 8 * a + 4 * (l >> 5);
+              *reinterpret_cast<float4*>(stg + nn * PITCH + mm * 4) =
+                  make_float4(c[4 * a], c[4 * a + 1], c[4 * a + 2], c[4 * a + 3]);
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int c = l + 64 * k, nn = c >> 4, q = c & 15;
+            const float4 v = *reinterpret_cast<const float4*>(stg + nn * PITCH + q * 16);
+            const int n = n0 + wn * WN + j * 32 + nn;
+            const int m = m0 + wm * WM + 4 * q;
+            if (n >= p.N || m >= p.Mrows) continue;
+            const int64_t o = (int64_t)n * p.ldc + m;
+            if (m + 4 <= p.Mrows) {
+              *reinterpret_cast<float4*>(Cf + o) = v;
+            } else {
+              const float vv[4] = {v.x, v.y, v.z, v.w};
+              for (int e = 0; e < p.Mrows - m; ++e) Cf[o + e] = vv[e];
             }
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
