@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_int, vp, vp, vp, vp]),
         "hna_affinity_loo": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, f32, vp, vp,
                                             sz, vp]),
-        "hna_mfma_rate_probe": (ctypes.c_int, [i32, i32, vp, vp, vp]),
+        "hna_mfma_rate_probe": (ctypes.c_int, [i32, i32, i32, vp, vp, vp]),
         "hna_layout_search": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                                               ctypes.POINTER(ctypes.c_double), ip, vp, sz, vp]),
     }
@@ -345,10 +345,10 @@ def down_combine(c_down, n, out=None) -> torch.Tensor:
 
 # ------------------------------------------------------- layout objective
 def mfma_rate_probe(seed: torch.Tensor, n_workgroups: int, iters: int,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Run the matrix-core rate probe (hna_mfma_rate_probe): `seed` holds
-    n_workgroups * 256 * 128 bytes of bf16 operands; returns the per-thread
-    checksums (fp32, n_workgroups * 256)."""
+                    out: Optional[torch.Tensor] = None, shape: int = 0) -> torch.Tensor:
+    """Run the matrix-core rate probe (hna_mfma_rate_probe; shape 0: 32x32x16
+    MFMAs, 1: 16x16x32): `seed` holds n_workgroups * 256 * 128 bytes of bf16
+    operands; returns the per-thread checksums (fp32, n_workgroups * 256)."""
     _need_cuda(seed)
     n = int(n_workgroups) * 256
     if seed.numel() * seed.element_size() < n * 128:
@@ -356,8 +356,8 @@ def mfma_rate_probe(seed: torch.Tensor, n_workgroups: int, iters: int,
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=seed.device)
     _expect(out, "out", (n,), torch.float32)
-    _check(lib().hna_mfma_rate_probe(int(n_workgroups), int(iters), _ptr(seed), _ptr(out),
-                                     _stream(seed.device)), "hna_mfma_rate_probe")
+    _check(lib().hna_mfma_rate_probe(int(n_workgroups), int(iters), int(shape), _ptr(seed),
+                                     _ptr(out), _stream(seed.device)), "hna_mfma_rate_probe")
     return out
 
 

@@ -537,9 +537,11 @@ int hna_unit_mass(const float* S, int64_t count, int32_t n_matrices, float* out,
   return finish(launch_unit_mass(S, count, n_matrices, out, st), st, fn);
 }
 
-int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, const void* seed, float* out,
-                        void* stream) {
+int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, int32_t shape, const void* seed,
+                        float* out, void* stream) {
   const char* fn = "hna_mfma_rate_probe";
+  if (shape != 0 && shape != 1)
+    return fail(HNA_ERR_INVALID_ARG, "%s: shape=%d is neither 0 (32x32x16) nor 1 (16x16x32)", fn, shape);
   if (n_workgroups < 1 || n_workgroups > 65536)
     return fail(HNA_ERR_INVALID_ARG, "%s: n_workgroups=%d outside [1, 65536]", fn, n_workgroups);
   if (iters < 1 || iters > 1000000)
@@ -547,7 +549,7 @@ int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, const void* seed, f
   REQUIRE_PTR(seed);
   REQUIRE_PTR(out);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return finish(launch_mfma_rate(seed, n_workgroups, iters, out, st), st, fn);
+  return finish(launch_mfma_rate(seed, n_workgroups, iters, shape, out, st), st, fn);
 }
 
 int hna_layout_objective(int32_t N, int32_t G, int32_t I, const float* S_up, const float* S_down,

@@ -146,7 +146,8 @@ hipError_t launch_down_combine(const float* c, const float* n, int I, int G_next
 
 // ----------------------------------------------------------- layout objective
 hipError_t launch_unit_mass(const float* S, int64_t count, int n_mat, float* out, hipStream_t st);
-hipError_t launch_mfma_rate(const void* seed, int n_wg, int iters, float* out, hipStream_t st);
+hipError_t launch_mfma_rate(const void* seed, int n_wg, int iters, int shape, float* out,
+                            hipStream_t st);
 int max_objective_layers();
 hipError_t launch_layout_objective(const float* S_up, const float* S_down, const int32_t* heads,
                                    const int32_t* neurons, int N, int G, int I, double* frac_up,

@@ -408,17 +408,20 @@ int hna_layout_search(int32_t N, int32_t G, int32_t I, int32_t L, const float* S
  * Sustained bf16 matrix-core rate (a measurement aid, not a step of the
  * method; it reads the dense rate the affinity kernel's MFMA throughput is
  * compared with).  n_workgroups workgroups of 256 threads each run `iters`
- * rounds of four independent 32x32x16 bf16 MFMAs (v_mfma_f32_32x32x16_bf16)
- * per wave: n_workgroups * 4 * iters * 4 * 32768 FLOP in all.  Thread t of
+ * rounds of independent bf16 MFMAs per wave: four 32x32x16
+ * (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) for shape 0, eight 16x16x32
+ * (v_mfma_f32_16x16x32_bf16, 16384 FLOP each, accumulators k and k + 4 on
+ * operand pair k) for shape 1; n_workgroups * 4 * iters * 131072 FLOP in all
+ * either way.  Thread t of
  * the grid loads its four operand pairs from seed[8 t .. 8 t + 7] (16-byte
  * items of bf16: seed holds n_workgroups * 256 * 128 bytes; random values
  * give the power draw, and the clock, of real data) and writes the sum of its
  * accumulators to out[t] (n_workgroups * 256 floats).  Both buffers are
  * caller-owned device memory, 16-byte aligned.  Limits: 1 <= n_workgroups <=
- * 65536 and 1 <= iters <= 1,000,000, else HNA_ERR_INVALID_ARG.
+ * 65536, 1 <= iters <= 1,000,000 and shape 0 or 1, else HNA_ERR_INVALID_ARG.
  */
-int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, const void* seed, float* out,
-                        void* stream);
+int hna_mfma_rate_probe(int32_t n_workgroups, int32_t iters, int32_t shape, const void* seed,
+                        float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -333,13 +333,15 @@ def test_mfma_rate_probe_validates():
     vp = ctypes.c_void_p
     F = vp(FAKE)
     probe = L.hna_mfma_rate_probe
-    assert probe(0, 10, F, F, None) == -1            # no workgroups
-    assert probe(65537, 10, F, F, None) == -1        # past the grid limit
-    assert probe(8, 0, F, F, None) == -1             # no rounds
+    assert probe(0, 10, 0, F, F, None) == -1            # no workgroups
+    assert probe(65537, 10, 0, F, F, None) == -1        # past the grid limit
+    assert probe(8, 0, 0, F, F, None) == -1             # no rounds
     assert "iters" in L.hna_last_error().decode()
-    assert probe(8, 1_000_001, F, F, None) == -1     # past the round limit
-    assert probe(8, 10, None, F, None) == -1
-    assert probe(8, 10, F, vp(MIS), None) == -3
+    assert probe(8, 1_000_001, 1, F, F, None) == -1     # past the round limit
+    assert probe(8, 10, 2, F, F, None) == -1            # no such MFMA shape
+    assert "shape" in L.hna_last_error().decode()
+    assert probe(8, 10, 0, None, F, None) == -1
+    assert probe(8, 10, 1, F, vp(MIS), None) == -3
     assert "out" in L.hna_last_error().decode()
 
 
