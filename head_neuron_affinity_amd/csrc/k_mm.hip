@@ -12,8 +12,9 @@
 // The fold (256 x 256, or 256 x 192 where that fills the CUs better) and the
 // large stores run 256-row tiles on 8 waves in ping-pong:
 // the two waves of a SIMD alternate between an MFMA phase and a memory phase
-// (LDS fragment reads, copies), barrier to barrier; the segment square and
-// the small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.
+// (LDS fragment reads, copies), barrier to barrier; so do the segment
+// squares of 128-wide segments, two to a tile.  Other segment squares and the
+// small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.
 // Both operand tiles arrive in LDS by asynchronous 16-byte buffer -> LDS
 // copies into a ring of NST stages: the copies of K step k + NST - 1 are
 // issued before the MFMAs of step k (BK = 64 with two stages measured faster
@@ -86,7 +87,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   constexpr int NCP = ROWS / (RPI * NW);      // copies per thread per stage
   constexpr int NCX = BM / (RPI * NW);        // of which X rows
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "copy rounds cover whole rows");
-  static_assert(EPI != kEpiSegSq || (BN == 128 && BM <= 64 * NW), "a segment is one tile column");
+  // segment squares: one 128-wide segment per tile (BN = 128), or, on the
+  // 256 x 256 kernel, one per wave column (two per tile, WN = 128)
+  constexpr int SEGS = EPI == kEpiSegSq ? BN / 128 : 1;
+  static_assert(EPI != kEpiSegSq || (BN == 128 && BM <= 64 * NW) || (BN == 256 && WN == 128),
+                "a segment is a tile column or a wave column");
 
   static_assert((NST - 2) * NCP <= 63, "copies in flight must fit the wait counter");
   __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STAGE];
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   const int wm = w / WGN, wn = w % WGN;
 
   // ---- tile of this workgroup ----
-  const int N = EPI == kEpiSegSq ? p.d_next : p.N;
+  const int N = EPI == kEpiSegSq ? SEGS * p.d_next : p.N;
   const int ntm = (p.Mrows + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   const int ntiles = ntm * ntn;
   const int per_xcd = (ntiles + 7) / 8;
@@ -123,11 +128,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
     Y = static_cast<const __bf16*>(z ? p.Y[1] : p.Y[0]);
     Nrows = p.Nvalid;
   } else if constexpr (EPI == kEpiSegSq) {
-    const int c = z < p.H_next ? 0 : (z < p.H_next + p.G_next ? 1 : 2);
-    const int zs = z - (c == 0 ? 0 : (c == 1 ? p.H_next : p.H_next + p.G_next));
+    // segments SEGS z .. SEGS z + SEGS - 1 (of one matrix: the host keeps
+    // H', G' multiples of SEGS)
+    const int sz = SEGS * z;
+    const int c = sz < p.H_next ? 0 : (sz < p.H_next + p.G_next ? 1 : 2);
+    const int zs = sz - (c == 0 ? 0 : (c == 1 ? p.H_next : p.H_next + p.G_next));
     Y = static_cast<const __bf16*>(c == 0 ? p.Y[0] : (c == 1 ? p.Y[1] : p.Y[2])) +
         (int64_t)zs * p.d_next * p.ldy;
-    Nrows = p.d_next;
+    Nrows = SEGS * p.d_next;
   } else {
     Y = static_cast<const __bf16*>(p.Y[0]);
     Nrows = p.N;
@@ -367,10 +375,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
     }
     __syncthreads();
     if (tid < BM && m0 + tid < p.Mrows) {
-      float t = 0.f;
+      if constexpr (SEGS == 1) {
+        float t = 0.f;
 #pragma unroll
-      for (int q = 0; q < WGN; ++q) t += red[q][tid];
-      p.seg_part[(int64_t)z * p.Mrows + m0 + tid] = t;
+        for (int q = 0; q < WGN; ++q) t += red[q][tid];
+        p.seg_part[(int64_t)z * p.Mrows + m0 + tid] = t;
+      } else {
+        static_assert(SEGS == WGN, "one segment per wave column");
+#pragma unroll
+        for (int q = 0; q < WGN; ++q) p.seg_part[(int64_t)(SEGS * z + q) * p.Mrows + m0 + tid] = red[q][tid];
+      }
     }
   } else {
     char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
@@ -502,7 +516,7 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
   // a tile's rows must lie within the 32-bit range of its buffer resource
   if ((int64_t)BM * p.ldx * 2 > kMaxResourceBytes || (int64_t)BN * p.ldy * 2 > kMaxResourceBytes)
     return hipErrorInvalidValue;
-  const int N = EPI == kEpiSegSq ? p.d_next : p.N;
+  const int N = EPI == kEpiSegSq ? (BN / 128) * p.d_next : p.N;
   const int ntiles = ((p.Mrows + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid(8 * ((ntiles + 7) / 8), ny);
   hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, BK, WGM, WGN, NST, EPI, PP>), grid, dim3(64 * WGM * WGN), 0, st, p);
@@ -518,9 +532,14 @@ static int64_t tiling_cost(int64_t tiles, int slots, int cols) { return (tiles +
 hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
   const int64_t ntm256 = (p.Mrows + 255) / 256;
-  // one segment per tile column (192-row ping-pong tiles measured 17-36%
-  // slower than these)
-  if (epilogue == kEpiSegSq) return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
+  if (epilogue == kEpiSegSq) {
+    // 128-wide segments two to a 256 x 256 ping-pong tile when the segment
+    // counts of W_q and of W_k, W_v are even; else one per 128 x 128 tile
+    // (192-row tiles, ping-pong or not, measured 4-36% slower than these)
+    if (p.d_next == 128 && p.H_next % 2 == 0 && p.G_next % 2 == 0 && ny % 2 == 0)
+      return launch_t<256, 256, 64, 4, 2, 2, kEpiSegSq, true>(p, ny / 2, st);
+    return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
+  }
   if (epilogue == kEpiFold) {
     // 256 x 192 tiles where they fill the CUs with less work per CU (the
     // Qwen3-0.6B-shaped fold: 256 tiles instead of 192 on 256 CUs)
