@@ -13,8 +13,9 @@
 // large stores run 256-row tiles on 8 waves in ping-pong:
 // the two waves of a SIMD alternate between an MFMA phase and a memory phase
 // (LDS fragment reads, copies), barrier to barrier; so do the segment
-// squares of 128-wide segments, two to a tile.  Other segment squares and the
-// small stores run 128 x 128 tiles on 4 waves, two workgroups per CU.
+// squares of 128-, 96- or 64-wide segments, two to a tile (one per wave
+// column).  Other segment squares and the small stores run 128 x 128 tiles on
+// 4 waves, two workgroups per CU.
 // Both operand tiles arrive in LDS by asynchronous 16-byte buffer -> LDS
 // copies into a ring of NST stages: the copies of K step k + NST - 1 are
 // issued before the MFMAs of step k (BK = 64 with two stages measured faster
@@ -87,10 +88,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
   constexpr int NCP = ROWS / (RPI * NW);      // copies per thread per stage
   constexpr int NCX = BM / (RPI * NW);        // of which X rows
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "copy rounds cover whole rows");
-  // segment squares: one 128-wide segment per tile (BN = 128), or, on the
-  // 256 x 256 kernel, one per wave column (two per tile, WN = 128)
-  constexpr int SEGS = EPI == kEpiSegSq ? BN / 128 : 1;
-  static_assert(EPI != kEpiSegSq || (BN == 128 && BM <= 64 * NW) || (BN == 256 && WN == 128),
+  // segment squares: one segment per tile (BN = 128 >= d'), or, on the
+  // ping-pong kernel, one per wave column (WGN per tile; the host launches it
+  // only when the segment width d' is WN)
+  constexpr int SEGS = (EPI == kEpiSegSq && PP) ? WGN : 1;
+  static_assert(EPI != kEpiSegSq || (!PP && BN == 128 && BM <= 64 * NW) || PP,
                 "a segment is a tile column or a wave column");
 
   static_assert((NST - 2) * NCP <= 63, "copies in flight must fit the wait counter");
@@ -516,7 +518,7 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
   // a tile's rows must lie within the 32-bit range of its buffer resource
   if ((int64_t)BM * p.ldx * 2 > kMaxResourceBytes || (int64_t)BN * p.ldy * 2 > kMaxResourceBytes)
     return hipErrorInvalidValue;
-  const int N = EPI == kEpiSegSq ? (BN / 128) * p.d_next : p.N;
+  const int N = EPI == kEpiSegSq ? (PP ? WGN : 1) * p.d_next : p.N;
   const int ntiles = ((p.Mrows + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid(8 * ((ntiles + 7) / 8), ny);
   hipLaunchKernelGGL((mm_bf16_kernel<BM, BN, BK, WGM, WGN, NST, EPI, PP>), grid, dim3(64 * WGM * WGN), 0, st, p);
@@ -533,11 +535,15 @@ hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
   const int64_t ntm256 = (p.Mrows + 255) / 256;
   if (epilogue == kEpiSegSq) {
-    // 128-wide segments two to a 256 x 256 ping-pong tile when the segment
-    // counts of W_q and of W_k, W_v are even; else one per 128 x 128 tile
-    // (192-row tiles, ping-pong or not, measured 4-36% slower than these)
-    if (p.d_next == 128 && p.H_next % 2 == 0 && p.G_next % 2 == 0 && ny % 2 == 0)
-      return launch_t<256, 256, 64, 4, 2, 2, kEpiSegSq, true>(p, ny / 2, st);
+    // segments two to a ping-pong tile whose wave columns are one segment
+    // wide (d' = 128, 96 or 64) when the segment counts of W_q and of W_k,
+    // W_v are even; else one per 128 x 128 tile (192-row tiles, ping-pong or
+    // not, measured 4-36% slower than these)
+    if (p.H_next % 2 == 0 && p.G_next % 2 == 0 && ny % 2 == 0) {
+      if (p.d_next == 128) return launch_t<256, 256, 64, 4, 2, 2, kEpiSegSq, true>(p, ny / 2, st);
+      if (p.d_next == 96) return launch_t<256, 192, 64, 4, 2, 2, kEpiSegSq, true>(p, ny / 2, st);
+      if (p.d_next == 64) return launch_t<256, 128, 64, 4, 2, 2, kEpiSegSq, true>(p, ny / 2, st);
+    }
     return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
   }
   if (epilogue == kEpiFold) {
