@@ -9,8 +9,8 @@
 //     fp32 or bf16, per batch entry or per K chunk.
 // Workgroup tile BM x BN x BK on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
-// The fold (256 x 256, or 256 x 192 where that fills the CUs better) and the
-// large stores run 256-row tiles on 8 waves in ping-pong:
+// The fold (256 x 256, or 256 x 192 or 192 x 256 where that fills the CUs
+// better) and the large stores run 8-wave tiles in ping-pong:
 // the two waves of a SIMD alternate between an MFMA phase and a memory phase
 // (LDS fragment reads, copies), barrier to barrier; so do the segment
 // squares of 128-, 96- or 64-wide segments, two to a tile (one per wave
@@ -528,8 +528,8 @@ hipError_t launch_t(const GemmParams& p, int ny, hipStream_t st) {
 }  // namespace
 
 // rounds of `slots` concurrent workgroups (one per CU) times the work of one
-// tile (its column count, at equal rows and K): the cost of a tiling
-static int64_t tiling_cost(int64_t tiles, int slots, int cols) { return (tiles + slots - 1) / slots * cols; }
+// tile (its area, at equal K): the cost of a tiling
+static int64_t tiling_cost(int64_t tiles, int slots, int area) { return (tiles + slots - 1) / slots * area; }
 
 hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t st) {
   if (ny == 0 || p.Mrows == 0) return hipSuccess;
@@ -547,11 +547,14 @@ hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t
     return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
   }
   if (epilogue == kEpiFold) {
-    // 256 x 192 tiles where they fill the CUs with less work per CU (the
-    // Qwen3-0.6B-shaped fold: 256 tiles instead of 192 on 256 CUs)
-    const int64_t c256 = tiling_cost(ntm256 * ((p.N + 255) / 256) * ny, 256, 256);
-    const int64_t c192 = tiling_cost(ntm256 * ((p.N + 191) / 192) * ny, 256, 192);
-    if (c192 < c256) return launch_t<256, 192, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
+    // the ping-pong tile (256 x 256, 256 x 192 or 192 x 256) that needs the
+    // least work per CU: the Qwen3-0.6B-shaped fold gets 256 x 192 and the
+    // Danube3-500M-shaped one 192 x 256 (256 tiles on 256 CUs instead of 192)
+    const int64_t c_sq = tiling_cost(ntm256 * ((p.N + 255) / 256) * ny, 256, 256 * 256);
+    const int64_t c_n192 = tiling_cost(ntm256 * ((p.N + 191) / 192) * ny, 256, 256 * 192);
+    const int64_t c_m192 = tiling_cost((p.Mrows + 191) / 192 * ((p.N + 255) / 256) * ny, 256, 192 * 256);
+    if (c_n192 < c_sq && c_n192 <= c_m192) return launch_t<256, 192, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
+    if (c_m192 < c_sq) return launch_t<192, 256, 64, 2, 4, 2, kEpiFold, true>(p, ny, st);
     return launch_t<256, 256, 64, 4, 2, 2, kEpiFold, true>(p, ny, st);
   }
   if (p.N == 0) return hipSuccess;
