@@ -837,8 +837,29 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
       return hip_fail(e, fn);
     const void* xg = bf ? xl : static_cast<const void*>(x);
     const bool fused = loo_coef_fused(d, dt);
+    // bf16, d = 64 or 128: x . o_h straight from the GEMM (Z never stored;
+    // its buffer holds the d / 64 fp32 partial planes [q][H][T] instead)
+    const bool dot = fused && loo_dot_epilogue(d, dt);
+    float* xo_part = dot ? static_cast<float*>(Z) : nullptr;
+    auto gemm_dot = [&]() {
+      GemmParams p{};
+      p.X = WoT;
+      p.Y[0] = xg;
+      p.ldx = D;
+      p.ldy = D;
+      p.Mrows = HD;
+      p.N = T;
+      p.Nvalid = T;
+      p.K = D;
+      p.dot_a = a;
+      p.dot_out = xo_part;
+      p.dot_lda = HD;
+      p.dot_H = dm->H;
+      p.dot_d = d;
+      return launch_mm_bf16(p, kEpiDot, 1, st);
+    };
     if ((e = launch_scale_transpose(W_o, nullptr, WoT, D, HD, D, dt, st)) != hipSuccess ||
-        (e = gemm(WoT, D, xg, D, HD, T, D, Z, HD, true, 1, 0, 0, 0, 0)) != hipSuccess ||
+        (e = dot ? gemm_dot() : gemm(WoT, D, xg, D, HD, T, D, Z, HD, true, 1, 0, 0, 0, 0)) != hipSuccess ||
         (e = gemm(WoT, D, WoT, D, d, d, D, Q, d, true, dm->H, (int64_t)d * D, (int64_t)d * D,
                   (int64_t)d * d, 0)) != hipSuccess ||
         (!fused && (e = gemm(Q, d, a, HD, d, T, d, U, HD, true, dm->H, (int64_t)d * d, d, d,
@@ -849,7 +870,7 @@ int hna_affinity_loo(const hna_dims* dm, const void* a, const void* g, const voi
     //    head outputs, transposed (ZAT), and x^T make R one GEMM over the tokens
     //    (HD x hidden, in K chunks), and Y^g, Y^u are two GEMMs over hidden
     if (fused) {
-      if ((e = launch_loo_coef_fused(a, Z, ZAT, Q, xx, dm->T, dm->H, d, D, coef, st)) != hipSuccess)
+      if ((e = launch_loo_coef_fused(a, Z, xo_part, ZAT, Q, xx, dm->T, dm->H, d, D, coef, st)) != hipSuccess)
         return hip_fail(e, fn);
     } else if ((e = launch_loo_coef(a, Z, U, xx, dm->T, dm->H, d, D, coef, dt, st)) != hipSuccess ||
                (e = launch_scale_a(a, coef, xx, dm->T, dm->H, d, D, Z, dt, st)) != hipSuccess ||

@@ -192,8 +192,11 @@ hipError_t launch_head_step(const HeadStepParams& p, hipStream_t st);
 // c contiguous.  launch_scale_transpose makes X[m, c] = s[c] * W[c, m] from a
 // row-major W [K, Mrows].  Epilogues: write the folded layout, sum C^2 over
 // the n of a segment, or store C[m, n] (fp32, or bf16 from the bf16 kernel)
-// at C + n * ldc + m (C transposed: m contiguous, ldc and m0 multiples of 4).
-enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1, kEpiStore = 2 };
+// at C + n * ldc + m (C transposed: m contiguous, ldc and m0 multiples of 4),
+// or (dot) dot each 64-row block of C's column n with the matching entries of
+// a row-major token operand A_tok [N][lda]: out[q][h][n] = sum over the 64
+// rows m = h d + 64 q + i of C[m, n] A_tok[n][m] (d a multiple of 64).
+enum GemmEpilogue { kEpiFold = 0, kEpiSegSq = 1, kEpiStore = 2, kEpiDot = 3 };
 
 struct GemmParams {
   const void* X;       // Xs [Mrows, K]
@@ -214,6 +217,11 @@ struct GemmParams {
   int64_t ldc, bx, by, bc;
   int k_split;
   int out_bf16;        // store in bf16 (fp32 otherwise)
+  // dot output: A_tok (bf16, [N][dot_lda]) and out ([d / 64][dot_H][N] fp32)
+  const void* dot_a;
+  float* dot_out;
+  int64_t dot_lda;
+  int dot_H, dot_d;
 };
 // The bf16 GEMM (k_mm.hip): grid y runs over gate / up (fold, ny = 2), the
 // H' + 2 G' segments of W_q, W_k, W_v (segment square), or batches / K chunks
@@ -243,11 +251,14 @@ hipError_t launch_loo_coef(const void* a, const void* Z, const void* U, const fl
                            int H, int d, int D, float2* coef, int dtype, hipStream_t st);
 // bf16 with d a multiple of 32 up to 128: the moments (|o_h|^2 on the matrix
 // cores from Q_h = W_o^(h)T W_o^(h)), alpha and beta, and (alpha beta / r) a
-// written transposed, ZAT [H d][Tp] (Z = x W_o is read), in one kernel
+// written transposed, ZAT [H d][Tp], in one kernel.  x . o_h is Z_h . a_h
+// from Z = x W_o, or (xo_part non-null; d = 64 or 128) the sum of the d / 64
+// planes xo_part[q][h][t] that the GEMM's dot epilogue wrote.
 bool loo_coef_fused(int d, int dtype);
-hipError_t launch_loo_coef_fused(const void* a, const void* Z, void* ZAT, const void* Q,
-                                 const float* xx, int64_t T, int H, int d, int D, float2* coef,
-                                 hipStream_t st);
+bool loo_dot_epilogue(int d, int dtype);
+hipError_t launch_loo_coef_fused(const void* a, const void* Z, const float* xo_part, void* ZAT,
+                                 const void* Q, const float* xx, int64_t T, int H, int d, int D,
+                                 float2* coef, hipStream_t st);
 hipError_t launch_scale_a(const void* a, const float2* coef, const float* xx, int64_t T, int H,
                           int d, int D, void* As, int dtype, hipStream_t st);
 // Tokens padded to a multiple of 8 (the K length of the token GEMM)

@@ -231,9 +231,12 @@ __device__ inline float bf16_at(const uint4& v, int e) {
 // 128-byte run of 16-byte stores.
 constexpr int kCoefBlocksPerHead = 128;
 
-template <int ND>
+// XO: x . o_h comes as d / 64 fp32 partial planes xo[q][h][t] (summed here in
+// plane order) instead of from Z.
+template <int ND, bool XO>
 __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __restrict__ a,
                                                             const __bf16* __restrict__ Z,
+                                                            const float* __restrict__ xo_part,
                                                             __bf16* __restrict__ ZAT,
                                                             const __bf16* __restrict__ Q,
                                                             const float* __restrict__ xx,
@@ -264,7 +267,8 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
   const int64_t n_blk = (n_tiles + 3) / 4;
   const int wave = threadIdx.x >> 6;
   int64_t tile = (int64_t)blockIdx.x * 4 + wave;
-  uint4 ar[ND], zr[ND];
+  uint4 ar[ND], zr[XO ? 1 : ND];
+  float xr = 0.f;   // XO: this token's x . o_h (lanes of quarter 0; 0 elsewhere)
   auto fetch = [&](int64_t tt) {
     const int64_t t = tt * 16 + tl;
     const bool ok = tt < n_tiles && t < T;
@@ -272,14 +276,24 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
 #pragma unroll
     for (int ks = 0; ks < ND; ++ks) {
       ar[ks] = ok ? *reinterpret_cast<const uint4*>(ap + base + 32 * ks) : make_uint4(0, 0, 0, 0);
-      zr[ks] = ok ? *reinterpret_cast<const uint4*>(zp + base + 32 * ks) : make_uint4(0, 0, 0, 0);
+      if constexpr (!XO)
+        zr[ks] = ok ? *reinterpret_cast<const uint4*>(zp + base + 32 * ks) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (XO) {
+      xr = 0.f;
+      if (ok && qq == 0)
+        for (int q = 0; q < d / 64; ++q) xr += xo_part[((int64_t)q * H + h) * T + t];
     }
   };
   fetch(tile);
   for (int64_t blk = blockIdx.x; blk < n_blk; blk += gridDim.x, tile += step) {
-    uint4 a_cur[ND], z_cur[ND];
+    uint4 a_cur[ND], z_cur[XO ? 1 : ND];
+    const float x_cur = xr;
 #pragma unroll
-    for (int ks = 0; ks < ND; ++ks) { a_cur[ks] = ar[ks]; z_cur[ks] = zr[ks]; }
+    for (int ks = 0; ks < ND; ++ks) {
+      a_cur[ks] = ar[ks];
+      if constexpr (!XO) z_cur[ks] = zr[ks];
+    }
     fetch(tile + step);  // the next tile loads under this one's work (zeros past the last)
     const int64_t t = tile * 16 + tl;
     const bool ok = t < T;
@@ -302,10 +316,14 @@ __global__ __launch_bounds__(256) void loo_coef_mfma_kernel(const __bf16* __rest
 #pragma unroll
       for (int r = 0; r < 4; ++r) oo = fmaf(acc[r], bf16_at(a_cur[mt >> 1], 4 * (mt & 1) + r), oo);
     }
+    if constexpr (XO) {
+      xo = x_cur;
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < ND; ++ks)
+      for (int ks = 0; ks < ND; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xo = fmaf(bf16_at(z_cur[ks], e), bf16_at(a_cur[ks], e), xo);
+        for (int e = 0; e < 8; ++e) xo = fmaf(bf16_at(z_cur[ks], e), bf16_at(a_cur[ks], e), xo);
+    }
     xo += __shfl_xor(xo, 16);
     oo += __shfl_xor(oo, 16);
     xo += __shfl_xor(xo, 32);
@@ -618,10 +636,11 @@ hipError_t launch_scale_cols(const float* R, int parts, const float* gamma, int 
 }
 
 bool loo_coef_fused(int d, int dtype) { return dtype == 1 && d % 32 == 0 && d >= 32 && d <= 128; }
+bool loo_dot_epilogue(int d, int dtype) { return dtype == 1 && (d == 64 || d == 128); }
 
-hipError_t launch_loo_coef_fused(const void* a, const void* Z, void* ZAT, const void* Q,
-                                 const float* xx, int64_t T, int H, int d, int D, float2* coef,
-                                 hipStream_t st) {
+hipError_t launch_loo_coef_fused(const void* a, const void* Z, const float* xo_part, void* ZAT,
+                                 const void* Q, const float* xx, int64_t T, int H, int d, int D,
+                                 float2* coef, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int64_t n_tiles = (T + 15) / 16;
   const int64_t bx = (n_tiles + 3) / 4;
@@ -631,11 +650,20 @@ hipError_t launch_loo_coef_fused(const void* a, const void* Z, void* ZAT, const 
   const auto* zb = static_cast<const __bf16*>(Z);
   auto* zt = static_cast<__bf16*>(ZAT);
   const auto* qb = static_cast<const __bf16*>(Q);
+  if (xo_part != nullptr) {
+    // partial planes of x . o_h (head dims 64 and 128)
+    switch (d) {
+      case 64: hipLaunchKernelGGL((loo_coef_mfma_kernel<2, true>), grid, dim3(256), 0, st, ab, zb, xo_part, zt, qb, xx, T, Tp, H, D, coef); break;
+      case 128: hipLaunchKernelGGL((loo_coef_mfma_kernel<4, true>), grid, dim3(256), 0, st, ab, zb, xo_part, zt, qb, xx, T, Tp, H, D, coef); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (d / 32) {
-    case 1: hipLaunchKernelGGL(loo_coef_mfma_kernel<1>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
-    case 2: hipLaunchKernelGGL(loo_coef_mfma_kernel<2>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
-    case 3: hipLaunchKernelGGL(loo_coef_mfma_kernel<3>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
-    case 4: hipLaunchKernelGGL(loo_coef_mfma_kernel<4>, grid, dim3(256), 0, st, ab, zb, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 1: hipLaunchKernelGGL((loo_coef_mfma_kernel<1, false>), grid, dim3(256), 0, st, ab, zb, xo_part, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 2: hipLaunchKernelGGL((loo_coef_mfma_kernel<2, false>), grid, dim3(256), 0, st, ab, zb, xo_part, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 3: hipLaunchKernelGGL((loo_coef_mfma_kernel<3, false>), grid, dim3(256), 0, st, ab, zb, xo_part, zt, qb, xx, T, Tp, H, D, coef); break;
+    case 4: hipLaunchKernelGGL((loo_coef_mfma_kernel<4, false>), grid, dim3(256), 0, st, ab, zb, xo_part, zt, qb, xx, T, Tp, H, D, coef); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -388,6 +388,59 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mm_bf16_kernel(const GemmParam
         for (int q = 0; q < WGN; ++q) p.seg_part[(int64_t)(SEGS * z + q) * p.Mrows + m0 + tid] = red[q][tid];
       }
     }
+  } else if constexpr (EPI == kEpiDot) {
+    // x . o_h without storing Z: C[m][n] = Z[n][m] (m = h d + j) dotted with
+    // A_tok[n][m] over each wave's 64 rows, one partial per (64-row block,
+    // head, token).  The tile's A_tok block (256 tokens x 256 columns, bf16)
+    // is copied into the idle operand stages: row t holds 32 chunks of 16
+    // bytes, chunk c in slot c ^ (t % 32), so that the 32 tokens one read
+    // serves land in distinct slots.
+    static_assert(PP && BM == 256 && BN == 256 && WM == 64 && WN == 128, "the 256 x 256 ping-pong tile");
+    static_assert(NST * STAGE >= 256 * 512, "the operand block fits the stages");
+    __syncthreads();
+    const int64_t lda2 = p.dot_lda * 2;                 // bytes per token row of A_tok
+    const int64_t rows_left = (int64_t)p.N - n0;
+    const int cols = min(256, p.Mrows - m0);           // columns of A_tok this tile covers
+    // the range ends at the last needed byte: rows past N and columns past
+    // Mrows read zeros
+    const int64_t ab = rows_left > 0 ? (rows_left - 1) * lda2 + (int64_t)cols * 2 : 0;
+    const u32x4 ra = uniform_rsrc(static_cast<const char*>(p.dot_a) + (int64_t)n0 * lda2 + (int64_t)m0 * 2,
+                                  ab > (int64_t)lim ? lim : (uint32_t)ab);
+    const uint32_t lds_a = lds_addr(lds);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      // copy k of wave w fills tile rows 2 (16 w + k) and + 1 (512 bytes each)
+      const int r = 2 * (16 * w + k) + (l >> 5), c = (l & 31) ^ (r & 31);
+      dma16s(ra, (uint32_t)((int64_t)r * lda2) + (uint32_t)(c * 16), 0u, lds_a + (uint32_t)(16 * w + k) * 1024u);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int half = l >> 5;
+    const int mrow = m0 + wm * WM;                      // the wave's first row
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int t = wn * WN + j * 32 + (l & 31);       // tile row of A_tok (token)
+      const unsigned char* arow = lds + t * 512;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int hd = wm * WM + i * 32 + 8 * a + 4 * half;   // tile column: 4 consecutive
+          const uint2 v = *reinterpret_cast<const uint2*>(arow + (((hd >> 3) ^ (t & 31)) << 4) + (hd & 7) * 2);
+          const f32x16& cc = acc[i][j];
+          s = fmaf(cc[4 * a], __uint_as_float(v.x << 16), s);
+          s = fmaf(cc[4 * a + 1], __uint_as_float(v.x & 0xffff0000u), s);
+          s = fmaf(cc[4 * a + 2], __uint_as_float(v.y << 16), s);
+          s = fmaf(cc[4 * a + 3], __uint_as_float(v.y & 0xffff0000u), s);
+        }
+      s += __shfl_xor(s, 32);
+      const int n = n0 + t;
+      if (l < 32 && n < p.N && mrow < p.Mrows) {
+        const int h = mrow / p.dot_d, q = (mrow - h * p.dot_d) / 64;
+        p.dot_out[((int64_t)q * p.dot_H + h) * p.N + n] = s;
+      }
+    }
   } else {
     char* Cb = static_cast<char*>(p.C) + (int64_t)z * p.bc * (p.out_bf16 ? 2 : 4);
     if constexpr (PP && WM == 64 && WN % 64 == 0) {
@@ -546,6 +599,7 @@ hipError_t launch_mm_bf16(const GemmParams& p, int epilogue, int ny, hipStream_t
     }
     return launch_t<128, 128, 64, 2, 2, 2, kEpiSegSq>(p, ny, st);
   }
+  if (epilogue == kEpiDot) return launch_t<256, 256, 64, 4, 2, 2, kEpiDot, true>(p, ny, st);
   if (epilogue == kEpiFold) {
     // the ping-pong tile (256 x 256, 256 x 192 or 192 x 256) that needs the
     // least work per CU: the Qwen3-0.6B-shaped fold gets 256 x 192 and the

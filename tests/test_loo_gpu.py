@@ -66,6 +66,10 @@ def check(got, ref, tol, metric):
     (synth.LayerShape("split-remainder-bf16", 8195, 128, 4, 2, 32, 200, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("split-remainder-fp32", 12289, 64, 4, 2, 16, 128, "f32", 0.5), FP32_TOL, "max"),
     (synth.LayerShape("d128-bf16", 512, 512, 16, 8, 128, 256, "bf16", 0.5), BF16_TOL, "fro"),
+    # x . o_h from the GEMM's dot epilogue with partial tiles both ways: H d
+    # below or past a multiple of 256, tokens not a multiple of 256
+    (synth.LayerShape("d64-ragged-bf16", 777, 192, 3, 1, 64, 200, "bf16", 0.5), BF16_TOL, "fro"),
+    (synth.LayerShape("d128-ragged-bf16", 1001, 320, 5, 1, 128, 136, "bf16", 0.5), BF16_TOL, "fro"),
     # fewer tokens than one 8-token pad group (one K step of 64, mostly zeros)
     (synth.LayerShape("five-tokens-bf16", 5, 128, 4, 2, 32, 64, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("three-tokens-fp32", 3, 64, 4, 2, 16, 64, "f32", 0.5), FP32_TOL, "max"),
