@@ -634,7 +634,12 @@ LooWorkspace loo_workspace(const hna_dims* dm) {
   w.xl = o;        o += dm->dtype == HNA_BF16 ? align256((size_t)dm->T * D * 2) : 0;
   w.xT = o;        o += align256(D * tp * es);      // x^T, padded tokens
   w.WoT = o;       o += align256(HD * D * es);      // W_o^T
-  w.Z = o;         o += align256(thd * es);         // x W_o (then a scaled, unfused path)
+  // x W_o (then a scaled, unfused path); with the dot epilogue only the
+  // d / 64 fp32 planes of x . o_h
+  w.Z = o;
+  o += loo_coef_fused(dm->d, dm->dtype) && loo_dot_epilogue(dm->d, dm->dtype)
+           ? align256((size_t)(dm->d / 64) * dm->H * dm->T * sizeof(float))
+           : align256(thd * es);
   w.ZAT = o;       o += align256(HD * tp * es);     // (alpha beta / r) a, transposed
   w.U = o;         o += loo_coef_fused(dm->d, dm->dtype) ? 0 : align256(thd * es);
   w.Q = o;         o += align256(HD * dm->d * es);
