@@ -1,12 +1,15 @@
 // bf16 "NT" GEMM on the matrix cores for the weight products of the affinity
 // pass and of the leave-one-out score: C[m, n] = sum_k X[m, k] Y[n, k], X and Y
-// row-major with k contiguous, fp32 accumulation.  Three epilogues:
+// row-major with k contiguous, fp32 accumulation.  Four epilogues:
 //   * fold (section 3, "Affinity scores": M_h = W_o^(h)T diag(gamma) W^T): C is
 //     written in the fragment order of the folded weights;
 //   * segment square (the down edge's ||b_gk||^2): C^2 summed over the rows n
 //     of one W_q / W_k / W_v segment, b never stored;
 //   * plain store of C transposed (C[m, n] at n * ldc + m, m contiguous),
-//     fp32 or bf16, per batch entry or per K chunk.
+//     fp32 or bf16, per batch entry or per K chunk;
+//   * dot (the leave-one-out score's x . o_h = (x W_o^(h)) . a_h): each 64-row
+//     block of C's column n dotted with a token operand's row n, C never
+//     stored.
 // Workgroup tile BM x BN x BK on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) as 32x32 MFMA tiles (every LDS fragment read feeds several MFMAs).
 // The fold (256 x 256, or 256 x 192 or 192 x 256 where that fills the CUs
