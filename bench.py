@@ -63,9 +63,14 @@ def cpu_baseline(layer_gpu):
     token chunk of the oracle; its cost is linear in the token count)."""
     import torch
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        libs = [f"{i.get('internal_api', '?')} ({i.get('num_threads', '?')} threads)"
+                for i in info if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or blas
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
 
@@ -91,7 +96,8 @@ def cpu_baseline(layer_gpu):
     dt = run(T1)
     return {"value": T1 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {T1} of the {Tmax} tokens of the same synthetic layer, whole pass "
-                      f"(S_fo, S_add, S_down) in float64 numpy, {dt:.1f} s"}
+                      f"(S_fo, S_add, S_down) in float64 numpy, {dt:.1f} s",
+            "blas": blas, "host_cpus": os.cpu_count()}
 
 
 def copy_probe(mib: int):
