@@ -156,3 +156,14 @@ def test_edge_extreme_rms(hna, dtype, r_scale):
     L = edge_layer(dtype, 23)
     L["r"] = (L["r"].double() * r_scale).to(L["r"].dtype)
     check_layer(hna, L, dtype)
+
+
+# ------------------------------------------- down-edge segments, unpaired
+@pytest.mark.parametrize("d,H,G", [(128, 6, 3), (96, 3, 1), (64, 5, 5)])
+def test_down_edge_unpaired_segments(hna, d, H, G):
+    """bf16 down-edge weight norms at head dims 128, 96 and 64 with an odd
+    number of next-layer query heads or KV groups: the segment squares then
+    take one head segment per tile instead of two side by side."""
+    print(f"bf16 d={d} H={H} G={G}", flush=True)
+    sh = synth.LayerShape("unpaired", 300, 256, H, G, d, 264, "bf16", 0.5)
+    check_layer(hna, synth.make_layer(sh, seed=31 + d + H), "bf16")
