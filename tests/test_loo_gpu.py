@@ -79,6 +79,9 @@ def check(got, ref, tol, metric):
     # with Z stored (head dim 32) and with the dot epilogue (head dim 128)
     (synth.LayerShape("odd-I-bf16", 300, 128, 4, 2, 32, 100, "bf16", 0.5), BF16_TOL, "fro"),
     (synth.LayerShape("odd-I-d128-bf16", 259, 256, 2, 1, 128, 77, "bf16", 0.5), BF16_TOL, "fro"),
+    # the fp32 path at the larger head dims (unfused coefficients, fp32 GEMMs)
+    (synth.LayerShape("d128-fp32", 300, 256, 4, 2, 128, 100, "f32", 0.5), FP32_TOL, "max"),
+    (synth.LayerShape("d96-fp32", 333, 192, 3, 3, 96, 130, "f32", 0.5), FP32_TOL, "max"),
 ], ids=lambda v: v.name if isinstance(v, synth.LayerShape) else str(v))
 def test_loo_matches_oracle(hna, shape, tol, metric):
     layer = synth.make_layer(shape, seed=17, device="cuda", with_next=False, with_x=True)
