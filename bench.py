@@ -12,10 +12,12 @@ its average duration measured with HIP events on the launch stream);
 `cpu_baseline` is the float64 oracle timed on this host on a bounded token
 sample of the same layer; `mfma_loop` is the matrix cores' sustained bf16
 rate on random operands (hna_mfma_rate_probe), the second reference for the
-hot kernel's MFMA rate besides the published peak.  Unless --no-legs is given, the line also carries
-the other single-layer workloads (Danube3-500M-shaped and the large
-4096 x 14336 layer) measured the same way, the 28-layer Qwen3-0.6B-shaped
-stack end to end, the leave-one-out score and the layout-search calls.
+hot kernel's MFMA rate besides the published peak.  Unless --no-legs is given,
+the line also carries the other single-layer workloads (Danube3-500M-shaped
+and the large 4096 x 14336 layer, and the benchmark layer with fp32 inputs
+against the fp32 matrix peak) measured the same way, the 28-layer
+Qwen3-0.6B-shaped stack end to end, the leave-one-out score and the
+layout-search calls.
 Progress lines go to stderr.
 """
 from __future__ import annotations
@@ -342,12 +344,16 @@ def layer_figures(shape, ms_step: float, hot_ms: float):
     }
 
 
-def layer_leg(hna, config: int, steps: int, warmup: int):
-    """Another single-layer workload, measured like the main line."""
+def layer_leg(hna, config: int, steps: int, warmup: int, dtype=None):
+    """Another single-layer workload, measured like the main line (optionally
+    with another input dtype, named as a workload of its own)."""
+    import dataclasses
     import torch
     import synth
     shape = synth.layer_shape(config)
-    layer = synth.make_config_layer(config, device="cuda")
+    if dtype is not None and dtype != shape.dtype:
+        shape = dataclasses.replace(shape.with_dtype(dtype), name=f"{shape.name}-{dtype}")
+    layer = synth.make_config_layer(config, device="cuda", dtype=dtype)
     torch.cuda.synchronize()
     _, ms_step, hot_ms = time_layer(hna, layer, steps, warmup)
     rec = {"workload": shape.name, "T": shape.T, "hidden": shape.hidden, "H": shape.H,
@@ -465,6 +471,11 @@ def main():
             if c != args.config:
                 legs[synth.layer_shape(c).name] = layer_leg(hna, c, 10, 2)
                 progress(f"{synth.layer_shape(c).name} done")
+        if shape.dtype == "bf16":
+            # the fp32 instantiation of the same layer, against the fp32 matrix peak
+            fp = layer_leg(hna, args.config, 5, 1, dtype="f32")
+            legs[fp["workload"]] = fp
+            progress(f"{fp['workload']} done")
         rec["other_layers"] = legs
         rec["stack"] = stack_leg(hna, 3, 1, T=args.tokens)
         progress("stack done")
